@@ -1,0 +1,355 @@
+"""Pins of the CPU oracle against facts fixed outside it: published
+known-answer vectors, hand-worked examples, closed forms, brute force on tiny
+shapes, the pages' measured codec error, and the invariants the pages state."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+import oracle
+from oracle import looped
+from tests import _bruteforce
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- generators
+def test_philox_known_answers():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "philox4x32_10_kat.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) == 3
+    for r in rows:
+        v = [int(t, 16) for t in r]
+        out = synth.philox4x32_10(np.array(v[:4], np.uint32), np.array(v[4:6], np.uint32))
+        assert [int(t) for t in out] == v[6:]
+
+
+def test_prior_h_moments_and_determinism():
+    h = synth.prior_h(2, 3, 1, np.arange(512), 256)
+    assert h.dtype == np.float32 and h.shape == (512, 256)
+    assert abs(float(h.mean())) < 0.01 and abs(float(h.var()) - 1.0) < 0.02
+    assert np.abs(h).max() < 4.95
+    h2 = synth.prior_h(2, 3, 1, np.arange(100, 140), 256)
+    assert np.array_equal(h[100:140], h2)
+    assert not np.array_equal(h, synth.prior_h(2, 4, 1, np.arange(512), 256))
+
+
+# ---------------------------------------------------------------- codec
+@pytest.mark.parametrize("kind", ["int4", "int8"])
+def test_codec_hand_cases(kind):
+    cases = _golden("codec_hand_cases.json")[kind]
+    D = 32 if kind == "int4" else 64
+    for c in cases:
+        h = np.zeros(D, np.float16)
+        h[:len(c["h_head"])] = np.array(c["h_head"], np.float64).astype(np.float16)
+        assert np.array_equal(h[:len(c["h_head"])].astype(np.float64), np.array(c["h_head"])), c["note"]
+        q, s = looped.int4_encode(h) if kind == "int4" else looped.int8_encode(h)
+        assert float(s[0]) == c["scale"], c["note"]
+        assert list(q[:len(c["q_head"])]) == c["q_head"], c["note"]
+        assert np.all(q[len(c["q_head"]):][h[len(c["q_head"]):] == 0] == 0)
+
+
+def test_codec_int4_is_nearest_code_bruteforce():
+    """Every code is the nearest of the 16 representable levels q*s (ties to the
+    even code), found by exhaustive search rather than by the formula."""
+    rng = np.random.default_rng(5)
+    h = (rng.standard_normal((400, 32)) * rng.uniform(0.01, 30, size=(400, 1))).astype(np.float16)
+    h[::7, 3] = 0
+    q, s = looped.int4_encode(h)
+    levels = np.arange(-8, 8, dtype=np.float64)
+    for r in range(h.shape[0]):
+        sf = float(s[r, 0])
+        assert sf == float(np.float16(np.float32(np.abs(h[r].astype(np.float32)).max()) / np.float32(7)))
+        for k in range(32):
+            x = float(h[r, k]) / sf
+            dist = np.abs(levels - x)
+            best = levels[dist == dist.min()]
+            want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+            assert q[r, k] == int(want), (r, k, x)
+        # the absmax element maps to +-7 (scale rounding is within half an fp16 ulp)
+        k = int(np.argmax(np.abs(h[r].astype(np.float64))))
+        assert abs(int(q[r, k])) == 7 or int(q[r, k]) == -8
+
+
+def test_codec_decode_roundtrip_exact_levels():
+    """Dequantisation is fp16(q*s): decode(encode(h)) of an h that already
+    lies on the grid returns h bit for bit."""
+    s = np.float16(0.375)
+    q = np.tile(np.arange(-7, 8), 3)[:32].astype(np.int8)
+    q[0] = 7
+    h = (q.astype(np.float32) * np.float32(s)).astype(np.float16)
+    q2, s2 = looped.int4_encode(h)
+    assert s2[0] == s and np.array_equal(q2, q)
+    assert np.array_equal(looped.decode_int(q2, s2), h)
+
+
+def test_codec_error_matches_pages():
+    """Relative L2 error of h' and of K = W_k h' against the pages' measured
+    store-h quality table (INT8-h ~0.6 %, INT4-h ~10 %). On N(0,1) h this
+    codec gives about 0.78 % and 9.7 %; the bands allow for the pages'
+    real activations."""
+    pages = _golden("pages_store_h_table.json")["kv_rel_l2_error"]
+    rng = np.random.default_rng(11)
+    D = 1024
+    h = rng.standard_normal((256, D)).astype(np.float16)
+    wk = (rng.standard_normal((D, D)) * 0.02).astype(np.float16).astype(np.float64)
+    hf = h.astype(np.float64)
+    for kind, lo, hi in (("int8", 0.004, 0.012), ("int4", 0.08, 0.12)):
+        q, s = looped.int4_encode(h) if kind == "int4" else looped.int8_encode(h)
+        hp = looped.decode_int(q, s).astype(np.float64)
+        e_h = np.linalg.norm(hp - hf) / np.linalg.norm(hf)
+        e_k = np.linalg.norm((hp - hf) @ wk.T) / np.linalg.norm(hf @ wk.T)
+        assert lo < e_h < hi and lo < e_k < hi, (kind, e_h, e_k)
+        assert 0.5 * pages[kind] < e_k < 2.0 * pages[kind]
+
+
+# ---------------------------------------------------------------- elementwise
+def test_rmsnorm_closed_form():
+    x = np.array([[3.0, 4.0]])
+    g = np.array([1.0, 2.0])
+    r = looped.rmsnorm(x, g, 1e-5)
+    inv = 1.0 / math.sqrt(12.5 + 1e-5)          # mean(9, 16) = 12.5
+    assert np.allclose(r, [[3.0 * inv, 8.0 * inv]], rtol=0, atol=1e-15)
+
+
+def test_gelu_values():
+    # Phi(1) = 0.8413447460685429 (standard normal CDF table value)
+    assert abs(looped.gelu_erf(np.array(1.0)) - 0.8413447460685429) < 1e-15
+    assert abs(looped.gelu_erf(np.array(-1.0)) + 0.15865525393145707) < 1e-15
+    x = np.linspace(-6, 6, 101)
+    assert np.allclose(looped.gelu_erf(x) - looped.gelu_erf(-x), x, atol=1e-14)
+    assert looped.gelu_erf(np.array(0.0)) == 0.0
+
+
+# ---------------------------------------------------------------- attention
+def test_attention_hand_case():
+    c = _golden("attention_hand_case.json")
+    K, V = np.array(c["K"]), np.array(c["V"])
+    o = looped.attend(np.array(c["q"]), K, V, c["n_heads"], c["pos0"])
+    assert np.allclose(o, c["o"], atol=1e-14)
+    o0 = looped.attend(np.array(c["q_at_pos0"]), K[:1], V[:1], c["n_heads"], 0)
+    assert np.allclose(o0, c["o_at_pos0"], atol=1e-14)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(3)
+    H, d, T = 4, 8, 9
+    D = H * d
+    q = rng.standard_normal((1, D))
+    K = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    # a query at position 0 sees only itself: o = V_0
+    assert np.allclose(looped.attend(q, K[:1], V[:1], H, 0), V[:1], atol=1e-14)
+    # identical keys -> uniform weights -> o = mean V
+    Ks = np.tile(K[:1], (T, 1))
+    assert np.allclose(looped.attend(q, Ks, V, H, T - 1), V.mean(0, keepdims=True), atol=1e-13)
+    # causal: rows after the query's position do not matter
+    V2 = V.copy()
+    V2[5:] = 1e6
+    K2 = K.copy()
+    K2[5:] = -3.0
+    qq = rng.standard_normal((3, D))
+    o1 = looped.attend(qq, K[:5], V[:5], H, 2)
+    o2 = looped.attend(qq, K2[:5], V2[:5], H, 2)
+    assert np.allclose(o1, o2)
+    # heads do not mix: changing head 1's V leaves head 0's output alone
+    V3 = V.copy()
+    V3[:, d:2 * d] += 10
+    a, b = looped.attend(q, K, V, H, T - 1), looped.attend(q, K, V3, H, T - 1)
+    assert np.allclose(a[:, :d], b[:, :d]) and not np.allclose(a[:, d:2 * d], b[:, d:2 * d])
+
+
+# ---------------------------------------------------------------- whole model
+TINY = synth.ModelShape("bf-tiny", 4, 2, 2, 8, 1, 7, "f32")
+
+
+def _tiny_weights(seed=0):
+    return synth.make_weights(TINY, seed, random_gains=True, std=0.5)
+
+
+def test_bruteforce_tiny_model_matches_oracle():
+    w = _tiny_weights()
+    toks = [3, 1, 6, 0, 2]
+    wl = {
+        "embed": w["embed"].astype(float).tolist(),
+        "lm_head": w["lm_head"].astype(float).tolist(),
+        "final_norm": w["final_norm"].astype(float).tolist(),
+        "layers": [{k: v.astype(float).tolist() for k, v in lw.items()} for lw in w["layers"]],
+    }
+    bf_logits, bf_h = _bruteforce.run_sequence(wl, TINY.n_heads, TINY.n_pre, 2, toks, TINY.norm_eps)
+    for mode in ("f32", "kv"):
+        o = oracle.LoopedOracle(TINY, w, mode, 1, 8, 2, exact=True)
+        # prefill 3 then two decode steps (teacher forced)
+        r = o.prefill(0, toks[:3], 2)
+        got = [r["logits"][i] for i in range(3)]
+        for t in toks[3:]:
+            got.append(o.decode_step([0], [2], [t])["logits"][0])
+        for p in range(len(toks)):
+            assert np.allclose(got[p], bf_logits[p], rtol=0, atol=1e-12), (mode, p)
+        if mode == "f32":
+            for (layer, p), h in bf_h.items():
+                assert np.allclose(o.read_h(layer, 0, 5)[p], h, atol=1e-12)
+
+
+def _run(shape, w, mode, lanes, loops, prompts, steps, exact=False, l_max=None, thr=math.inf):
+    l_max = l_max or max(loops)
+    o = oracle.LoopedOracle(shape, w, mode, len(lanes), prompts.shape[1] + steps + 1, l_max, exact)
+    toks = []
+    for k, lane in enumerate(lanes):
+        toks.append(o.prefill(lane, prompts[k], loops[k])["next_token"])
+    out = [list(toks)]
+    logits = []
+    for _ in range(steps):
+        r = o.decode_step(lanes, loops, toks, thr)
+        toks = list(r["tokens"])
+        out.append(toks)
+        logits.append(r["logits"])
+    return o, np.array(out), np.array(logits)
+
+
+SMALL16 = synth.ModelShape("small16", 64, 4, 16, 128, 2, 97, "f16")
+
+
+def test_store_h_equals_stored_kv_exact():
+    """Store-h attention is ordinary attention with K = W_k h, V = W_v h: with
+    the rounding points off, the h modes and the stored-K/V mode agree to
+    float64 rounding (the pages' 'FP16-h: K/V bit-exact')."""
+    for shape, mode in ((synth.SHAPES["tiny"], "f32"), (SMALL16, "f16")):
+        w = synth.make_weights(shape, 1, random_gains=True)
+        pr = synth.make_prompts(shape.vocab, 1, 6, 4)
+        _, t_h, l_h = _run(shape, w, mode, [0], [3], pr, 3, exact=True)
+        _, t_kv, l_kv = _run(shape, w, "kv", [0], [3], pr, 3, exact=True)
+        assert np.array_equal(t_h, t_kv)
+        assert np.max(np.abs(l_h - l_kv)) <= 1e-12 * np.max(np.abs(l_kv))
+
+
+def test_variable_L_layer_reuse_bitwise():
+    """Cache layer n_pre + i is written only by loop iteration i, so for the
+    same tokens it is identical at L = i + 1 and at L_max."""
+    w = synth.make_weights(SMALL16, 2, random_gains=True)
+    pr = synth.make_prompts(SMALL16.vocab, 1, 5, 7)
+    seq = list(pr[0]) + [11, 23, 5]
+    caches = {}
+    for L in (2, 5):
+        o = oracle.LoopedOracle(SMALL16, w, "int4", 1, 16, 5)
+        o.prefill(0, seq[:5], L)
+        for t in seq[5:]:
+            o.decode_step([0], [L], [t])
+        caches[L] = o
+    for layer in range(SMALL16.n_pre + 2):
+        a = caches[2].read_codes(layer, 0, 0, 8)
+        b = caches[5].read_codes(layer, 0, 0, 8)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_resume_equals_fresh_run():
+    """Warm start: a prompt run at L=4, extended to L=8 from its saved residual,
+    then decoded at L=8, is bit-identical to a fresh L=8 run."""
+    w = synth.make_weights(SMALL16, 3, random_gains=True)
+    pr = synth.make_prompts(SMALL16.vocab, 1, 6, 8)[0]
+    fresh = oracle.LoopedOracle(SMALL16, w, "int4", 1, 16, 8)
+    rf = fresh.prefill(0, pr, 8)
+    warm = oracle.LoopedOracle(SMALL16, w, "int4", 1, 16, 8)
+    r4 = warm.forward(0, pr, 4, check_safety=False)
+    r8 = warm.extend_depth(0, r4["x"], 4, 8)
+    assert np.array_equal(r8["logits"], rf["logits"])
+    tf, tw = rf["next_token"], oracle.argmax_lowest(r8["logits"][-1])
+    assert tf == tw
+    for _ in range(4):
+        a = fresh.decode_step([0], [8], [tf])
+        b = warm.decode_step([0], [8], [tw])
+        assert np.array_equal(a["logits"], b["logits"])
+        tf, tw = a["tokens"][0], b["tokens"][0]
+    for layer in range(SMALL16.n_pre + 8):
+        ca, cb = fresh.read_codes(layer, 0, 0, 10), warm.read_codes(layer, 0, 0, 10)
+        assert np.array_equal(ca[0], cb[0]) and np.array_equal(ca[1], cb[1])
+
+
+def test_lanes_are_independent():
+    """A mixed-loops batch equals each lane run alone (the pages' L-aware
+    batching check), bit for bit."""
+    w = synth.make_weights(SMALL16, 4, random_gains=True)
+    pr = synth.make_prompts(SMALL16.vocab, 3, 5, 9)
+    loops = [1, 3, 6]
+    _, t_b, l_b = _run(SMALL16, w, "int8", [0, 1, 2], loops, pr, 3, l_max=6)
+    for k in range(3):
+        _, t_1, l_1 = _run(SMALL16, w, "int8", [0], [loops[k]], pr[k:k + 1], 3, l_max=6)
+        assert np.array_equal(t_b[:, k], t_1[:, 0])
+        assert np.array_equal(l_b[:, k], l_1[:, 0])
+
+
+def test_safety_threshold_bracket():
+    """The check fires exactly when a loop iteration's residual norm exceeds
+    the threshold; the aborted lane emits no token and keeps its length."""
+    w = synth.make_weights(SMALL16, 5, random_gains=True)
+    pr = synth.make_prompts(SMALL16.vocab, 1, 4, 10)[0]
+    L = 5
+
+    def fresh():
+        o = oracle.LoopedOracle(SMALL16, w, "int4", 1, 12, L)
+        t = o.prefill(0, pr, L)["next_token"]
+        return o, t
+
+    o, t = fresh()
+    r = o.decode_step([0], [L], [t])
+    norms = o.norms[0][:L].copy()
+    assert np.all(np.isfinite(norms)) and r["status"][0] == oracle.LANE_OK
+    assert np.isclose(norms[-1], np.linalg.norm(r["x"][0]), rtol=1e-15)
+    # threshold = max norm: never strictly exceeded
+    o, t = fresh()
+    r = o.decode_step([0], [L], [t], float(norms.max()))
+    assert r["status"][0] == oracle.LANE_OK and r["tokens"][0] >= 0
+    for i in range(L):
+        thr = float(norms[i]) * (1 - 1e-6)
+        first = int(np.argmax(norms > thr))
+        o, t = fresh()
+        r = o.decode_step([0], [L], [t], thr)
+        assert r["status"][0] == oracle.LANE_ABORTED and r["tokens"][0] == -1
+        assert o.length[0] == len(pr)
+        ran = o.norms[0]
+        assert np.all(np.isfinite(ran[:first + 1])) and np.all(np.isnan(ran[first + 1:]))
+        # the aborted lane is skipped by the next step
+        r2 = o.decode_step([0], [L], [t], math.inf)
+        assert r2["status"][0] == oracle.LANE_ABORTED and o.length[0] == len(pr)
+
+
+def test_cache_gap_rejected():
+    w = synth.make_weights(SMALL16, 6)
+    o = oracle.LoopedOracle(SMALL16, w, "int4", 1, 12, 8)
+    t = o.prefill(0, [1, 2, 3], 2)["next_token"]
+    o.decode_step([0], [1], [t])                  # a lower L is allowed
+    with pytest.raises(oracle.CacheGapError):
+        o.decode_step([0], [2], [t])              # layer n_pre+1 misses the last position
+
+
+def test_prefill_equals_token_by_token():
+    w = synth.make_weights(SMALL16, 7, random_gains=True)
+    pr = synth.make_prompts(SMALL16.vocab, 1, 7, 12)[0]
+    a = oracle.LoopedOracle(SMALL16, w, "f16", 1, 8, 3)
+    ra = a.prefill(0, pr, 3)
+    b = oracle.LoopedOracle(SMALL16, w, "f16", 1, 8, 3)
+    b.prefill(0, pr[:1], 3)
+    last = None
+    for t in pr[1:]:
+        last = b.decode_step([0], [3], [t])["logits"][0]
+    assert np.allclose(ra["logits"][-1], last, rtol=0, atol=1e-12 * np.abs(last).max())
+
+
+def test_cache_bytes_closed_form():
+    # per-entry bytes at d_model 1024: fp16 K/V 4096, fp16-h 2048, INT8-h 1026, INT4-h 576
+    assert looped.cache_bytes("kv", 1024, "f16", 1, 1, 1, 0) == 4096
+    assert looped.entry_bytes("f16", 1024) == 2048
+    assert looped.entry_bytes("int8", 1024) == 1026
+    assert looped.entry_bytes("int4", 1024) == 576
+    assert looped.entry_bytes("int4", 2048) == 1152
+    # 4 lanes x 10 layers x 4224 positions x 576 B
+    assert looped.cache_bytes("int4", 1024, "f16", 4, 4224, 8, 2) == 97_320_960
+    assert looped.cache_bytes("kv", 1024, "f16", 4, 4224, 8, 2) == 692_060_160
