@@ -1,0 +1,234 @@
+"""Decode throughput of the store-h looped decoder on one MI355X.
+
+Workload (default): 407M-shaped looped decoder (d_model 1024, 16 heads x 64,
+MLP 4096, n_pre 2, loop block applied L = 8 times, vocab 32000, fp16 weights),
+INT4-h cache (group-32 absmax, fp16 scales), 4 lanes, 4096-token prompts, then
+greedy decode. A step is one tl_decode_step over the 4 lanes: every layer-
+iteration appends h, rebuilds K|V from the INT4 cache on MFMA, attends, runs
+W_o and the MLP, and checks the residual norm after every loop iteration.
+
+Prints one JSON line: decode tokens/s, the roofline of the dominant kernel
+(the reconstruction + attention kernel, timed with HIP events on the stream it
+runs on), and the CPU oracle timed on a bounded sample of the same workload.
+Inputs are synthetic (seeded weights ~ N(0, 0.02), uniform prompt ids).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(msg: str):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def recon_flops_bytes(shape, mode_entry_bytes, lanes, loops, t_values):
+    """Algorithmic work of the attention kernel over decode steps.
+
+    Per (lane, layer-iteration) with T cached positions: rebuilding K and V is
+    2 * T * D * 2D flops, scores and weighted values 4 * T * D; the h entries
+    streamed are T * entry_bytes, and W_k|W_v (2D x D fp16) once per launch.
+    Returns (flops, h_bytes, launches) summed over the given steps."""
+    D = shape.d_model
+    n_layers = shape.n_pre + max(loops)
+    flops = 0.0
+    hbytes = 0.0
+    launches = 0
+    for T in t_values:
+        for layer in range(n_layers):
+            active = [L for L in loops if shape.n_pre + L > layer]
+            flops += len(active) * (4.0 * T * D * D + 4.0 * T * D)
+            hbytes += len(active) * T * mode_entry_bytes
+            launches += 1
+    return flops, hbytes, launches
+
+
+def cpu_baseline(shape, w, mode, context, loops, budget_s=12.0, max_steps=8):
+    """The CPU oracle decoding one lane of the same workload (context `context`,
+    same mode and loops); the lane's cache is filled through the oracle's own
+    codec from N(0, 1) draws (the contents do not change the work)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    L = loops
+    orc = oracle.LoopedOracle(shape, w, mode, 1, context + max_steps + 1, L)
+    rng = np.random.default_rng(2)
+    n_layers = shape.n_pre + L
+    orc.prime_synthetic(0, range(n_layers), context,
+                        lambda layer: rng.standard_normal((context, shape.d_model)).astype(np.float32))
+    tok = 1
+    steps = 0
+    t0 = time.perf_counter()
+    while steps < max_steps:
+        r = orc.decode_step([0], [L], [tok])
+        tok = int(r["tokens"][0])
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "1 lane x %d decode steps at context %d, %s-h, L=%d, FP64 numpy oracle "
+                      "(%.1f s)" % (steps, context, mode, L, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--mode", default="int4", choices=["int4", "int8", "f16", "kv"])
+    ap.add_argument("--workload", default="407m-int4h-ctx4096-b4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile-pass", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: the decode step is measured per GPU; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from kv_compression_amd import tl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tl.load()
+    wl = synth.workload(args.workload)
+    shape = wl.shape
+    lanes = list(range(wl.lanes))
+    loops = wl.lane_loops()
+    K, W = args.steps, args.warmup
+    context = wl.context
+    max_seq = context + max(K, W) + 1
+    log("weights %s seed %d" % (shape.name, wl.seed_weights))
+    w = synth.make_weights(shape, wl.seed_weights)
+    model = tl.Model(shape, tl.upload_weights(shape, w))
+    cache = tl.Cache(model, args.mode, wl.lanes, max_seq, wl.l_max)
+    prompts = synth.make_prompts(shape.vocab, wl.lanes, context, wl.seed_prompt)
+    log("prefill %d lanes x %d tokens (%s)" % (wl.lanes, context, args.mode))
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    first = torch.empty(wl.lanes, dtype=torch.int32, device="cuda")
+    for k in lanes:
+        nxt, _ = cache.prefill(k, prompts[k], loops[k])
+        first[k:k + 1].copy_(nxt)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - tp0
+    log("prefill %.2f s" % prefill_s)
+    n_layers = shape.n_pre + max(loops)
+
+    ta = torch.empty(wl.lanes, dtype=torch.int32, device="cuda")
+    tb = torch.empty(wl.lanes, dtype=torch.int32, device="cuda")
+    st = torch.empty(wl.lanes, dtype=torch.int32, device="cuda")
+
+    def reset():
+        for k in lanes:
+            cache.tl_cache_set_length(k, context, n_layers)
+        ta.copy_(first)
+
+    def run(steps):
+        tin, tout = ta, tb
+        for _ in range(steps):
+            cache.tl_decode_step(lanes, loops, tin, wl.threshold, tout, None, st)
+            tin, tout = tout, tin
+        return tin
+
+    reset()
+    run(W)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    last = run(K)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    st_host = st.cpu().numpy()
+    assert np.all(st_host == 0), "a lane aborted during the benchmark"
+    tokens = wl.lanes * K
+    value = tokens / wall
+    log("decode %d steps: %.1f ms wall, %.1f ms events, %.0f tok/s" % (K, wall * 1e3, gpu_ms, value))
+
+    roof = None
+    extra = {}
+    if not args.no_profile_pass:
+        reset()
+        torch.cuda.synchronize()
+        cache.tl_profile_start()
+        run(K)
+        kern_ms, launches = cache.tl_profile_stop()
+        import oracle.looped as _ol  # entry-size closed form only (no oracle arithmetic)
+        eb = _ol.entry_bytes(args.mode, shape.d_model) if args.mode != "kv" else 4 * shape.d_model
+        t_values = [context + 1 + s for s in range(K)]
+        flops, hbytes, n_launch = recon_flops_bytes(shape, eb, lanes, loops, t_values)
+        assert n_launch == launches, (n_launch, launches)
+        avg_ms = kern_ms / launches
+        if args.mode == "kv":
+            achieved = hbytes / (kern_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+        else:
+            achieved = flops / (kern_ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None}
+        extra = {"kernel": "recon_attn" if args.mode != "kv" else "kv_attn",
+                 "kernel_avg_us": round(avg_ms * 1e3, 2), "kernel_launches": launches,
+                 "kernel_share_of_step": round(kern_ms / gpu_ms, 3),
+                 "flops_per_launch": flops / launches,
+                 "h_bytes_per_launch": hbytes / launches,
+                 "h_stream_GBs": round(hbytes / (kern_ms * 1e-3) / 1e9, 1)}
+        log("kernel: %d launches, avg %.1f us, %s" % (launches, avg_ms * 1e3, roof))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu oracle baseline")
+        cpu = cpu_baseline(shape, w, args.mode, context, max(loops))
+        log("cpu oracle %.3f tok/s (%s)" % (cpu["value"], cpu["sample"]))
+
+    out = {
+        "metric": "decode tok/s + reconstruct-attn MFMA % peak, 407M-shape L=8 INT4-h ctx 4096",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "model_shape": shape.name, "cache_mode": args.mode,
+                   "lanes": wl.lanes, "loops": loops[0] if len(set(loops)) == 1 else loops,
+                   "context": context, "decode_steps": K,
+                   "kv_bytes": cache.cache_bytes, "prefill_s": round(prefill_s, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * tl.h — C ABI of the store-h looped-decoder library (libtl.so, gfx950).
+ *
+ * The library runs one decode step of a weight-shared looped transformer
+ * (n_pre unique layers, then one loop block applied L times with the same
+ * W_q, W_k, W_v, W_o, norms and MLP at every iteration; TinyLoop
+ * architecture-exclusive features page, introduction) over a store-h KV
+ * cache: the cache keeps the pre-QKV norm output h of every token and every
+ * layer-iteration, and attention rebuilds K = W_k h and V = W_v h from it
+ * with the layer's own weights (same page, "Store-h KV cache"; novel
+ * contributions page, "Store-h KV Cache").
+ *
+ * Conventions shared by every call:
+ *  - Device memory belongs to the caller. The library never allocates device
+ *    memory; weights, the cache, the workspace and all inputs and outputs are
+ *    caller buffers. Pointers documented as "device" must be device memory
+ *    (hipMalloc / torch CUDA tensors); "host" pointers are ordinary memory.
+ *  - Every call is asynchronous on the given HIP stream (hipStream_t passed as
+ *    void*, NULL = the default stream) unless documented to synchronise.
+ *  - Every call returns a tl_status. Arguments are validated before anything
+ *    is enqueued; on an error nothing is enqueued, the cache is unchanged, and
+ *    tl_last_error() returns a message (thread-local).
+ *  - Calls on one cache must be serialised by the caller (one stream, or
+ *    external synchronisation). Weights must outlive the model; the cache and
+ *    workspace buffers must outlive the cache handle.
+ *  - Matrices are row-major with y = W x (W is [out, in]).
+ */
+#ifndef TL_H
+#define TL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TL_OK = 0,
+  TL_E_ARG = 1,          /* an argument is out of range or inconsistent */
+  TL_E_UNSUPPORTED = 2,  /* a shape / dtype / mode combination the kernels do not cover */
+  TL_E_CAPACITY = 3,     /* appending would pass max_seq positions */
+  TL_E_CACHE_GAP = 4,    /* a deeper L than the lane's upper layers were filled for */
+  TL_E_HIP = 5           /* a HIP runtime error; the cache contents are undefined */
+} tl_status;
+
+/* What one cache entry (one token, one layer-iteration) holds.
+ * KV:      K and V rows, model dtype (the stored-K/V baseline; measured-benchmarks
+ *          page, section 3, "FP16 KV baseline"), 2*D elements.
+ * H_F32:   h in fp32 (fp32 models only), 4*D bytes.
+ * H_F16:   h in fp16 (fp16 models), 2*D bytes.
+ * H_INT8:  h as int8 codes with one fp16 absmax scale per token, D + 2 bytes.
+ * H_INT4:  h as 4-bit codes with one fp16 absmax scale per 32 consecutive
+ *          d_model elements, D/2 + D/16 bytes.
+ * (features page, "Store-h KV cache": FP16-h, INT8-h and INT4-h modes.) */
+typedef enum {
+  TL_CACHE_KV = 0,
+  TL_CACHE_H_F32 = 1,
+  TL_CACHE_H_F16 = 2,
+  TL_CACHE_H_INT8 = 3,
+  TL_CACHE_H_INT4 = 4
+} tl_cache_mode;
+
+typedef enum { TL_LANE_OK = 0, TL_LANE_ABORTED = 1 } tl_lane_status;
+typedef enum { TL_DTYPE_F32 = 0, TL_DTYPE_F16 = 1 } tl_dtype;
+
+/* Model shape. Supported: d_model = n_heads * d_head; fp16 models with
+ * d_head in {64, 128}, d_model a multiple of 256; fp32 models with d_head 32
+ * and d_model 128. d_mlp a multiple of 128. */
+typedef struct {
+  int32_t d_model, n_heads, d_head, d_mlp, n_pre, vocab;
+  float norm_eps;   /* RMSNorm epsilon */
+  int32_t dtype;    /* tl_dtype: weights, h, and matrix-product operands */
+} tl_config;
+
+/* Device pointers (model dtype) of one unique layer. u = n_pre is the loop
+ * block shared by every loop iteration. */
+typedef struct {
+  const void* norm1;   /* [D]      RMSNorm gain before QKV */
+  const void* w_qkv;   /* [3D, D]  rows q | k | v, head-major inside each */
+  const void* w_o;     /* [D, D]   */
+  const void* norm2;   /* [D]      RMSNorm gain before the MLP */
+  const void* w_up;    /* [F, D]   */
+  const void* w_down;  /* [D, F]   */
+} tl_layer_weights;
+
+typedef struct {
+  const void* embed;                 /* [V, D] */
+  const void* final_norm;            /* [D]    */
+  const void* lm_head;               /* [V, D] */
+  const tl_layer_weights* layers;    /* host array of n_pre + 1 entries */
+} tl_weights;
+
+typedef struct tl_model tl_model;
+typedef struct tl_cache tl_cache;
+
+/* Library version (major * 100 + minor). */
+int tl_version(void);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* tl_last_error(void);
+
+/* Create a model handle over caller-owned device weights (borrowed, not
+ * copied). Host state only; enqueues nothing. */
+tl_status tl_model_create(const tl_config* cfg, const tl_weights* w, tl_model** out);
+void tl_model_destroy(tl_model* m);
+
+/* Exact payload bytes of a cache of n_pre + l_max layers x n_lanes x max_seq
+ * entries in `mode` (closed form; features page, "Variable-L KV cache": the
+ * cache is sized by n_pre + L_max). 0 if the arguments are invalid. */
+size_t tl_cache_bytes(const tl_config* cfg, int mode, int n_lanes, int max_seq, int l_max);
+
+/* Bytes of device workspace a cache needs: per-lane state (length, status,
+ * residual norms, last residual) and step scratch for up to
+ * min(n_lanes, 256) lanes per decode call and 512 tokens per prefill call. */
+size_t tl_workspace_bytes(const tl_config* cfg, int mode, int n_lanes, int max_seq, int l_max);
+
+/* Bind a cache to caller memory: d_cache (tl_cache_bytes) holds the entries,
+ * d_workspace (tl_workspace_bytes) the per-lane state and scratch. Enqueues a
+ * reset of every lane (length 0, status OK) on `stream`. A lane's cache layer
+ * n_pre + i is written only by loop iteration i, so it stays valid for every
+ * later call with loops >= i + 1. */
+tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, int l_max,
+                         void* d_cache, size_t cache_bytes, void* d_workspace, size_t ws_bytes,
+                         void* stream, tl_cache** out);
+/* Host state only; the caller frees the device buffers after the stream is idle. */
+void tl_cache_free(tl_cache* c);
+
+/* Prefill: append n_tokens (1..512) prompt tokens to `lane` at its current
+ * length and run them through n_pre + loops layers (chunked prefill; features
+ * page, closing list of supported techniques). Every layer first appends the
+ * chunk's h rows, then rebuilds K/V for all of the lane's positions and runs
+ * causal attention (query i at position len + i). Residual norms are not
+ * checked during prefill. d_tokens: device int32 [n_tokens].
+ * d_next_token (nullable): device int32 [1], greedy token after the chunk.
+ * d_last_logits (nullable): device f32 [vocab], logits of the chunk's last token.
+ * A lane left aborted by a decode step is skipped on the device (next token
+ * -1) until tl_cache_reset_lane.
+ * Errors: TL_E_ARG (loops not in 1..l_max, lane out of range, n_tokens out of
+ * range), TL_E_CAPACITY, TL_E_CACHE_GAP (the lane already holds positions and
+ * n_pre + loops exceeds the layers filled for them). */
+tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_tokens,
+                           int n_tokens, int32_t* d_next_token, float* d_last_logits,
+                           void* stream);
+
+/* One greedy decode step for n lanes (1..min(n_lanes, 256)), lane k running
+ * loops[k] iterations of the loop block (features page, "L-aware batching";
+ * lanes never interact, so a lane's result does not depend on its batch mates).
+ * lanes, loops: host int32 [n] (distinct lane ids; 1 <= loops[k] <= l_max).
+ * d_tokens_in: device int32 [n], the token at each lane's current position (ids
+ * outside [0, vocab) are clamped into it).
+ * safety_threshold: after every loop iteration the FP32 L2 norm of the lane's
+ * residual is compared with it and the lane aborts iff !(norm <= threshold)
+ * (novel-contributions page, "Per-Iteration Safety Check"); +INF turns the
+ * check off. An abort is not an error: the lane's remaining iterations and its
+ * token are skipped, d_lane_status[k] = TL_LANE_ABORTED, d_tokens_out[k] = -1,
+ * its length does not advance, and later calls skip it until
+ * tl_cache_reset_lane.
+ * d_tokens_out: device int32 [n]. d_logits (nullable): device f32 [n, vocab].
+ * d_lane_status: device int32 [n].
+ * Errors: TL_E_ARG, TL_E_CAPACITY, TL_E_CACHE_GAP (as for prefill). */
+tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t* loops,
+                         const int32_t* d_tokens_in, float safety_threshold,
+                         int32_t* d_tokens_out, float* d_logits, int32_t* d_lane_status,
+                         void* stream);
+
+/* Residual norms of `lane`'s last decode step, one per loop iteration
+ * (NaN for iterations that did not run). h_out: host float [l_max].
+ * Synchronises `stream`. */
+tl_status tl_residual_norms(const tl_cache* c, int lane, float* h_out, void* stream);
+
+/* Copy the lane's residual after its last decode step (f32 [d_model]) into
+ * device memory d_out. */
+tl_status tl_lane_residual(const tl_cache* c, int lane, float* d_out, void* stream);
+
+/* Write n rows of h (device, model dtype, [n, d_model]) into cache layer
+ * `layer` of `lane` at positions pos0 .. pos0+n-1 through the same encoder the
+ * step uses (KV mode: K = W_k h and V = W_v h of that layer are stored).
+ * Does not change the lane's length. */
+tl_status tl_cache_write_h(tl_cache* c, int lane, int layer, int pos0, int n, const void* d_h,
+                           void* stream);
+
+/* Fill positions pos0 .. pos0+n-1 of cache layer `layer` of `lane` with
+ * synthetic h drawn on the GPU: Philox4x32-10 (Salmon et al., SC'11) with
+ * counter (k, pos, lane, layer) and key (seed, 0x1F0E9D75); the eight 16-bit
+ * halves of the output are summed, centred (minus 262140) and multiplied in
+ * fp32 by 1/(65536*sqrt(2/3)) (bits 0x379CC471), then rounded to the model
+ * dtype and encoded like tl_cache_write_h. Does not change the lane's length. */
+tl_status tl_cache_fill_synthetic(tl_cache* c, int lane, int layer, int pos0, int n,
+                                  uint32_t seed, void* stream);
+
+/* Declare that `lane` holds `length` valid positions in its first
+ * `layers_valid` cache layers (after tl_cache_write_h / _fill_synthetic).
+ * Resets the lane's status to OK. */
+tl_status tl_cache_set_length(tl_cache* c, int lane, int length, int layers_valid, void* stream);
+
+/* Read entries of positions pos0 .. pos0+n-1 of layer `layer`, lane `lane`.
+ * d_codes (nullable, INT modes): device int8 [n, d_model], unpacked codes.
+ * d_scales (nullable, INT modes): device uint16 (fp16 bits) [n, groups]
+ *   (INT8: 1 group, INT4: d_model/32 groups).
+ * d_h (nullable): device, model dtype: [n, d_model] the h the attention uses
+ *   (dequantised fp16(q*s) for INT modes), or [n, 2*d_model] K|V in KV mode. */
+tl_status tl_cache_read(const tl_cache* c, int lane, int layer, int pos0, int n, int8_t* d_codes,
+                        uint16_t* d_scales, void* d_h, void* stream);
+
+/* Forget a lane: length 0, status OK, no valid layers. */
+tl_status tl_cache_reset_lane(tl_cache* c, int lane, void* stream);
+
+/* Kernel timing for measurement: between tl_profile_start and tl_profile_stop
+ * every launch of the decode attention kernel (store-h reconstruction +
+ * attention, or the stored-K/V streaming attention) made by tl_decode_step is
+ * bracketed with HIP events recorded on the call's stream. tl_profile_stop
+ * waits for the last event and returns the summed kernel time in milliseconds
+ * and the number of launches. Host-side events only; no device memory. */
+tl_status tl_profile_start(tl_cache* c);
+tl_status tl_profile_stop(tl_cache* c, double* total_ms, int* n_launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TL_H */

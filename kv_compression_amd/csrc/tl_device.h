@@ -1,0 +1,136 @@
+// Device helpers shared by the kernel translation units.
+#pragma once
+
+#include "tl_internal.h"
+
+namespace tl {
+
+template <typename T> struct DT;
+template <> struct DT<float> { static constexpr int id = TL_DTYPE_F32; };
+template <> struct DT<half_t> { static constexpr int id = TL_DTYPE_F16; };
+
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(half_t v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ half_t from_f<half_t>(float v) { return (half_t)v; }
+
+__device__ __forceinline__ uint16_t h_bits(half_t v) { return __builtin_bit_cast(uint16_t, v); }
+__device__ __forceinline__ half_t h_from_bits(uint16_t b) { return __builtin_bit_cast(half_t, b); }
+
+// Warp (64-lane) reductions in a fixed butterfly order.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block reductions (blockDim.x a multiple of 64, at most 1024). Every thread
+// gets the result. The partial of wave w is combined in order w = 0, 1, ...
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = red[0];
+  for (int i = 1; i < nw; ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// h codec: symmetric absmax, fp16 scale (IEEE fp32 divide, round half to even)
+// ---------------------------------------------------------------------------
+// scale = fp16(absmax / qmax)
+__device__ __forceinline__ half_t codec_scale(float absmax, float qmax) {
+  return (half_t)__fdiv_rn(absmax, qmax);
+}
+// q = clamp(rint(h / s), qmin, qmax), 0 when s == 0
+__device__ __forceinline__ int codec_code(float h, float s, float qmin, float qmax) {
+  if (s == 0.f) return 0;
+  float q = rintf(__fdiv_rn(h, s));
+  q = fminf(fmaxf(q, qmin), qmax);
+  return (int)q;
+}
+
+// INT4 nibble placement inside a 32-bit word of 8 consecutive elements
+// e0..e7: element j sits at bit 4*(j/2) for even j and 16 + 4*(j/2) for odd j,
+// so (w >> 4i) & 0x000F000F yields the pair (e_2i, e_2i+1) in the two halves
+// of a word. Codes are stored offset by 8 (0..15).
+__device__ __forceinline__ int int4_shift(int j) { return (j & 1) ? 16 + 4 * (j >> 1) : 4 * (j >> 1); }
+
+// Dequantise 8 INT4 codes (one word) with scale s into 8 fp16: fp16(q * s).
+// (1024 + u) is exact in fp16; subtracting 1032 gives q exactly; the product
+// with s is one correctly rounded fp16 multiply.
+__device__ __forceinline__ half8 int4_dequant8(uint32_t w, half_t s) {
+  half8 r;
+  const half2v bias = {(half_t)1032.f, (half_t)1032.f};
+  const half2v sv = {s, s};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t v = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+    half2v x = __builtin_bit_cast(half2v, v);
+    x = (x - bias) * sv;
+    r[2 * i] = x[0];
+    r[2 * i + 1] = x[1];
+  }
+  return r;
+}
+
+// Dequantise 4 INT8 codes (one word, two's complement bytes) into fp16(q * s).
+// (byte ^ 0x80) | 0x6400 = 1024 + (q + 128) exactly; minus 1152 gives q.
+__device__ __forceinline__ half4 int8_dequant4(uint32_t w, half_t s) {
+  const uint32_t f = w ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, f, 0x07010700u);  // bytes b1,b0 -> halves
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, f, 0x07030702u);
+  const half2v bias = {(half_t)1152.f, (half_t)1152.f};
+  const half2v sv = {s, s};
+  half2v a = (__builtin_bit_cast(half2v, lo) - bias) * sv;
+  half2v b = (__builtin_bit_cast(half2v, hi) - bias) * sv;
+  half4 r = {a[0], a[1], b[0], b[1]};
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) for synthetic inputs
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+  }
+}
+// Synthetic h element: centred sum of the eight 16-bit halves, one fp32 multiply.
+__device__ __forceinline__ float synth_h(uint32_t seed, int layer, int lane, int pos, int k) {
+  uint32_t c[4] = {(uint32_t)k, (uint32_t)pos, (uint32_t)lane, (uint32_t)layer};
+  philox4x32_10(c, seed, 0x1F0E9D75u);
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += (int)(c[i] & 0xFFFFu) + (int)(c[i] >> 16);
+  return (float)(s - 262140) * __builtin_bit_cast(float, 0x379CC471u);
+}
+
+__device__ __forceinline__ float gelu_f(float v) {
+  return 0.5f * v * (1.f + erff(v * 0.70710678118654752f));
+}
+
+}  // namespace tl

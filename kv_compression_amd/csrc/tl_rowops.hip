@@ -1,0 +1,422 @@
+// Row-wise kernels of the decode step: setup + embedding gather, RMSNorm +
+// h encode + cache append, residual-norm safety check, argmax/finish, and the
+// cache test hooks.
+//
+// The h codec follows the INT8-h / INT4-h store-h modes (TinyLoop
+// architecture-exclusive features page, "Store-h KV cache"): symmetric absmax
+// with an fp16 scale, one scale per token (INT8) or per 32 consecutive d_model
+// elements (INT4), codes clamp(rint(h / s)) computed with an IEEE fp32 divide
+// and round-half-to-even.
+#include "tl_device.h"
+
+namespace tl {
+
+namespace {
+
+constexpr int kRowThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void step_setup_kernel(ModelView m, Workspace ws,
+                                                                 StepMap map,
+                                                                 const int32_t* tokens_in,
+                                                                 int l_max) {
+  const int r = blockIdx.x;
+  const int lane = map.lane[r], slot = map.slot[r];
+  const int st = ws.status[lane];
+  if (threadIdx.x == 0) {
+    ws.row_lane[r] = lane;
+    ws.row_slot[r] = slot;
+    ws.row_pos[r] = st == TL_LANE_ABORTED ? -1 : ws.len[lane];
+  }
+  if (st == TL_LANE_ABORTED) return;
+  for (int i = threadIdx.x; i < l_max; i += blockDim.x) ws.norms[(size_t)lane * l_max + i] = __builtin_nanf("");
+  // ids outside [0, vocab) are clamped so the gather stays inside the table
+  const int tok = min(max(tokens_in[slot], 0), m.V - 1);
+  const T* e = (const T*)m.embed + (size_t)tok * m.D;
+  for (int i = threadIdx.x; i < m.D; i += blockDim.x) ws.x[(size_t)r * m.D + i] = to_f(e[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void prefill_setup_kernel(ModelView m, Workspace ws,
+                                                                    int lane, const int32_t* tokens,
+                                                                    int pos0) {
+  const int r = blockIdx.x;
+  if (threadIdx.x == 0) {
+    ws.row_lane[r] = lane;
+    ws.row_pos[r] = pos0 + r;
+  }
+  const int tok = min(max(tokens[r], 0), m.V - 1);
+  const T* e = (const T*)m.embed + (size_t)tok * m.D;
+  for (int i = threadIdx.x; i < m.D; i += blockDim.x) ws.x[(size_t)r * m.D + i] = to_f(e[i]);
+}
+
+// One block per row; thread t owns elements [t*EPT, t*EPT + EPT).
+template <typename T, int EPT>
+__global__ __launch_bounds__(kRowThreads) void norm_append_kernel(ModelView m, CacheView c,
+                                                                  AppendArgs a) {
+  __shared__ float red[kRowThreads / 64];
+  const int r = blockIdx.x;
+  const int lane = a.row_lane ? a.row_lane[r] : a.fixed_lane;
+  const int pos = a.row_pos ? a.row_pos[r] : a.pos0 + r;
+  if (a.status && a.status[lane] == TL_LANE_ABORTED) return;
+  const int D = m.D;
+  const int e0 = threadIdx.x * EPT;
+  float h[EPT];
+  if (a.src == HS_NORM) {
+    float xv[EPT];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      xv[i] = a.x[(size_t)r * D + e0 + i];
+      ss += xv[i] * xv[i];
+    }
+    ss = block_sum(ss, red);
+    const float inv = __fdiv_rn(1.f, __fsqrt_rn(__fdiv_rn(ss, (float)D) + m.eps));
+    const T* g = (const T*)a.gain;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) h[i] = to_f(from_f<T>(xv[i] * inv * to_f(g[e0 + i])));
+  } else if (a.src == HS_INPUT) {
+    const T* hi = (const T*)a.h_in + (size_t)r * D;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) h[i] = to_f(hi[e0 + i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      h[i] = to_f(from_f<T>(synth_h(a.seed, a.layer, lane, pos, e0 + i)));
+  }
+  if (a.h_out) {
+    T* ho = (T*)a.h_out + (size_t)r * D;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) ho[e0 + i] = from_f<T>(h[i]);
+  }
+  if (c.mode == TL_CACHE_KV) return;
+  const int kb = e0 / kKBlock, w = e0 % kKBlock;
+  char* row = c.code_row(a.layer, lane, kb, pos);
+  if (c.mode == TL_CACHE_H_F32 || c.mode == TL_CACHE_H_F16) {
+    T* dst = (T*)row + w;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) dst[i] = from_f<T>(h[i]);
+    return;
+  }
+  if (c.mode == TL_CACHE_H_INT8) {
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) am = fmaxf(am, fabsf(h[i]));
+    am = block_max(am, red);
+    const half_t s = codec_scale(am, 127.f);
+    const float sf = (float)s;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) ((int8_t*)row)[w + i] = (int8_t)codec_code(h[i], sf, -127.f, 127.f);
+    if (threadIdx.x == 0) *c.int8_scale(a.layer, lane, pos) = h_bits(s);
+    return;
+  }
+  // INT4: group of 32 elements = 32 / EPT consecutive threads
+  constexpr int TPG = kInt4Group / EPT;
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) am = fmaxf(am, fabsf(h[i]));
+#pragma unroll
+  for (int o = 1; o < TPG; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+  const half_t s = codec_scale(am, 7.f);
+  const float sf = (float)s;
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int q = codec_code(h[i], sf, -8.f, 7.f);
+    word |= (uint32_t)(q + 8) << int4_shift((e0 + i) & 7);
+  }
+  static_assert(EPT <= 8, "one INT4 word per thread at most");
+  if constexpr (EPT < 8) {
+    constexpr int TPW = 8 / EPT;   // threads sharing one word
+#pragma unroll
+    for (int o = 1; o < TPW; o <<= 1) word |= __shfl_xor(word, o, 64);
+    if ((threadIdx.x % TPW) == 0) ((uint32_t*)row)[w / 8] = word;
+  } else {
+    ((uint32_t*)row)[w / 8] = word;
+  }
+  if ((e0 % kInt4Group) == 0) {
+    const int g = e0 / kInt4Group;
+    c.int4_scale(a.layer, lane, g / 2, pos)[g & 1] = h_bits(s);
+  }
+}
+
+template <typename T, int EPT>
+__global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(ModelView m, const float* x,
+                                                              const void* gain, void* out,
+                                                              const int32_t* row_lane,
+                                                              const int32_t* status) {
+  __shared__ float red[kRowThreads / 64];
+  const int r = blockIdx.x;
+  if (status && status[row_lane[r]] == TL_LANE_ABORTED) return;
+  const int D = m.D, e0 = threadIdx.x * EPT;
+  float xv[EPT], ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    xv[i] = x[(size_t)r * D + e0 + i];
+    ss += xv[i] * xv[i];
+  }
+  ss = block_sum(ss, red);
+  const float inv = __fdiv_rn(1.f, __fsqrt_rn(__fdiv_rn(ss, (float)D) + m.eps));
+  const T* g = (const T*)gain;
+  T* o = (T*)out + (size_t)r * D;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) o[e0 + i] = from_f<T>(xv[i] * inv * to_f(g[e0 + i]));
+}
+
+template <int EPT>
+__global__ __launch_bounds__(kRowThreads) void resid_norm_kernel(int D, const float* x,
+                                                                 const int32_t* row_lane,
+                                                                 int32_t* status, float* norms,
+                                                                 int l_max, int iter, int check,
+                                                                 float thr) {
+  __shared__ float red[kRowThreads / 64];
+  const int r = blockIdx.x;
+  const int lane = row_lane[r];
+  if (status[lane] == TL_LANE_ABORTED) return;
+  const int e0 = threadIdx.x * EPT;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const float v = x[(size_t)r * D + e0 + i];
+    ss += v * v;
+  }
+  ss = block_sum(ss, red);
+  if (threadIdx.x == 0) {
+    const float nrm = __fsqrt_rn(ss);
+    norms[(size_t)lane * l_max + iter] = nrm;
+    if (check && !(nrm <= thr)) status[lane] = TL_LANE_ABORTED;
+  }
+}
+
+// argmax with ties to the lowest index: (value, index) pairs, larger value
+// wins, equal values keep the smaller index.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+__device__ int block_argmax(const float* lg, int V) {
+  __shared__ float sv[kRowThreads / 64];
+  __shared__ int si[kRowThreads / 64];
+  float best = -__builtin_inff();
+  int bi = 0x7fffffff;
+  for (int j = threadIdx.x; j < V; j += blockDim.x) argmax_merge(best, bi, lg[j], j);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(best, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    argmax_merge(best, bi, v2, i2);
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  float b = sv[0];
+  int ib = si[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_merge(b, ib, sv[w], si[w]);
+  return ib == 0x7fffffff ? 0 : ib;
+}
+
+__global__ __launch_bounds__(kRowThreads) void finish_kernel(ModelView m, Workspace ws,
+                                                             const float* logits, int ld,
+                                                             int by_slot, int32_t* tokens_out,
+                                                             int32_t* lane_status,
+                                                             float* user_logits) {
+  const int r = blockIdx.x;
+  const int lane = ws.row_lane[r], slot = ws.row_slot[r];
+  const bool started = ws.row_pos[r] >= 0;
+  if (ws.status[lane] == TL_LANE_ABORTED) {
+    if (threadIdx.x == 0) { tokens_out[slot] = -1; lane_status[slot] = TL_LANE_ABORTED; }
+    if (user_logits)
+      for (int j = threadIdx.x; j < m.V; j += blockDim.x)
+        user_logits[(size_t)slot * m.V + j] = __builtin_nanf("");
+    if (started)
+      for (int i = threadIdx.x; i < m.D; i += blockDim.x)
+        ws.xres[(size_t)lane * m.D + i] = ws.x[(size_t)r * m.D + i];
+    return;
+  }
+  const float* lg = logits + (size_t)(by_slot ? slot : r) * ld;
+  const int tok = block_argmax(lg, m.V);
+  for (int i = threadIdx.x; i < m.D; i += blockDim.x)
+    ws.xres[(size_t)lane * m.D + i] = ws.x[(size_t)r * m.D + i];
+  if (threadIdx.x == 0) {
+    tokens_out[slot] = tok;
+    lane_status[slot] = TL_LANE_OK;
+    ws.len[lane] = ws.row_pos[r] + 1;
+  }
+}
+
+__global__ __launch_bounds__(kRowThreads) void prefill_finish_kernel(ModelView m, Workspace ws,
+                                                                     int lane, int new_len,
+                                                                     const float* logits,
+                                                                     int32_t* next_token) {
+  if (ws.status[lane] == TL_LANE_ABORTED) {
+    if (threadIdx.x == 0 && next_token) *next_token = -1;
+    return;
+  }
+  const int tok = block_argmax(logits, m.V);
+  if (threadIdx.x == 0) {
+    if (next_token) *next_token = tok;
+    ws.len[lane] = new_len;
+  }
+}
+
+__global__ void lane_reset_kernel(Workspace ws, int l0, int n, int l_max, int length) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    ws.len[l0 + i] = length;
+    ws.status[l0 + i] = TL_LANE_OK;
+  }
+  for (int j = i; j < n * l_max; j += gridDim.x * blockDim.x)
+    ws.norms[(size_t)l0 * l_max + j] = __builtin_nanf("");
+}
+
+// One block per (row); threads over d_model.
+template <typename T>
+__global__ void cache_read_kernel(ModelView m, CacheView c, int lane, int layer, int pos0,
+                                  int8_t* codes, uint16_t* scales, void* hout) {
+  const int r = blockIdx.x, pos = pos0 + r, D = m.D;
+  if (c.mode == TL_CACHE_KV) {
+    if (!hout) return;
+    const T* src = (const T*)c.kv_row(layer, lane, pos);
+    for (int e = threadIdx.x; e < 2 * D; e += blockDim.x) ((T*)hout)[(size_t)r * 2 * D + e] = src[e];
+    return;
+  }
+  for (int e = threadIdx.x; e < D; e += blockDim.x) {
+    const int kb = e / kKBlock, w = e % kKBlock;
+    const char* row = c.code_row(layer, lane, kb, pos);
+    if (c.mode == TL_CACHE_H_F32 || c.mode == TL_CACHE_H_F16) {
+      if (hout) ((T*)hout)[(size_t)r * D + e] = ((const T*)row)[w];
+      continue;
+    }
+    int q;
+    half_t s;
+    if (c.mode == TL_CACHE_H_INT8) {
+      q = ((const int8_t*)row)[w];
+      s = h_from_bits(*c.int8_scale(layer, lane, pos));
+      if (scales && e == 0) scales[r] = h_bits(s);
+    } else {
+      const uint32_t word = ((const uint32_t*)row)[w / 8];
+      q = (int)((word >> int4_shift(w & 7)) & 0xF) - 8;
+      const int g = e / kInt4Group;
+      s = h_from_bits(c.int4_scale(layer, lane, kb, pos)[g & 1]);
+      if (scales && (e % kInt4Group) == 0) scales[(size_t)r * (D / kInt4Group) + g] = h_bits(s);
+    }
+    if (codes) codes[(size_t)r * D + e] = (int8_t)q;
+    if (hout) ((T*)hout)[(size_t)r * D + e] = (half_t)((float)q * (float)s);
+  }
+}
+
+__global__ void copy_f32_kernel(const float* src, float* dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+int row_threads(int D) { return D < kRowThreads ? D : kRowThreads; }
+
+}  // namespace
+
+hipError_t launch_step_setup(const ModelView& m, const Workspace& ws, const StepMap& map,
+                             const int32_t* tokens_in, int l_max, hipStream_t s) {
+  if (m.dtype == TL_DTYPE_F32)
+    step_setup_kernel<float><<<map.n, kRowThreads, 0, s>>>(m, ws, map, tokens_in, l_max);
+  else
+    step_setup_kernel<half_t><<<map.n, kRowThreads, 0, s>>>(m, ws, map, tokens_in, l_max);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_setup(const ModelView& m, const Workspace& ws, int lane, int n,
+                                const int32_t* tokens, int pos0, hipStream_t s) {
+  if (m.dtype == TL_DTYPE_F32)
+    prefill_setup_kernel<float><<<n, kRowThreads, 0, s>>>(m, ws, lane, tokens, pos0);
+  else
+    prefill_setup_kernel<half_t><<<n, kRowThreads, 0, s>>>(m, ws, lane, tokens, pos0);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_append(const ModelView& m, const CacheView& c, const AppendArgs& a,
+                              hipStream_t s) {
+  const int nt = row_threads(m.D);
+  const int ept = m.D / nt;
+  if (m.dtype == TL_DTYPE_F32) {
+    if (ept != 1) return hipErrorInvalidValue;
+    norm_append_kernel<float, 1><<<a.n, nt, 0, s>>>(m, c, a);
+  } else if (ept == 1) {
+    norm_append_kernel<half_t, 1><<<a.n, nt, 0, s>>>(m, c, a);
+  } else if (ept == 4) {
+    norm_append_kernel<half_t, 4><<<a.n, nt, 0, s>>>(m, c, a);
+  } else if (ept == 8) {
+    norm_append_kernel<half_t, 8><<<a.n, nt, 0, s>>>(m, c, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const ModelView& m, int n, const float* x, const void* gain, void* out,
+                          const int32_t* row_lane, const int32_t* status, hipStream_t s) {
+  const int nt = row_threads(m.D);
+  const int ept = m.D / nt;
+  if (m.dtype == TL_DTYPE_F32 && ept == 1)
+    rmsnorm_kernel<float, 1><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status);
+  else if (m.dtype == TL_DTYPE_F16 && ept == 1)
+    rmsnorm_kernel<half_t, 1><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status);
+  else if (m.dtype == TL_DTYPE_F16 && ept == 4)
+    rmsnorm_kernel<half_t, 4><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status);
+  else if (m.dtype == TL_DTYPE_F16 && ept == 8)
+    rmsnorm_kernel<half_t, 8><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_norm(const ModelView& m, int n, const float* x, const int32_t* row_lane,
+                             int32_t* status, float* norms, int l_max, int iter, int check,
+                             float thr, hipStream_t s) {
+  const int nt = row_threads(m.D);
+  const int ept = m.D / nt;
+  if (ept == 1)
+    resid_norm_kernel<1><<<n, nt, 0, s>>>(m.D, x, row_lane, status, norms, l_max, iter, check, thr);
+  else if (ept == 4)
+    resid_norm_kernel<4><<<n, nt, 0, s>>>(m.D, x, row_lane, status, norms, l_max, iter, check, thr);
+  else if (ept == 8)
+    resid_norm_kernel<8><<<n, nt, 0, s>>>(m.D, x, row_lane, status, norms, l_max, iter, check, thr);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_finish(const ModelView& m, const Workspace& ws, int n, const float* logits,
+                         int ld_logits, int logits_by_slot, int32_t* tokens_out,
+                         int32_t* lane_status, float* user_logits, hipStream_t s) {
+  finish_kernel<<<n, kRowThreads, 0, s>>>(m, ws, logits, ld_logits, logits_by_slot, tokens_out,
+                                          lane_status, user_logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_finish(const ModelView& m, const Workspace& ws, int lane, int new_len,
+                                 const float* logits, int32_t* next_token, hipStream_t s) {
+  prefill_finish_kernel<<<1, kRowThreads, 0, s>>>(m, ws, lane, new_len, logits, next_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_lane_reset(const Workspace& ws, int l0, int n, int l_max, int length,
+                             hipStream_t s) {
+  const int blocks = (n * l_max + 255) / 256 + 1;
+  lane_reset_kernel<<<blocks < 1024 ? blocks : 1024, 256, 0, s>>>(ws, l0, n, l_max, length);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_read(const ModelView& m, const CacheView& c, int lane, int layer, int pos0,
+                             int n, int8_t* codes, uint16_t* scales, void* h, hipStream_t s) {
+  if (m.dtype == TL_DTYPE_F32)
+    cache_read_kernel<float><<<n, 256, 0, s>>>(m, c, lane, layer, pos0, codes, scales, h);
+  else
+    cache_read_kernel<half_t><<<n, 256, 0, s>>>(m, c, lane, layer, pos0, codes, scales, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s) {
+  const size_t blocks = (n + 255) / 256;
+  copy_f32_kernel<<<blocks < 1024 ? (unsigned)blocks : 1024u, 256, 0, s>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace tl

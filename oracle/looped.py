@@ -121,7 +121,10 @@ def decode_int(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     D = q.shape[-1]
     group = D // s.shape[-1]
     qf = q.astype(np.float32).reshape(q.shape[:-1] + (D // group, group))
-    return (qf * s.astype(np.float32)[..., None]).astype(np.float16).reshape(q.shape)
+    # near the fp16 maximum the rounded product can overflow to +-inf (e.g. h = 65504:
+    # s = fp16(65504 / 7) = 9360, q = 7, q * s = 65520); that is part of the codec
+    with np.errstate(over="ignore"):
+        return (qf * s.astype(np.float32)[..., None]).astype(np.float16).reshape(q.shape)
 
 
 def int8_encode(h16):
