@@ -100,26 +100,53 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(ModelView m, ReconArgs a, 
   for (int i = 0; i < EPT; ++i) dst[2 + (e0 % DH) + i] = o[i];
 }
 
-template <typename T>
-__global__ void merge_kernel(int D, int H, int DH, const int32_t* row_lane, const int32_t* row_pos,
-                             const int32_t* status, const float* part, int S, int split_len,
-                             void* out) {
+// One block of 256 threads per (row, head). The split weights exp(m_s - M)
+// are computed once per split into LDS; thread (dim, group g) then sums the
+// splits s = g, g + G, ... for its dimension, and the G group sums are added
+// in order g = 0, 1, ... . The summation order depends only on T.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void merge_kernel(int D, int H, const int32_t* row_lane,
+                                                    const int32_t* row_pos, const int32_t* status,
+                                                    const float* part, int S, int split_len,
+                                                    void* out) {
+  constexpr int G = 256 / DH, CH = 1024;
+  __shared__ float wgt[CH];
+  __shared__ float red[4];
+  __shared__ float osum[G][DH];
+  __shared__ float lsum[G];
   const int r = blockIdx.x / H, head = blockIdx.x % H;
   if (status[row_lane[r]] == TL_LANE_ABORTED) return;
   const int Tn = row_pos[r] + 1;
   const int ns = (Tn + split_len - 1) / split_len;
   const float* p = part + ((size_t)r * H + head) * S * (DH + 2);
+  const int t = threadIdx.x, dim = t % DH, g = t / DH;
   float M = -__builtin_inff();
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p[(size_t)s * (DH + 2)]);
-  float L = 0.f, acc = 0.f;
-  const int dim = threadIdx.x;
-  for (int s = 0; s < ns; ++s) {
-    const float* ps = p + (size_t)s * (DH + 2);
-    const float w = exp2f((ps[0] - M) * kLog2e);
-    L += ps[1] * w;
-    acc += ps[2 + dim] * w;
+  for (int s = t; s < ns; s += 256) M = fmaxf(M, p[(size_t)s * (DH + 2)]);
+  M = block_max(M, red);
+  float acc = 0.f, lacc = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += CH) {
+    const int cend = min(ns, c0 + CH);
+    __syncthreads();
+    for (int s = c0 + t; s < cend; s += 256) wgt[s - c0] = exp2f((p[(size_t)s * (DH + 2)] - M) * kLog2e);
+    __syncthreads();
+    for (int s = c0 + g; s < cend; s += G) {
+      const float* ps = p + (size_t)s * (DH + 2);
+      const float w = wgt[s - c0];
+      acc = fmaf(ps[2 + dim], w, acc);
+      if (dim == 0) lacc = fmaf(ps[1], w, lacc);
+    }
   }
-  ((T*)out)[(size_t)r * D + head * DH + dim] = from_f<T>(__fdiv_rn(acc, L));
+  osum[g][dim] = acc;
+  if (dim == 0) lsum[g] = lacc;
+  __syncthreads();
+  if (g != 0) return;
+  float o = 0.f, L = 0.f;
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    o += osum[k][dim];
+    L += lsum[k];
+  }
+  ((T*)out)[(size_t)r * D + head * DH + dim] = from_f<T>(__fdiv_rn(o, L));
 }
 
 // One block per (head, 64 queries); four threads per query, each owning
@@ -218,12 +245,15 @@ hipError_t launch_kv_attn(const ModelView& m, const ReconArgs& a, hipStream_t s)
 hipError_t launch_attn_merge(const ModelView& m, int n_rows, const int32_t* row_lane,
                              const int32_t* row_pos, const int32_t* status, const float* part,
                              int S, int split_len, void* o, hipStream_t s) {
-  if (m.dtype == TL_DTYPE_F32)
-    merge_kernel<float><<<n_rows * m.H, m.dh, 0, s>>>(m.D, m.H, m.dh, row_lane, row_pos, status,
-                                                      part, S, split_len, o);
-  else
-    merge_kernel<half_t><<<n_rows * m.H, m.dh, 0, s>>>(m.D, m.H, m.dh, row_lane, row_pos, status,
-                                                       part, S, split_len, o);
+  const int grid = n_rows * m.H;
+#define TL_MG(T_, DH_)                                                                    \
+  merge_kernel<T_, DH_><<<grid, 256, 0, s>>>(m.D, m.H, row_lane, row_pos, status, part, S, \
+                                              split_len, o)
+  if (m.dtype == TL_DTYPE_F32 && m.dh == 32) TL_MG(float, 32);
+  else if (m.dtype == TL_DTYPE_F16 && m.dh == 64) TL_MG(half_t, 64);
+  else if (m.dtype == TL_DTYPE_F16 && m.dh == 128) TL_MG(half_t, 128);
+  else return hipErrorInvalidValue;
+#undef TL_MG
   return hipGetLastError();
 }
 

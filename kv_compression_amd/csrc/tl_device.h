@@ -68,6 +68,14 @@ __device__ __forceinline__ int codec_code(float h, float s, float qmin, float qm
   return (int)q;
 }
 
+// Order of the codes inside one 64-element block row of an INT4 / INT8 cache
+// entry: the row is split into two halves; half hb holds, for k-steps
+// kk = 0..3, the 8 elements 16*kk + 8*hb .. 16*kk + 8*hb + 7. That is exactly
+// the run of k values one half-wave feeds to a 32x32x16 MFMA, so a lane reads
+// its four k-steps' codes as one contiguous 16-byte (INT4) or 32-byte (INT8)
+// load. Returns the index of the 8-element group holding element w (0..63).
+__host__ __device__ __forceinline__ int code_group(int w) { return ((w >> 3) & 1) * 4 + (w >> 4); }
+
 // INT4 nibble placement inside a 32-bit word of 8 consecutive elements
 // e0..e7: element j sits at bit 4*(j/2) for even j and 16 + 4*(j/2) for odd j,
 // so (w >> 4i) & 0x000F000F yields the pair (e_2i, e_2i+1) in the two halves
@@ -126,7 +134,11 @@ __device__ __forceinline__ float synth_h(uint32_t seed, int layer, int lane, int
   int s = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) s += (int)(c[i] & 0xFFFFu) + (int)(c[i] >> 16);
-  return (float)(s - 262140) * __builtin_bit_cast(float, 0x379CC471u);
+  float v = (float)(s - 262140) * __builtin_bit_cast(float, 0x379CC471u);
+  // keep the fp32 rounding of the product: without this the backend folds a
+  // later fp16 conversion into one mixed-precision FMA that rounds only once
+  __asm__ volatile("" : "+v"(v));
+  return v;
 }
 
 __device__ __forceinline__ float gelu_f(float v) {

@@ -25,7 +25,7 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Bytes of one tiled block row (kKBlock d_model elements of one position).
-__host__ __device__ inline int block_row_bytes(int mode) {
+constexpr __host__ __device__ inline int block_row_bytes(int mode) {
   switch (mode) {
     case TL_CACHE_H_F32: return kKBlock * 4;
     case TL_CACHE_H_F16: return kKBlock * 2;

@@ -6,31 +6,42 @@
 //
 // One workgroup computes the product tile C[f, j] = sum_k W[f, k] h'[j, k] for
 // BF features (the K and V rows of whole heads) and BJ cached positions of one
-// lane, streaming d_model in BK-deep stages:
-//   * W rows (fp16, from L2 / MALL) and the stored h entries (INT4 / INT8
-//     codes + fp16 scales, or fp16 / fp32 h, from HBM) are loaded one stage
-//     ahead into registers; h codes are dequantised to fp16(q * s) on the way
-//     into LDS, so the MFMA operands are exactly the dequantised cache values;
-//   * both tiles sit in LDS (double buffered, rows padded to 144 B so the
-//     16-byte fragment reads of 16 lanes hit disjoint banks);
-//   * four waves, 2 x 2, each own a 128 x 128 tile (fp16: 4 x 4
-//     v_mfma_f32_32x32x16_f16 blocks, 256 accumulators per lane).
-// The decode epilogue reads the scores q . K_j out of the MFMA accumulator
-// layout (features in rows, positions in columns, so each lane holds one
-// position), applies a wave-level online softmax and reduces p_j V_j across
-// lanes, writing (max, sum, o) per (row, head, 128-position split).
+// lane, streaming d_model in BK = 64 deep stages. Four waves, 2 x 2, each own
+// a 128 x 128 tile (fp16: 4 x 4 v_mfma_f32_32x32x16_f16 blocks, 256
+// accumulators per lane); features run down the MFMA rows and positions along
+// its columns, so each lane ends up holding whole positions.
+//   * W rows (fp16, L2-resident: consecutive workgroups take different head
+//     groups, i.e. different XCDs, so each XCD streams one head group's rows)
+//     are loaded one stage ahead into registers and staged through LDS (double
+//     buffered, rows padded to 144 B: the 16-byte fragment reads of 16 lanes
+//     hit disjoint banks).
+//   * INT4 / INT8 h never goes through LDS: each lane loads the codes of its
+//     own positions for the next stages straight from the cache (the block
+//     rows are laid out so that one half-wave's k-run is contiguous) and
+//     dequantises them in registers into MFMA operands, fp16(q * s) exactly.
+//     That halves the LDS traffic per MFMA compared with staging both
+//     operands. fp16 / fp32 h (no dequantisation) is staged through LDS.
+// The decode epilogue reads the scores q . K_j out of the accumulators,
+// applies a wave-level online softmax and reduces p_j V_j across lanes,
+// writing (max, sum, o) per (row, head, 128-position split).
+#include <type_traits>
+
 #include "tl_device.h"
 
 namespace tl {
 
 namespace {
 
+// Tile shapes. fp16: 8 waves (2 per SIMD, 128 accumulators each) so that one
+// wave's waits are covered by the other wave's MFMAs; fp32: 4 waves.
 template <typename T> struct Cfg;
 template <> struct Cfg<half_t> {
-  static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 128, BK = 64;
+  static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 64, BK = 64;
+  static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
 template <> struct Cfg<float> {
   static constexpr int BF = 128, BJ = 128, WF = 64, WJ = 64, BK = 64;
+  static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
 
 enum { EPI_ATTN = 0, EPI_KVSTORE = 1 };
@@ -58,7 +69,7 @@ struct KArgs {
   int layer;
   const void* w_qkv;
   int D, H;
-  int n_hg, n_ptiles;
+  int n_hg, n_ptiles, n_rows;
   // decode
   const int32_t* row_lane;
   const int32_t* row_pos;
@@ -71,37 +82,101 @@ struct KArgs {
   void* kvbuf;
 };
 
-// chunks of 16 bytes per thread per stage for the h tile
-template <int MODE> struct HLoad;
-template <> struct HLoad<TL_CACHE_H_INT4> { static constexpr int NCH = 2, CPP = 2; };
-template <> struct HLoad<TL_CACHE_H_INT8> { static constexpr int NCH = 4, CPP = 4; };
-template <> struct HLoad<TL_CACHE_H_F16> { static constexpr int NCH = 8, CPP = 8; };
-template <> struct HLoad<TL_CACHE_H_F32> { static constexpr int NCH = 8, CPP = 16; };
+// chunks of 16 bytes per thread per stage for an LDS-staged h tile
+template <int MODE> struct HLoad { static constexpr int NCH = 1, CPP = 1; };
+template <> struct HLoad<TL_CACHE_H_F16> { static constexpr int NCH = 4, CPP = 8; };   // 512 threads
+template <> struct HLoad<TL_CACHE_H_F32> { static constexpr int NCH = 8, CPP = 16; };  // 256 threads
+
+// One level of a reduce-scatter over lane bit O: the lanes with that bit set
+// keep the upper half of v, the others the lower half, each adding its
+// partner's copy. LEN is the current length (compile time, so v stays in
+// registers).
+template <int LEN, int O>
+__device__ __forceinline__ void rs_level(float* v, int l) {
+  if constexpr (LEN >= 2) {
+    const bool up = (l & O) != 0;
+#pragma unroll
+    for (int e = 0; e < LEN / 2; ++e) {
+      const float keep = up ? v[e + LEN / 2] : v[e];
+      const float send = up ? v[e] : v[e + LEN / 2];
+      v[e] = keep + __shfl_xor(send, O, 64);
+    }
+  } else {
+    v[0] += __shfl_xor(v[0], O, 64);
+  }
+}
+// Sum v[0..NV) over the 32 lanes of each half-wave; lane l ends with
+// max(NV / 32, 1) values: indices (l % 32) * (NV / 32) + k (NV >= 32) or
+// (l % 32) / 2 (NV == 16, lanes l and l ^ 1 hold the same value).
+template <int NV>
+__device__ __forceinline__ void reduce_scatter32(float* v, int l) {
+  rs_level<NV, 16>(v, l);
+  rs_level<(NV >> 1), 8>(v, l);
+  rs_level<(NV >> 2), 4>(v, l);
+  rs_level<(NV >> 3), 2>(v, l);
+  rs_level<(NV >> 4), 1>(v, l);
+}
+
+// Call f(integral_constant<int, n>) for the run-time n in [0, CB].
+template <int CB, typename F>
+__device__ __forceinline__ void dispatch_nb(int n, F&& f) {
+  if constexpr (CB == 4) {
+    if (n >= 4) f(std::integral_constant<int, 4>{});
+    else if (n == 3) f(std::integral_constant<int, 3>{});
+    else if (n == 2) f(std::integral_constant<int, 2>{});
+    else if (n == 1) f(std::integral_constant<int, 1>{});
+    else f(std::integral_constant<int, 0>{});
+  } else {
+    static_assert(CB == 2, "2 or 4 position blocks per wave");
+    (void)0;
+    if (n >= 2) f(std::integral_constant<int, 2>{});
+    else if (n == 1) f(std::integral_constant<int, 1>{});
+    else f(std::integral_constant<int, 0>{});
+  }
+}
+
+// Raw codes of one lane for one stage: per 32-position block, the lane's
+// 16-byte (INT4) or 32-byte (INT8) k-run and, for INT4, the two group scales.
+template <int MODE, int CB> struct Raw { u32x4 w[CB]; };
+template <int CB> struct Raw<TL_CACHE_H_INT4, CB> {
+  u32x4 w[CB];
+  uint32_t s[CB];
+};
+template <int CB> struct Raw<TL_CACHE_H_INT8, CB> {
+  u32x4 w[CB][2];
+};
 
 template <typename T, int MODE, int DH, int EPI>
-__global__ __launch_bounds__(256, 1) void recon_kernel(KArgs a) {
+__global__ __launch_bounds__(Cfg<T>::NT, 1) void recon_kernel(KArgs a) {
   typedef Cfg<T> C;
-  constexpr int BF = C::BF, BJ = C::BJ, WF = C::WF, WJ = C::WJ, BK = C::BK;
+  constexpr int BF = C::BF, BJ = C::BJ, WF = C::WF, WJ = C::WJ, BK = C::BK, NT = C::NT;
+  constexpr int WJN = BJ / WJ;                // waves along positions
   constexpr int ES = sizeof(T);
   constexpr int ROWB = BK * ES + 16;          // padded LDS row bytes
   constexpr int RB = WF / 32, CB = WJ / 32;   // MFMA blocks per wave
   constexpr int A_CPR = BK * ES / 16;         // 16-byte chunks per W row per stage
-  constexpr int A_NCH = BF * A_CPR / 256;     // per thread
+  constexpr int A_NCH = BF * A_CPR / NT;      // per thread
+  constexpr bool B_REG = MODE == TL_CACHE_H_INT4 || MODE == TL_CACHE_H_INT8;
   constexpr int B_NCH = HLoad<MODE>::NCH;
   constexpr int B_CPP = HLoad<MODE>::CPP;     // chunks per position
-  static_assert(BJ * B_CPP == 256 * B_NCH, "h tile chunks");
-  __shared__ __attribute__((aligned(16))) char smem[2 * (BF + BJ) * ROWB];
+  static_assert(B_REG || BJ * B_CPP == NT * B_NCH, "h tile chunks");
+  static_assert(!B_REG || (std::is_same<T, half_t>::value && BK == kKBlock), "register h path");
+  constexpr int TILE_BYTES = (B_REG ? BF : BF + BJ) * ROWB;   // one LDS buffer
+  __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
 
   const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
-  const int wf = wave >> 1, wj = wave & 1;
+  const int wf = wave / WJN, wj = wave % WJN;
   const int D = a.D;
 
   int hg, ptile, r = 0, lane, Tn;
   if (EPI == EPI_ATTN) {
+    // head group fastest (consecutive workgroups land on different XCDs, each
+    // XCD keeping its head group's W rows in L2), position tile slowest so the
+    // partial last tiles of the lanes form the final dispatch round
     hg = blockIdx.x % a.n_hg;
     const int rest = blockIdx.x / a.n_hg;
-    ptile = rest % a.n_ptiles;
-    r = rest / a.n_ptiles;
+    r = rest % a.n_rows;
+    ptile = rest / a.n_rows;
     lane = a.row_lane[r];
     if (a.status[lane] == TL_LANE_ABORTED) return;
     Tn = a.row_pos[r] + 1;
@@ -116,125 +191,253 @@ __global__ __launch_bounds__(256, 1) void recon_kernel(KArgs a) {
   if (j0 >= Tn) return;
 
   // ---- W rows of this workgroup's BF features ------------------------------
+  // Thread t loads 16-byte chunk `part` of A-tile rows f = f0 + F0STEP * i
+  // (f0 = t / A_CPR). The W row of tile row f is f0 + C(i) with C(i) uniform:
+  // decode tiles interleave heads as [K_t | V_t] per head, prefill tiles keep
+  // the natural K | V order.
+  constexpr int F0STEP = NT / A_CPR;
+  static_assert(DH % F0STEP == 0, "head dim must be a multiple of the row step");
   const T* W = (const T*)a.w_qkv;
-  const T* arow[A_NCH];
-#pragma unroll
-  for (int i = 0; i < A_NCH; ++i) {
-    const int c = tid + 256 * i;
-    const int f = c / A_CPR, part = c % A_CPR;
-    int wrow;
+  const int f0 = tid / A_CPR, apart = tid % A_CPR;
+  const T* wbase = W + (size_t)f0 * D + apart * (16 / ES);
+  auto wrow_off = [&](int i) -> size_t {
+    const int fi = F0STEP * i;
+    int r0;
     if (EPI == EPI_ATTN) {
-      // head-interleaved: [K_t | V_t] per head, heads t0, t0 + 1, ...
-      const int within = f % (2 * DH);
-      const int head = hg * (BF / (2 * DH)) + f / (2 * DH);
-      wrow = D * (within < DH ? 1 : 2) + head * DH + (within % DH);
+      const int within = fi % (2 * DH);
+      const int head = hg * (BF / (2 * DH)) + fi / (2 * DH);
+      r0 = D * (within < DH ? 1 : 2) + head * DH + (within % DH);
     } else {
-      wrow = D + hg * BF + f;   // natural K | V order
+      r0 = D + hg * BF + fi;
     }
-    arow[i] = W + (size_t)wrow * D + part * (16 / ES);
-  }
-  // ---- h entries of this workgroup's BJ positions ----------------------------
+    return (size_t)r0 * D;
+  };
+
   const CacheView& cv = a.cache;
-  int bpos[B_NCH], bpart[B_NCH];
-  bool bok[B_NCH];
-#pragma unroll
-  for (int i = 0; i < B_NCH; ++i) {
-    const int c = tid + 256 * i;
-    bpos[i] = c / B_CPP;
-    bpart[i] = c % B_CPP;
-    bok[i] = j0 + bpos[i] < Tn;
-  }
-  half_t s8[B_NCH];   // INT8: per-position scale, fixed over the k loop
-  if (MODE == TL_CACHE_H_INT8) {
-#pragma unroll
-    for (int i = 0; i < B_NCH; ++i)
-      s8[i] = bok[i] ? h_from_bits(*cv.int8_scale(a.layer, lane, j0 + bpos[i])) : (half_t)0.f;
-  }
+  constexpr int HRB = block_row_bytes(MODE);
+  const char* hbase = cv.code_row(a.layer, lane, 0, 0);
+  const size_t kb_stride = (size_t)cv.max_seq * HRB;
+  const int nst = D / BK;
 
-  u32x4 ra[A_NCH], rb[B_NCH];
-  uint16_t rs[B_NCH];
-  auto load_stage = [&](int st) {
-    const int k0 = st * BK;
-#pragma unroll
-    for (int i = 0; i < A_NCH; ++i) ra[i] = *(const u32x4*)(arow[i] + k0);
-    const int kb = k0 / kKBlock;
-#pragma unroll
-    for (int i = 0; i < B_NCH; ++i) {
-      if (bok[i]) {
-        const char* p = cv.code_row(a.layer, lane, kb, j0 + bpos[i]) + bpart[i] * 16;
-        rb[i] = *(const u32x4*)p;
-        if (MODE == TL_CACHE_H_INT4) rs[i] = cv.int4_scale(a.layer, lane, kb, j0 + bpos[i])[bpart[i]];
-      } else {
-        rb[i] = u32x4{0u, 0u, 0u, 0u};
-        rs[i] = 0;
-      }
-    }
-  };
-  auto store_stage = [&](int buf) {
-    char* As = smem + buf * (BF + BJ) * ROWB;
-    char* Bs = As + BF * ROWB;
-#pragma unroll
-    for (int i = 0; i < A_NCH; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4*)(As + (c / A_CPR) * ROWB + (c % A_CPR) * 16) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_NCH; ++i) {
-      char* dst = Bs + bpos[i] * ROWB;
-      if (MODE == TL_CACHE_H_INT4) {
-        const half_t s = h_from_bits(rs[i]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          *(half8*)(dst + bpart[i] * 64 + w * 16) = int4_dequant8(rb[i][w], s);
-      } else if (MODE == TL_CACHE_H_INT8) {
-#pragma unroll
-        for (int w = 0; w < 4; w += 2) {
-          const half4 lo = int8_dequant4(rb[i][w], s8[i]);
-          const half4 hi = int8_dequant4(rb[i][w + 1], s8[i]);
-          half8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          *(half8*)(dst + bpart[i] * 32 + w * 8) = v;
-        }
-      } else {
-        *(u32x4*)(dst + bpart[i] * 16) = rb[i];
-      }
-    }
-  };
+  // 32-position blocks of this wave that hold positions < T; the others are all
+  // zero, so their MFMAs are skipped (whole waves past T also skip the
+  // epilogue) while the wave keeps loading, storing and synchronising
+  const int ncb = min(max((Tn - (j0 + wj * WJ) + 31) / 32, 0), CB);
+  const bool wave_live = ncb > 0;
 
+  typedef typename Mma<T>::frag Frag;
   float16v acc[RB][CB];
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] = float16v{};
 
-  // waves whose positions all lie past T have an all-zero tile and skip the epilogue
-  const bool wave_live = j0 + wj * WJ < Tn;
-  const int nst = D / BK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) load_stage(st + 1);
-    {
-      const char* As = smem + (st & 1) * (BF + BJ) * ROWB;
-      const char* Bs = As + BF * ROWB;
-      const int koff = 8 * (l >> 5) * ES;
-#pragma unroll 1
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        typename Mma<T>::frag fa[RB], fb[CB];
+  u32x4 ra[A_NCH];
+  auto load_w = [&](int st) {
+    const T* wk = wbase + st * BK;
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
-          fa[i] = *(const typename Mma<T>::frag*)(As + (wf * WF + i * 32 + (l & 31)) * ROWB + kk * 16 * ES + koff);
+    for (int i = 0; i < A_NCH; ++i) ra[i] = *(const u32x4*)(wk + wrow_off(i));
+  };
+  auto store_w = [&](int buf) {
+    char* As = smem + buf * TILE_BYTES;
 #pragma unroll
-        for (int j = 0; j < CB; ++j)
-          fb[j] = *(const typename Mma<T>::frag*)(Bs + (wj * WJ + j * 32 + (l & 31)) * ROWB + kk * 16 * ES + koff);
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-          for (int j = 0; j < CB; ++j) acc[i][j] = Mma<T>::mma(fa[i], fb[j], acc[i][j]);
-      }
+    for (int i = 0; i < A_NCH; ++i) {
+      const int c = tid + NT * i;
+      *(u32x4*)(As + (c / A_CPR) * ROWB + (c % A_CPR) * 16) = ra[i];
     }
-    if (st + 1 < nst) store_stage((st + 1) & 1);
+  };
+  const int koff = 8 * (l >> 5) * ES;
+  auto read_a = [&](int buf, int kk, Frag (&fa)[RB]) {
+    const char* As = smem + buf * TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      fa[i] = *(const Frag*)(As + (wf * WF + i * 32 + (l & 31)) * ROWB + kk * 16 * ES + koff);
+  };
+
+  if constexpr (B_REG) {
+    // ---- h operand straight from the cache into registers -----------------
+    // lane l serves positions p_j = j0 + wj*WJ + 32 j + l % 32 and, within each
+    // 64-element block, the k-run of half-wave hb = l / 32
+    const int hb = l >> 5;
+    uint32_t roff[CB], soff[CB];
+    uint32_t vmask = 0;   // positions < T
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int p = j0 + wj * WJ + j * 32 + (l & 31);
+      if (p < Tn) vmask |= 1u << j;
+      const int pc = min(p, Tn - 1);   // past T: read position T-1, zero its scale
+      roff[j] = (uint32_t)pc * HRB + hb * (HRB / 2);
+      soff[j] = (uint32_t)pc;
+    }
+    const uint16_t* s4base = MODE == TL_CACHE_H_INT4 ? cv.int4_scale(a.layer, lane, 0, 0) : nullptr;
+    half_t s8[CB];
+    if constexpr (MODE == TL_CACHE_H_INT8) {
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        s8[j] = ((vmask >> j) & 1) ? h_from_bits(*cv.int8_scale(a.layer, lane, soff[j])) : (half_t)0.f;
+    }
+    typedef Raw<MODE, CB> R;
+    auto load_raw = [&](int st, R& raw) {
+      const char* hk = hbase + (size_t)st * kb_stride;
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        if constexpr (MODE == TL_CACHE_H_INT4) {
+          raw.w[j] = *(const u32x4*)(hk + roff[j]);
+          const uint32_t sv = *(const uint32_t*)(s4base + ((size_t)st * cv.max_seq + soff[j]) * 2);
+          raw.s[j] = ((vmask >> j) & 1) ? sv : 0u;
+        } else {
+          raw.w[j][0] = *(const u32x4*)(hk + roff[j]);
+          raw.w[j][1] = *(const u32x4*)(hk + roff[j] + 16);
+        }
+      }
+    };
+    // MFMA operand of block j, k-step kk: 8 fp16 = fp16(q * s)
+    auto b_frag = [&](const R& raw, int j, int kk) -> half8 {
+      if constexpr (MODE == TL_CACHE_H_INT4) {
+        const uint32_t sv = raw.s[j];
+        const half_t sc = h_from_bits((uint16_t)(kk < 2 ? (sv & 0xFFFFu) : (sv >> 16)));
+        return int4_dequant8(raw.w[j][kk], sc);
+      } else {
+        const u32x4& w = raw.w[j][kk >> 1];
+        const half4 lo = int8_dequant4(w[(kk & 1) * 2], s8[j]);
+        const half4 hi = int8_dequant4(w[(kk & 1) * 2 + 1], s8[j]);
+        return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    };
+
+    // one stage on LDS buffer BUF with the lane's codes in `cur`; stage st+1's
+    // W rows go to the other buffer, stage st+2's codes refill `cur`
+    auto stage = [&](auto buf_c, auto nb_c, int st, Frag (&f0a)[RB], R& cur) {
+      constexpr int BUF = decltype(buf_c)::value;
+      constexpr int NB = decltype(nb_c)::value;
+      Frag f1a[RB];
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        Frag (&ca)[RB] = (kk & 1) ? f1a : f0a;
+        Frag (&na)[RB] = (kk & 1) ? f0a : f1a;
+        if (kk + 1 < BK / 16 && NB > 0) read_a(BUF, kk + 1, na);
+        half8 fb[CB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fb[j] = b_frag(cur, j, kk);
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = Mma<T>::mma(ca[i], fb[j], acc[i][j]);
+        if (kk == BK / 16 - 1) {
+          store_w(BUF ^ 1);
+          load_w(min(st + 2, nst - 1));
+        }
+      }
+      load_raw(min(st + 2, nst - 1), cur);
+      __syncthreads();
+      if (NB > 0) read_a(BUF ^ 1, 0, f0a);
+    };
+
+    R raw0, raw1;
+    load_w(0);
+    load_raw(0, raw0);
+    load_raw(min(1, nst - 1), raw1);
+    store_w(0);
+    load_w(min(1, nst - 1));
     __syncthreads();
+    Frag fa[RB];
+    auto loop = [&](auto nb_c) {
+      if (decltype(nb_c)::value > 0) read_a(0, 0, fa);
+      for (int st = 0; st < nst; st += 2) {
+        stage(std::integral_constant<int, 0>{}, nb_c, st, fa, raw0);
+        stage(std::integral_constant<int, 1>{}, nb_c, st + 1, fa, raw1);
+      }
+    };
+    dispatch_nb<CB>(ncb, loop);
+  } else {
+    // ---- fp16 / fp32 h staged through LDS ----------------------------------
+    // positions past T read the entry of position T-1 (always in bounds) and are
+    // zeroed by a select when stored, so the loop has no data-dependent branches
+    int bpos[B_NCH];
+    uint32_t hoff[B_NCH];
+    uint32_t bokmask = 0;
+#pragma unroll
+    for (int i = 0; i < B_NCH; ++i) {
+      const int c = tid + NT * i;
+      bpos[i] = c / B_CPP;
+      if (j0 + bpos[i] < Tn) bokmask |= 1u << i;
+      const int pos = min(j0 + bpos[i], Tn - 1);
+      hoff[i] = (uint32_t)pos * HRB + (c % B_CPP) * 16;
+    }
+    u32x4 rh[B_NCH];
+    auto load_h = [&](int st) {
+      const char* hk = hbase + (size_t)st * kb_stride;
+#pragma unroll
+      for (int i = 0; i < B_NCH; ++i) rh[i] = *(const u32x4*)(hk + hoff[i]);
+    };
+    auto store_h = [&](int buf) {
+      char* Bs = smem + buf * TILE_BYTES + BF * ROWB;
+#pragma unroll
+      for (int i = 0; i < B_NCH; ++i) {
+        const int c = tid + NT * i;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        *(u32x4*)(Bs + bpos[i] * ROWB + (c % B_CPP) * 16) = ((bokmask >> i) & 1) ? rh[i] : zero;
+      }
+    };
+    auto read_b = [&](auto nb_c, int buf, int kk, Frag (&fb)[CB]) {
+      constexpr int NB = decltype(nb_c)::value;
+      const char* Bs = smem + buf * TILE_BYTES + BF * ROWB;
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        fb[j] = *(const Frag*)(Bs + (wj * WJ + j * 32 + (l & 31)) * ROWB + kk * 16 * ES + koff);
+    };
+    auto stage = [&](auto buf_c, auto nb_c, int st, Frag (&f0a)[RB], Frag (&f0b)[CB]) {
+      constexpr int BUF = decltype(buf_c)::value;
+      constexpr int NB = decltype(nb_c)::value;
+      Frag f1a[RB], f1b[CB];
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        Frag (&ca)[RB] = (kk & 1) ? f1a : f0a;
+        Frag (&cb)[CB] = (kk & 1) ? f1b : f0b;
+        Frag (&na)[RB] = (kk & 1) ? f0a : f1a;
+        Frag (&nb)[CB] = (kk & 1) ? f0b : f1b;
+        if (kk + 1 < BK / 16 && NB > 0) {
+          read_a(BUF, kk + 1, na);
+          read_b(nb_c, BUF, kk + 1, nb);
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = Mma<T>::mma(ca[i], cb[j], acc[i][j]);
+        if (kk == BK / 16 - 2) {
+          store_h(BUF ^ 1);
+          load_h(min(st + 2, nst - 1));
+        }
+        if (kk == BK / 16 - 1) {
+          store_w(BUF ^ 1);
+          load_w(min(st + 2, nst - 1));
+        }
+      }
+      __syncthreads();
+      if (NB > 0) {
+        read_a(BUF ^ 1, 0, f0a);
+        read_b(nb_c, BUF ^ 1, 0, f0b);
+      }
+    };
+    load_w(0);
+    load_h(0);
+    store_w(0);
+    store_h(0);
+    load_w(min(1, nst - 1));
+    load_h(min(1, nst - 1));
+    __syncthreads();
+    Frag fa[RB], fb[CB];
+    auto loop = [&](auto nb_c) {
+      if (decltype(nb_c)::value > 0) {
+        read_a(0, 0, fa);
+        read_b(nb_c, 0, 0, fb);
+      }
+      for (int st = 0; st < nst; st += 2) {
+        stage(std::integral_constant<int, 0>{}, nb_c, st, fa, fb);
+        stage(std::integral_constant<int, 1>{}, nb_c, st + 1, fa, fb);
+      }
+    };
+    dispatch_nb<CB>(ncb, loop);
   }
 
   // ---- epilogues -------------------------------------------------------------
@@ -315,26 +518,7 @@ __global__ __launch_bounds__(256, 1) void recon_kernel(KArgs a) {
         for (int j = 0; j < CB; ++j) t = fmaf(p[j], acc[rb0 + kb][j][i], t);
         v[kb * 16 + i] = t;
       }
-    // reduce-scatter across lane bits 4..0
-    int len = NV;
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) {
-      if (len >= 2) {
-        const int hl = len >> 1;
-        const bool up = (l & o) != 0;
-#pragma unroll
-        for (int e = 0; e < NV / 2; ++e) {
-          if (e < hl) {
-            const float keep = up ? v[e + hl] : v[e];
-            const float send = up ? v[e] : v[e + hl];
-            v[e] = keep + __shfl_xor(send, o, 64);
-          }
-        }
-        len = hl;
-      } else {
-        v[0] += __shfl_xor(v[0], o, 64);
-      }
-    }
+    reduce_scatter32<NV>(v, l);
     float* dst = a.part + (((size_t)r * a.H + head) * a.S + split) * (DH + 2);
     if (l == 0) { dst[0] = m; dst[1] = lsum; }
     constexpr int FL = NV >= 32 ? NV / 32 : 1;
@@ -361,7 +545,7 @@ __global__ __launch_bounds__(256, 1) void recon_kernel(KArgs a) {
   } else {
     // K rows live in wave wf = 0, V rows in wf = 1 (same positions): pass the
     // weights p through LDS.
-    float* ex = (float*)smem;               // [2][WJ] p, then [2][2] (m, l)
+    float* ex = (float*)smem;               // [WJN][WJ] p, then [WJN][2] (m, l)
     const int head = hg;
     __syncthreads();
     if (wf == 0 && wave_live) {
@@ -371,22 +555,22 @@ __global__ __launch_bounds__(256, 1) void recon_kernel(KArgs a) {
       if (l < 32)
 #pragma unroll
         for (int j = 0; j < CB; ++j) ex[wj * WJ + j * 32 + l] = s[j];
-      if (l == 0) { ex[2 * WJ + 2 * wj] = m; ex[2 * WJ + 2 * wj + 1] = lsum; }
+      if (l == 0) { ex[WJN * WJ + 2 * wj] = m; ex[WJN * WJ + 2 * wj + 1] = lsum; }
     }
     __syncthreads();
     if (wf == 1 && wave_live) {
       float p[CB];
 #pragma unroll
       for (int j = 0; j < CB; ++j) p[j] = ex[wj * WJ + j * 32 + (l & 31)];
-      values(0, head, p, ex[2 * WJ + 2 * wj], ex[2 * WJ + 2 * wj + 1]);
+      values(0, head, p, ex[WJN * WJ + 2 * wj], ex[WJN * WJ + 2 * wj + 1]);
     }
   }
 }
 
 template <typename T, int MODE, int DH>
 hipError_t launch_mode(const KArgs& k, int grid, hipStream_t s, int epi) {
-  if (epi == EPI_ATTN) recon_kernel<T, MODE, DH, EPI_ATTN><<<grid, 256, 0, s>>>(k);
-  else recon_kernel<T, MODE, DH, EPI_KVSTORE><<<grid, 256, 0, s>>>(k);
+  if (epi == EPI_ATTN) recon_kernel<T, MODE, DH, EPI_ATTN><<<grid, Cfg<T>::NT, 0, s>>>(k);
+  else recon_kernel<T, MODE, DH, EPI_KVSTORE><<<grid, Cfg<T>::NT, 0, s>>>(k);
   return hipGetLastError();
 }
 
@@ -426,6 +610,7 @@ hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t
   k.H = m.H;
   k.n_hg = 2 * m.D / BF;
   k.n_ptiles = (r.t_ub + BJ - 1) / BJ;
+  k.n_rows = r.n_rows;
   k.row_lane = r.row_lane;
   k.row_pos = r.row_pos;
   k.status = r.status;
@@ -450,6 +635,7 @@ hipError_t launch_recon_store(const ModelView& m, const CacheView& c, int layer,
   k.H = m.H;
   k.n_hg = 2 * m.D / BF;
   k.n_ptiles = (T + BJ - 1) / BJ;
+  k.n_rows = 1;
   k.lane = lane;
   k.T = T;
   k.status = status;

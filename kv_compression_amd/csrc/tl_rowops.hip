@@ -106,7 +106,8 @@ __global__ __launch_bounds__(kRowThreads) void norm_append_kernel(ModelView m, C
     const half_t s = codec_scale(am, 127.f);
     const float sf = (float)s;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) ((int8_t*)row)[w + i] = (int8_t)codec_code(h[i], sf, -127.f, 127.f);
+    for (int i = 0; i < EPT; ++i)
+      ((int8_t*)row)[code_group(w + i) * 8 + ((w + i) & 7)] = (int8_t)codec_code(h[i], sf, -127.f, 127.f);
     if (threadIdx.x == 0) *c.int8_scale(a.layer, lane, pos) = h_bits(s);
     return;
   }
@@ -130,9 +131,9 @@ __global__ __launch_bounds__(kRowThreads) void norm_append_kernel(ModelView m, C
     constexpr int TPW = 8 / EPT;   // threads sharing one word
 #pragma unroll
     for (int o = 1; o < TPW; o <<= 1) word |= __shfl_xor(word, o, 64);
-    if ((threadIdx.x % TPW) == 0) ((uint32_t*)row)[w / 8] = word;
+    if ((threadIdx.x % TPW) == 0) ((uint32_t*)row)[code_group(w)] = word;
   } else {
-    ((uint32_t*)row)[w / 8] = word;
+    ((uint32_t*)row)[code_group(w)] = word;
   }
   if ((e0 % kInt4Group) == 0) {
     const int g = e0 / kInt4Group;
@@ -289,11 +290,11 @@ __global__ void cache_read_kernel(ModelView m, CacheView c, int lane, int layer,
     int q;
     half_t s;
     if (c.mode == TL_CACHE_H_INT8) {
-      q = ((const int8_t*)row)[w];
+      q = ((const int8_t*)row)[code_group(w) * 8 + (w & 7)];
       s = h_from_bits(*c.int8_scale(layer, lane, pos));
       if (scales && e == 0) scales[r] = h_bits(s);
     } else {
-      const uint32_t word = ((const uint32_t*)row)[w / 8];
+      const uint32_t word = ((const uint32_t*)row)[code_group(w)];
       q = (int)((word >> int4_shift(w & 7)) & 0xF) - 8;
       const int g = e / kInt4Group;
       s = h_from_bits(c.int4_scale(layer, lane, kb, pos)[g & 1]);
