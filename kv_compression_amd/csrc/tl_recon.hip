@@ -32,17 +32,31 @@ namespace tl {
 
 namespace {
 
-// Tile shapes. fp16: 8 waves (2 per SIMD, 128 accumulators each) so that one
-// wave's waits are covered by the other wave's MFMAs; fp32: 4 waves.
-template <typename T> struct Cfg;
-template <> struct Cfg<half_t> {
+// Tile shapes (BF features x BJ positions per workgroup, WF x WJ per wave).
+//   INT4 / INT8 h (operands copied to LDS, h dequantised in registers): 4
+//   waves, one per SIMD, each owning all 256 features of the tile for 64
+//   positions (256 accumulators, held in AGPRs). Every dequantised h operand
+//   feeds 8 MFMAs, and the MFMAs of one k-step cover the dequantisation and
+//   LDS reads of the next.
+//   fp16 h (staged through LDS from registers): 8 waves, 2 per SIMD, 128 x 64.
+//   fp32: 4 waves of 64 x 64.
+template <typename T, int MODE> struct Cfg {
   static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 64, BK = 64;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
-template <> struct Cfg<float> {
+template <> struct Cfg<half_t, TL_CACHE_H_INT4> {
+  static constexpr int BF = 256, BJ = 256, WF = 256, WJ = 64, BK = 64;
+  static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+};
+template <> struct Cfg<half_t, TL_CACHE_H_INT8> : Cfg<half_t, TL_CACHE_H_INT4> {};
+template <int MODE> struct Cfg<float, MODE> {
   static constexpr int BF = 128, BJ = 128, WF = 64, WJ = 64, BK = 64;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
+// every fp16 configuration shares BF, BJ and WJ (grid shape and split length)
+static_assert(Cfg<half_t, TL_CACHE_H_INT4>::BF == Cfg<half_t, TL_CACHE_H_F16>::BF &&
+              Cfg<half_t, TL_CACHE_H_INT4>::BJ == Cfg<half_t, TL_CACHE_H_F16>::BJ &&
+              Cfg<half_t, TL_CACHE_H_INT4>::WJ == Cfg<half_t, TL_CACHE_H_F16>::WJ, "fp16 tiles");
 
 enum { EPI_ATTN = 0, EPI_KVSTORE = 1 };
 
@@ -69,7 +83,7 @@ struct KArgs {
   int layer;
   const void* w_qkv;
   int D, H;
-  int n_hg, n_ptiles, n_rows;
+  int n_hg, n_ptiles, n_rows, hpx;
   // decode
   const int32_t* row_lane;
   const int32_t* row_pos;
@@ -146,9 +160,42 @@ template <int CB> struct Raw<TL_CACHE_H_INT8, CB> {
   u32x4 w[CB][2];
 };
 
+#define TL_LDS __attribute__((address_space(3)))
+
+// Word 3 of a raw buffer resource on this architecture: 32-bit data format,
+// no swizzling, offsets checked against the byte extent.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// One buffer of the LDS ring: a separate LDS array per index, so the compiler
+// can tell that reads of one buffer do not depend on copies into another.
+template <int B, int BYTES> struct Ring {
+  static __device__ __forceinline__ char* p() {
+    __shared__ __attribute__((aligned(16))) char buf[BYTES];
+    return buf;
+  }
+};
+
+// Wait until at most N of this wave's memory loads (LDS copies included) are
+// outstanding and its LDS reads are done, then synchronise the workgroup. The
+// empty asm statements keep the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void dma_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4] (7: no wait), lgkmcnt [11:8]
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Slot swizzle of the 128-byte W rows in the LDS ring: rows R..R+15 (R a
+// multiple of 16) reading the same chunk land on 16 distinct 16-byte slots of
+// a 256-byte bank window, and any 8 consecutive rows on 8 distinct slots.
+__device__ __forceinline__ int w_swz(int R) { return ((R >> 1) ^ (R << 2)) & 7; }
+
 template <typename T, int MODE, int DH, int EPI>
-__global__ __launch_bounds__(Cfg<T>::NT, 1) void recon_kernel(KArgs a) {
-  typedef Cfg<T> C;
+__global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
+  typedef Cfg<T, MODE> C;
   constexpr int BF = C::BF, BJ = C::BJ, WF = C::WF, WJ = C::WJ, BK = C::BK, NT = C::NT;
   constexpr int WJN = BJ / WJ;                // waves along positions
   constexpr int ES = sizeof(T);
@@ -161,8 +208,11 @@ __global__ __launch_bounds__(Cfg<T>::NT, 1) void recon_kernel(KArgs a) {
   constexpr int B_CPP = HLoad<MODE>::CPP;     // chunks per position
   static_assert(B_REG || BJ * B_CPP == NT * B_NCH, "h tile chunks");
   static_assert(!B_REG || (std::is_same<T, half_t>::value && BK == kKBlock), "register h path");
-  constexpr int TILE_BYTES = (B_REG ? BF : BF + BJ) * ROWB;   // one LDS buffer
-  __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
+  constexpr int TILE_BYTES = (B_REG ? BF : BF + BJ) * ROWB;   // one LDS buffer (LDS-staged h)
+  __shared__ __attribute__((aligned(16))) char smem[B_REG ? 16 : 2 * TILE_BYTES];
+  constexpr int HRB = block_row_bytes(MODE);
+  // one LDS ring buffer of the copied path: W tile, h codes, INT4 scales
+  constexpr int RING = B_REG ? BF * BK * ES + BJ * HRB + (MODE == TL_CACHE_H_INT4 ? BJ * 4 : 0) : 16;
 
   const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
   const int wf = wave / WJN, wj = wave % WJN;
@@ -173,10 +223,18 @@ __global__ __launch_bounds__(Cfg<T>::NT, 1) void recon_kernel(KArgs a) {
     // head group fastest (consecutive workgroups land on different XCDs, each
     // XCD keeping its head group's W rows in L2), position tile slowest so the
     // partial last tiles of the lanes form the final dispatch round
-    hg = blockIdx.x % a.n_hg;
-    const int rest = blockIdx.x / a.n_hg;
-    r = rest % a.n_rows;
-    ptile = rest / a.n_rows;
+    // Workgroup b runs on XCD b % 8. Each XCD takes a set of a.hpx head groups
+    // (their W rows stay in its L2) and every (8 / sets)-th tile, and runs the
+    // head groups of one tile back to back, so a tile's h codes are fetched
+    // into that XCD's L2 once and reused by the set. Tiles are numbered
+    // position-tile-major so the partial last tiles dispatch last.
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int sets = a.n_hg / a.hpx, parts = 8 / sets;
+    hg = (xcd % sets) * a.hpx + idx % a.hpx;
+    const int tile = (idx / a.hpx) * parts + xcd / sets;
+    r = tile % a.n_rows;
+    ptile = tile / a.n_rows;
+    if (ptile >= a.n_ptiles) return;
     lane = a.row_lane[r];
     if (a.status[lane] == TL_LANE_ABORTED) return;
     Tn = a.row_pos[r] + 1;
@@ -213,8 +271,17 @@ __global__ __launch_bounds__(Cfg<T>::NT, 1) void recon_kernel(KArgs a) {
     return (size_t)r0 * D;
   };
 
+  // W row of tile row f
+  auto wrow = [&](int f) -> int {
+    if (EPI == EPI_ATTN) {
+      const int within = f % (2 * DH);
+      const int head = hg * (BF / (2 * DH)) + f / (2 * DH);
+      return D * (within < DH ? 1 : 2) + head * DH + (within % DH);
+    }
+    return D + hg * BF + f;
+  };
+
   const CacheView& cv = a.cache;
-  constexpr int HRB = block_row_bytes(MODE);
   const char* hbase = cv.code_row(a.layer, lane, 0, 0);
   const size_t kb_stride = (size_t)cv.max_seq * HRB;
   const int nst = D / BK;
@@ -255,46 +322,146 @@ __global__ __launch_bounds__(Cfg<T>::NT, 1) void recon_kernel(KArgs a) {
   };
 
   if constexpr (B_REG) {
-    // ---- h operand straight from the cache into registers -----------------
+    // ---- W rows and h codes copied by the memory unit straight into LDS -----
+    // A ring of three stage buffers, each one separate LDS array: stage st
+    // reads buffer st % 3 while the copies of stages st+1 and st+2 are in
+    // flight, so every load has two stages of MFMA work to land. Each wave
+    // issues exactly DMA_PER_STAGE copies per stage; waiting until only the
+    // newest stage's copies are outstanding (the counter drains in issue order)
+    // and then synchronising the workgroup publishes the next stage's buffer.
+    //   W tile: BF rows x 128 bytes, 16-byte chunk c of row R at slot
+    //     c ^ swz(R), so the fragment reads of 16 consecutive rows are spread
+    //     over all banks without padding. One copy instruction fills 1 KB
+    //     (64 lanes x 16 B in lane order); lane l of a wave's copy fetches
+    //     whichever chunk belongs at its slot.
+    //   h codes: per 16 positions, the 16-byte runs of run index hq (half hb,
+    //     part q of that half's k-run) sit side by side, so lanes 0..15 of a
+    //     fragment read touch 16 consecutive slots.
+    //   INT4 scales: one 32-bit word (two fp16 group scales) per position.
+    // Positions past T copy the entry of position T-1 (always in bounds) and
+    // are zeroed through their scale when the operand is built.
+    constexpr int NW = NT / 64;
+    constexpr int NQ = HRB / 32;                         // 16-byte runs per half row
+    constexpr int W_BYTES = BF * BK * ES;
+    constexpr int H_BYTES = BJ * HRB;
+    constexpr int S_BYTES = MODE == TL_CACHE_H_INT4 ? BJ * 4 : 0;
+    constexpr int W_IPW = W_BYTES / 1024 / NW, H_IPW = H_BYTES / 1024 / NW;
+    constexpr int DMA_PER_STAGE = W_IPW + H_IPW + (S_BYTES ? 1 : 0);
+    static_assert(W_IPW * NW * 1024 == W_BYTES && H_IPW * NW * 1024 == H_BYTES, "copy split");
+    static_assert(S_BYTES == 0 || S_BYTES == NW * 256, "one 4-byte copy per lane and wave for the scales");
+    static_assert(3 * (W_BYTES + H_BYTES + S_BYTES) <= 160 * 1024, "LDS ring");
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+    uint32_t woff[W_IPW];     // byte offset of the lane's W chunk (stage 0)
+#pragma unroll
+    for (int i = 0; i < W_IPW; ++i) {
+      const int u = (wave_u * W_IPW + i) * 64 + l;
+      const int R = u >> 3;
+      const int c = (u & 7) ^ w_swz(R);
+      woff[i] = (uint32_t)(wrow(R) * (size_t)D * ES) + c * 16;
+    }
+    uint32_t hoff[H_IPW];     // byte offset of the lane's h run (stage 0)
+#pragma unroll
+    for (int i = 0; i < H_IPW; ++i) {
+      const int S = (wave_u * H_IPW + i) * 64 + l;
+      const int pos = (S / (32 * NQ)) * 16 + S % 16;
+      const int hq = (S / 16) % (2 * NQ);
+      hoff[i] = (uint32_t)min(j0 + pos, Tn - 1) * HRB + hq * 16;
+    }
+    const uint16_t* s4base = MODE == TL_CACHE_H_INT4 ? cv.int4_scale(a.layer, lane, 0, 0) : nullptr;
+    // scale copy (LDS copies write one dword per lane): lane l of wave w
+    // fetches the word of position 64 w + l
+    const uint32_t soff = (uint32_t)min(j0 + wave_u * 64 + l, Tn - 1) * 2;
+
+    // Copies go through buffer resources: the lane's offset stays in one VGPR,
+    // the stage offset is a scalar, and the hardware drops any access past the
+    // resource's extent instead of faulting.
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.w_qkv, 0, 3 * D * D * ES, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t h_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)hbase, 0, (int)(nst * kb_stride), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)s4base, 0, S_BYTES ? nst * cv.max_seq * 4 : 0, kRsrcWord3);
+    // The wave's copies of one stage, numbered 0 .. DMA_PER_STAGE-1 (W chunks,
+    // then h runs, then the scale words); issue_ops<LO, HI> issues ops LO..HI-1.
+    auto issue_ops = [&](auto buf_c, auto lo_c, auto hi_c, int st) {
+      constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+      char* rb = Ring<decltype(buf_c)::value, RING>::p();
+#pragma unroll
+      for (int i = 0; i < W_IPW; ++i)
+        if (i >= LO && i < HI)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (TL_LDS void*)(rb + (wave_u * W_IPW + i) * 1024), 16,
+                                                   (int)woff[i], st * BK * ES, 0, 0);
+#pragma unroll
+      for (int i = 0; i < H_IPW; ++i)
+        if (W_IPW + i >= LO && W_IPW + i < HI)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(h_rsrc,
+                                                   (TL_LDS void*)(rb + W_BYTES + (wave_u * H_IPW + i) * 1024), 16,
+                                                   (int)hoff[i], (int)(st * kb_stride), 0, 0);
+      if constexpr (S_BYTES > 0) {
+        if (W_IPW + H_IPW >= LO && W_IPW + H_IPW < HI)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (TL_LDS void*)(rb + W_BYTES + H_BYTES + wave_u * 256), 4,
+                                                   (int)(soff * 2), st * cv.max_seq * 4, 0, 0);
+      }
+    };
+    // The copies of a stage go out in three parts, so that the four waves'
+    // requests never queue up behind each other in the memory pipeline (a
+    // wave stalls at issue while its request waits, MFMAs included): part A
+    // right after the barrier that frees the buffer, parts B and C during the
+    // first two k-steps of the following stage.
+    constexpr int PA = (DMA_PER_STAGE + 2) / 3, PB = (DMA_PER_STAGE + 1) / 3;
+    using IA0 = std::integral_constant<int, 0>;
+    using IA1 = std::integral_constant<int, PA>;
+    using IB1 = std::integral_constant<int, PA + PB>;
+    using IC1 = std::integral_constant<int, DMA_PER_STAGE>;
+    auto issue = [&](auto buf_c, int st) {
+      issue_ops(buf_c, IA0{}, IC1{}, st);
+    };
+
     // lane l serves positions p_j = j0 + wj*WJ + 32 j + l % 32 and, within each
     // 64-element block, the k-run of half-wave hb = l / 32
     const int hb = l >> 5;
-    uint32_t roff[CB], soff[CB];
     uint32_t vmask = 0;   // positions < T
 #pragma unroll
-    for (int j = 0; j < CB; ++j) {
-      const int p = j0 + wj * WJ + j * 32 + (l & 31);
-      if (p < Tn) vmask |= 1u << j;
-      const int pc = min(p, Tn - 1);   // past T: read position T-1, zero its scale
-      roff[j] = (uint32_t)pc * HRB + hb * (HRB / 2);
-      soff[j] = (uint32_t)pc;
-    }
-    const uint16_t* s4base = MODE == TL_CACHE_H_INT4 ? cv.int4_scale(a.layer, lane, 0, 0) : nullptr;
+    for (int j = 0; j < CB; ++j)
+      if (j0 + wj * WJ + j * 32 + (l & 31) < Tn) vmask |= 1u << j;
     half_t s8[CB];
     if constexpr (MODE == TL_CACHE_H_INT8) {
 #pragma unroll
-      for (int j = 0; j < CB; ++j)
-        s8[j] = ((vmask >> j) & 1) ? h_from_bits(*cv.int8_scale(a.layer, lane, soff[j])) : (half_t)0.f;
-    }
-    typedef Raw<MODE, CB> R;
-    auto load_raw = [&](int st, R& raw) {
-      const char* hk = hbase + (size_t)st * kb_stride;
-#pragma unroll
       for (int j = 0; j < CB; ++j) {
+        const int pc = min(j0 + wj * WJ + j * 32 + (l & 31), Tn - 1);
+        s8[j] = ((vmask >> j) & 1) ? h_from_bits(*cv.int8_scale(a.layer, lane, pc)) : (half_t)0.f;
+      }
+    }
+    // fragment reads: W chunk kk*2 + hb of row wf*WF + i*32 + l%32 (the
+    // swizzle depends on l % 32 only), and the lane's h runs
+    const int arow = wf * WF + (l & 31);
+    const int aswz = w_swz(arow);
+    typedef Raw<MODE, CB> R;
+    auto read_a3 = [&](const char* rb, int kk, Frag (&fa)[RB]) {
+      const char* base = rb + arow * (BK * ES) + (((kk * 2 + hb) ^ aswz) * 16);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) fa[i] = *(const Frag*)(base + i * 32 * (BK * ES));
+    };
+    auto read_raw = [&](auto nb_c, const char* rb, R& raw) {
+      constexpr int NB = decltype(nb_c)::value;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int pos = wj * WJ + j * 32 + (l & 31);
+        const char* hs = rb + W_BYTES + ((pos >> 4) * (32 * NQ) + hb * NQ * 16 + (pos & 15)) * 16;
         if constexpr (MODE == TL_CACHE_H_INT4) {
-          raw.w[j] = *(const u32x4*)(hk + roff[j]);
-          const uint32_t sv = *(const uint32_t*)(s4base + ((size_t)st * cv.max_seq + soff[j]) * 2);
-          raw.s[j] = ((vmask >> j) & 1) ? sv : 0u;
+          raw.w[j] = *(const u32x4*)hs;
+          raw.s[j] = *(const uint32_t*)(rb + W_BYTES + H_BYTES + pos * 4);
         } else {
-          raw.w[j][0] = *(const u32x4*)(hk + roff[j]);
-          raw.w[j][1] = *(const u32x4*)(hk + roff[j] + 16);
+          raw.w[j][0] = *(const u32x4*)hs;
+          raw.w[j][1] = *(const u32x4*)(hs + 16 * 16);
         }
       }
     };
     // MFMA operand of block j, k-step kk: 8 fp16 = fp16(q * s)
     auto b_frag = [&](const R& raw, int j, int kk) -> half8 {
       if constexpr (MODE == TL_CACHE_H_INT4) {
-        const uint32_t sv = raw.s[j];
+        const uint32_t sv = ((vmask >> j) & 1) ? raw.s[j] : 0u;   // positions past T: scale 0
         const half_t sc = h_from_bits((uint16_t)(kk < 2 ? (sv & 0xFFFFu) : (sv >> 16)));
         return int4_dequant8(raw.w[j][kk], sc);
       } else {
@@ -305,48 +472,124 @@ __global__ __launch_bounds__(Cfg<T>::NT, 1) void recon_kernel(KArgs a) {
       }
     };
 
-    // one stage on LDS buffer BUF with the lane's codes in `cur`; stage st+1's
-    // W rows go to the other buffer, stage st+2's codes refill `cur`
-    auto stage = [&](auto buf_c, auto nb_c, int st, Frag (&f0a)[RB], R& cur) {
+    // One stage on ring buffer BUF, software-pipelined over its four k-steps.
+    // On entry ca / fbc hold the A and B operands of k-step 0 and `raw` the
+    // lane's codes of this stage. While the MFMAs of k-step kk run, the A
+    // fragments of kk+1 are read and its B operands dequantised. Before the
+    // last k-step the wave waits for the copies of stage st+1 and joins the
+    // workgroup barrier: every wave is then done with buffer BUF, which takes
+    // the copies of stage st+3 (part A now, parts B and C during k-steps 0
+    // and 1 of stage st+1), and the operands of the next stage's first
+    // k-step are read and dequantised under the last k-step's MFMAs.
+    // Every stage issues its copies and waits the same way, past the last
+    // stage too (the copy index is clamped to the last stage), so all paths
+    // through the loop leave the same copies in flight.
+    auto stage = [&](auto buf_c, auto nb_c, int st, Frag (&ca)[RB], half8 (&fbc)[CB], R& raw) {
       constexpr int BUF = decltype(buf_c)::value;
       constexpr int NB = decltype(nb_c)::value;
-      Frag f1a[RB];
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        Frag (&ca)[RB] = (kk & 1) ? f1a : f0a;
-        Frag (&na)[RB] = (kk & 1) ? f0a : f1a;
-        if (kk + 1 < BK / 16 && NB > 0) read_a(BUF, kk + 1, na);
-        half8 fb[CB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) fb[j] = b_frag(cur, j, kk);
+      constexpr int NXT = (BUF + 1) % 3;
+      const char* rb = Ring<BUF, RING>::p();
+      Frag na[RB];
+      half8 fbn[CB];
+      auto mfmas = [&](Frag (&fa)[RB], half8 (&fb)[CB]) {
 #pragma unroll
         for (int i = 0; i < RB; ++i)
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j] = Mma<T>::mma(ca[i], fb[j], acc[i][j]);
-        if (kk == BK / 16 - 1) {
-          store_w(BUF ^ 1);
-          load_w(min(st + 2, nst - 1));
+          for (int j = 0; j < NB; ++j) acc[i][j] = Mma<T>::mma(fa[i], fb[j], acc[i][j]);
+      };
+      auto copy_ops = [&](Frag (&dst)[RB], const Frag (&src)[RB], half8 (&fd)[CB], const half8 (&fs)[CB]) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) dst[i] = src[i];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) fd[j] = fs[j];
+      };
+      constexpr int PREV = (BUF + 2) % 3;   // buffer of stage st+2 (freed by the last barrier)
+      const int st2 = min(st + 2, nst - 1);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+        if (kk == 0) issue_ops(std::integral_constant<int, PREV>{}, IA1{}, IB1{}, st2);
+        if (kk == 1) issue_ops(std::integral_constant<int, PREV>{}, IB1{}, IC1{}, st2);
+        if constexpr (NB > 0) {
+          read_a3(rb, kk + 1, na);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) fbn[j] = b_frag(raw, j, kk + 1);
+          mfmas(ca, fbc);
+          // 16 MFMAs, up to 4 copies, 8 fragment reads, ~40 dequantisation
+#pragma unroll
+          for (int g = 0; g < RB; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            if (g < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // copy
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NB > 0) copy_ops(ca, na, fbc, fbn);
       }
-      load_raw(min(st + 2, nst - 1), cur);
-      __syncthreads();
-      if (NB > 0) read_a(BUF ^ 1, 0, f0a);
+      // copies of stage st+1 landed once only stage st+2's remain; after the
+      // barrier no wave reads buffer BUF any more
+      dma_sync<DMA_PER_STAGE>();
+      issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IA1{}, min(st + 3, nst - 1));
+      if constexpr (NB > 0) {
+        // operands of the next stage's k-step 0 (its buffer has landed; past
+        // the last stage it holds a clamped copy and the values go unused)
+        read_raw(nb_c, Ring<NXT, RING>::p(), raw);
+        read_a3(Ring<NXT, RING>::p(), 0, na);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fbn[j] = b_frag(raw, j, 0);
+        mfmas(ca, fbc);
+        // copies first (they follow no read of this wave), then the code and
+        // fragment reads, then the dequantisation
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // copy
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NB, 0);   // code reads
+#pragma unroll
+        for (int g = 0; g < RB / 2; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // A fragment reads
+        }
+#pragma unroll
+        for (int g = 0; g < NB * RB - 4 - RB / 2; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        copy_ops(ca, na, fbc, fbn);
+      }
     };
 
-    R raw0, raw1;
-    load_w(0);
-    load_raw(0, raw0);
-    load_raw(min(1, nst - 1), raw1);
-    store_w(0);
-    load_w(min(1, nst - 1));
-    __syncthreads();
-    Frag fa[RB];
+    // stages 0 and 1 and part A of stage 2 are issued back to back and drained
+    // here: entering the loop with no copy in flight lets the compiler see
+    // that each read waits on nothing beyond the explicit per-stage waits
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, min(1, nst - 1));
+    issue_ops(std::integral_constant<int, 2>{}, IA0{}, IA1{}, min(2, nst - 1));   // parts B, C: stage 0
+    dma_sync<0>();
     auto loop = [&](auto nb_c) {
-      if (decltype(nb_c)::value > 0) read_a(0, 0, fa);
-      for (int st = 0; st < nst; st += 2) {
-        stage(std::integral_constant<int, 0>{}, nb_c, st, fa, raw0);
-        stage(std::integral_constant<int, 1>{}, nb_c, st + 1, fa, raw1);
+      constexpr int NB = decltype(nb_c)::value;
+      Frag ca[RB];
+      half8 fbc[CB];
+      R raw;
+      if constexpr (NB > 0) {
+        read_raw(nb_c, Ring<0, RING>::p(), raw);
+        read_a3(Ring<0, RING>::p(), 0, ca);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fbc[j] = b_frag(raw, j, 0);
       }
+      int st = 0;
+      for (; st + 3 <= nst; st += 3) {
+        stage(std::integral_constant<int, 0>{}, nb_c, st, ca, fbc, raw);
+        stage(std::integral_constant<int, 1>{}, nb_c, st + 1, ca, fbc, raw);
+        stage(std::integral_constant<int, 2>{}, nb_c, st + 2, ca, fbc, raw);
+      }
+      if (st < nst) stage(std::integral_constant<int, 0>{}, nb_c, st, ca, fbc, raw);
+      if (st + 1 < nst) stage(std::integral_constant<int, 1>{}, nb_c, st + 1, ca, fbc, raw);
+      dma_sync<0>();   // no copy may still be writing LDS past this point
     };
     dispatch_nb<CB>(ncb, loop);
   } else {
@@ -545,7 +788,10 @@ __global__ __launch_bounds__(Cfg<T>::NT, 1) void recon_kernel(KArgs a) {
   } else {
     // K rows live in wave wf = 0, V rows in wf = 1 (same positions): pass the
     // weights p through LDS.
-    float* ex = (float*)smem;               // [WJN][WJ] p, then [WJN][2] (m, l)
+    char* ex_base;
+    if constexpr (B_REG) ex_base = Ring<0, RING>::p();
+    else ex_base = smem;
+    float* ex = (float*)ex_base;            // [WJN][WJ] p, then [WJN][2] (m, l)
     const int head = hg;
     __syncthreads();
     if (wf == 0 && wave_live) {
@@ -569,8 +815,8 @@ __global__ __launch_bounds__(Cfg<T>::NT, 1) void recon_kernel(KArgs a) {
 
 template <typename T, int MODE, int DH>
 hipError_t launch_mode(const KArgs& k, int grid, hipStream_t s, int epi) {
-  if (epi == EPI_ATTN) recon_kernel<T, MODE, DH, EPI_ATTN><<<grid, Cfg<T>::NT, 0, s>>>(k);
-  else recon_kernel<T, MODE, DH, EPI_KVSTORE><<<grid, Cfg<T>::NT, 0, s>>>(k);
+  if (epi == EPI_ATTN) recon_kernel<T, MODE, DH, EPI_ATTN><<<grid, Cfg<T, MODE>::NT, 0, s>>>(k);
+  else recon_kernel<T, MODE, DH, EPI_KVSTORE><<<grid, Cfg<T, MODE>::NT, 0, s>>>(k);
   return hipGetLastError();
 }
 
@@ -596,12 +842,12 @@ hipError_t dispatch(const ModelView& m, const KArgs& k, int grid, hipStream_t s,
 }  // namespace
 
 int recon_split_len(const ModelView& m) {
-  return m.dtype == TL_DTYPE_F32 ? Cfg<float>::WJ : Cfg<half_t>::WJ;
+  return m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::WJ : Cfg<half_t, TL_CACHE_H_F16>::WJ;
 }
 
 hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t s) {
-  const int BF = m.dtype == TL_DTYPE_F32 ? Cfg<float>::BF : Cfg<half_t>::BF;
-  const int BJ = m.dtype == TL_DTYPE_F32 ? Cfg<float>::BJ : Cfg<half_t>::BJ;
+  const int BF = m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::BF : Cfg<half_t, TL_CACHE_H_F16>::BF;
+  const int BJ = m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::BJ : Cfg<half_t, TL_CACHE_H_F16>::BJ;
   KArgs k{};
   k.cache = r.cache;
   k.layer = r.layer;
@@ -617,7 +863,18 @@ hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t
   k.q = r.q;
   k.part = r.part;
   k.S = r.S;
-  const long grid = (long)k.n_hg * k.n_ptiles * r.n_rows;
+  // head groups per XCD: as many as keep their W rows within 2 MB of the
+  // XCD's 4 MB L2 (the rest streams h), with the sets dividing the 8 XCDs
+  const size_t hg_bytes = (size_t)BF * m.D * (m.dtype == TL_DTYPE_F32 ? 4 : 2);
+  k.hpx = k.n_hg;
+  for (int h = k.n_hg; h >= 1; h >>= 1) {
+    if (k.n_hg % h || (k.n_hg / h) > 8 || 8 % (k.n_hg / h)) continue;
+    k.hpx = h;
+    if ((size_t)h * hg_bytes <= ((size_t)2 << 20)) break;
+  }
+  const int sets = k.n_hg / k.hpx, parts = 8 / sets;
+  const long n_tiles = (long)k.n_ptiles * r.n_rows;
+  const long grid = ((n_tiles + parts - 1) / parts) * parts * k.n_hg;
   if (grid <= 0 || grid > (1L << 30)) return hipErrorInvalidValue;
   return dispatch(m, k, (int)grid, s, EPI_ATTN);
 }
@@ -625,8 +882,8 @@ hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t
 hipError_t launch_recon_store(const ModelView& m, const CacheView& c, int layer, int lane, int T,
                               const void* w_qkv, void* kvbuf, const int32_t* status,
                               hipStream_t s) {
-  const int BF = m.dtype == TL_DTYPE_F32 ? Cfg<float>::BF : Cfg<half_t>::BF;
-  const int BJ = m.dtype == TL_DTYPE_F32 ? Cfg<float>::BJ : Cfg<half_t>::BJ;
+  const int BF = m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::BF : Cfg<half_t, TL_CACHE_H_F16>::BF;
+  const int BJ = m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::BJ : Cfg<half_t, TL_CACHE_H_F16>::BJ;
   KArgs k{};
   k.cache = c;
   k.layer = layer;
