@@ -56,6 +56,43 @@ def recon_flops_bytes(shape, mode_entry_bytes, lanes, loops, t_values):
     return flops, hbytes, launches
 
 
+KERNEL_SOURCES = ("kv_compression_amd/csrc/tl_recon.hip", "kv_compression_amd/csrc/tl_device.h",
+                  "kv_compression_amd/csrc/tl_internal.h")
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the attention kernel's sources: traffic counters taken on other
+    sources do not describe the kernel that runs."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str, mode: str):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, each calibrated on a copy of
+    known size), or None if there is none for this workload or it was taken on
+    different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "recon_attn_%s_%s_traffic.txt" % (workload, mode))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(shape, w, mode, context, loops, budget_s=12.0, max_steps=8):
     """The CPU oracle decoding one lane of the same workload (context `context`,
     same mode and loops); the lane's cache is filled through the oracle's own
@@ -96,6 +133,8 @@ def main():
     ap.add_argument("--workload", default="407m-int4h-ctx4096-b4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile-pass", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="end with a 64 MiB device copy (calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU: the decode step is measured per GPU; "
@@ -184,14 +223,15 @@ def main():
         flops, hbytes, n_launch = recon_flops_bytes(shape, eb, lanes, loops, t_values)
         assert n_launch == launches, (n_launch, launches)
         avg_ms = kern_ms / launches
+        traffic = load_traffic(wl.name, args.mode)
         if args.mode == "kv":
             achieved = hbytes / (kern_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
         else:
             achieved = flops / (kern_ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": traffic}
         extra = {"kernel": "recon_attn" if args.mode != "kv" else "kv_attn",
                  "kernel_avg_us": round(avg_ms * 1e3, 2), "kernel_launches": launches,
                  "kernel_share_of_step": round(kern_ms / gpu_ms, 3),
@@ -199,6 +239,15 @@ def main():
                  "h_bytes_per_launch": hbytes / launches,
                  "h_stream_GBs": round(hbytes / (kern_ms * 1e-3) / 1e9, 1)}
         log("kernel: %d launches, avg %.1f us, %s" % (launches, avg_ms * 1e3, roof))
+
+    if args.calib_copy:
+        src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x 64 MiB")
 
     cpu = None
     if not args.no_cpu_baseline:

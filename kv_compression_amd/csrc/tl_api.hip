@@ -531,7 +531,7 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     if (c->prof_on) {
       while (c->prof_ev.size() < c->prof_used + 2) {
         hipEvent_t e;
-        TL_HIP(hipEventCreate(&e));
+        TL_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
         c->prof_ev.push_back(e);
       }
       TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
