@@ -551,7 +551,7 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
       g.scale = qscale; g.row_lane = ws.row_lane; g.status = ws.status;
       TL_HIP(launch_gemm(mv, g, s));
       TL_HIP(launch_recon_attn(mv, ra, s));
-      split_len = recon_split_len(mv);
+      split_len = recon_split_len(mv, c->mode);
     }
     if (ev_stop) TL_HIP(hipEventRecord(ev_stop, s));
     TL_HIP(launch_attn_merge(mv, rows, ws.row_lane, ws.row_pos, ws.status, ws.part, ws.S, split_len,

@@ -89,14 +89,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(ModelView m, GemmArgs g) {
     X[gi] = (const T*)g.X + (size_t)(ok[gi] ? row : 0) * g.ldx + 8 * (l >> 4) + kbeg;
   }
   float4v acc[4] = {};
-#pragma unroll 2
-  for (int k = 0; k < kq; k += 32) {
-    const typename F::type a = F::load(W + k);
+  // U 32-deep steps per batch: all their loads are issued before the first
+  // MFMA, so a wave keeps U weight loads in flight (decode is latency-bound).
+  // The MFMAs still run in k order, so the sums do not depend on U.
+  constexpr int U = 8;
+  for (int k = 0; k < kq; k += 32 * U) {
+    typename F::type a[U];
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      if (gi < ng) {
-        const typename F::type b = ok[gi] ? F::load(X[gi] + k) : F::zero();
-        acc[gi] = F::mma(a, b, acc[gi]);
+    for (int u = 0; u < U; ++u) a[u] = k + 32 * u < kq ? F::load(W + k + 32 * u) : F::zero();
+    if (ng == 1) {
+      typename F::type b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) b[u] = (ok[0] && k + 32 * u < kq) ? F::load(X[0] + k + 32 * u) : F::zero();
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (k + 32 * u < kq) acc[0] = F::mma(a[u], b[u], acc[0]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k + 32 * u >= kq) break;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          if (gi < ng) {
+            const typename F::type b = ok[gi] ? F::load(X[gi] + k + 32 * u) : F::zero();
+            acc[gi] = F::mma(a[u], b, acc[gi]);
+          }
+        }
       }
     }
   }

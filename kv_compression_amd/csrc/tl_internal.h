@@ -198,7 +198,7 @@ struct ReconArgs {
   int S;                     // splits capacity per (row, head)
 };
 hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& a, hipStream_t s);
-int recon_split_len(const ModelView& m);
+int recon_split_len(const ModelView& m, int mode);
 
 // Prefill: rebuild K|V (fp32 accumulators, kept in fp32) for positions 0..T-1
 // into kvbuf [T, 2D].

@@ -188,6 +188,17 @@ __device__ __forceinline__ void dma_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Make this wave's LDS writes visible to the workgroup without waiting for its
+// memory loads (LDS copies in flight stay in flight): wait for LDS only, then
+// synchronise.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  // vmcnt 63 (no wait), expcnt 7 (no wait), lgkmcnt 0
+  __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Slot swizzle of the 128-byte W rows in the LDS ring: rows R..R+15 (R a
 // multiple of 16) reading the same chunk land on 16 distinct 16-byte slots of
 // a 256-byte bank window, and any 8 consecutive rows on 8 distinct slots.
@@ -213,6 +224,10 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
   constexpr int HRB = block_row_bytes(MODE);
   // one LDS ring buffer of the copied path: W tile, h codes, INT4 scales
   constexpr int RING = B_REG ? BF * BK * ES + BJ * HRB + (MODE == TL_CACHE_H_INT4 ? BJ * 4 : 0) : 16;
+  // per-wave attention partials of the copied-operand path, combined in LDS
+  constexpr int NWV = NT / 64;
+  constexpr int HPW_T = 2 * DH > WF ? 1 : WF / (2 * DH);
+  __shared__ __attribute__((aligned(16))) float comb_lds[B_REG && EPI == EPI_ATTN ? NWV * HPW_T * (DH + 2) : 1];
 
   const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
   const int wf = wave / WJN, wj = wave % WJN;
@@ -286,10 +301,26 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
   const size_t kb_stride = (size_t)cv.max_seq * HRB;
   const int nst = D / BK;
 
-  // 32-position blocks of this wave that hold positions < T; the others are all
-  // zero, so their MFMAs are skipped (whole waves past T also skip the
-  // epilogue) while the wave keeps loading, storing and synchronising
-  const int ncb = min(max((Tn - (j0 + wj * WJ) + 31) / 32, 0), CB);
+  // Tile-local position of this lane in the wave's 32-position block j. The
+  // copied-operand path deals the tile's blocks round-robin to the waves
+  // (block j*WJN + wj), so a partial last tile spreads over all waves; the
+  // LDS-staged path gives each wave WJ consecutive positions.
+  auto pos_local = [&](int j) -> int {
+    return B_REG ? (j * WJN + wj) * 32 + (l & 31) : wj * WJ + j * 32 + (l & 31);
+  };
+  // blocks of this wave that hold positions < T (a prefix of j = 0, 1, ...);
+  // the others are all zero, so their MFMAs are skipped while the wave keeps
+  // loading and synchronising
+  int ncb;
+  if constexpr (B_REG) {
+    const int nbl = min(max((Tn - j0 + 31) / 32, 0), BJ / 32);
+    ncb = 0;
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+      if (j * WJN + wj < nbl) ncb = j + 1;
+  } else {
+    ncb = min(max((Tn - (j0 + wj * WJ) + 31) / 32, 0), CB);
+  }
   const bool wave_live = ncb > 0;
 
   typedef typename Mma<T>::frag Frag;
@@ -424,12 +455,12 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     uint32_t vmask = 0;   // positions < T
 #pragma unroll
     for (int j = 0; j < CB; ++j)
-      if (j0 + wj * WJ + j * 32 + (l & 31) < Tn) vmask |= 1u << j;
+      if (j0 + pos_local(j) < Tn) vmask |= 1u << j;
     half_t s8[CB];
     if constexpr (MODE == TL_CACHE_H_INT8) {
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
-        const int pc = min(j0 + wj * WJ + j * 32 + (l & 31), Tn - 1);
+        const int pc = min(j0 + pos_local(j), Tn - 1);
         s8[j] = ((vmask >> j) & 1) ? h_from_bits(*cv.int8_scale(a.layer, lane, pc)) : (half_t)0.f;
       }
     }
@@ -447,7 +478,7 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
       constexpr int NB = decltype(nb_c)::value;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int pos = wj * WJ + j * 32 + (l & 31);
+        const int pos = pos_local(j);
         const char* hs = rb + W_BYTES + ((pos >> 4) * (32 * NQ) + hb * NQ * 16 + (pos & 15)) * 16;
         if constexpr (MODE == TL_CACHE_H_INT4) {
           raw.w[j] = *(const u32x4*)hs;
@@ -692,7 +723,7 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     float* out = (float*)a.kvbuf;
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
-      const int pos = j0 + wj * WJ + j * 32 + (l & 31);
+      const int pos = j0 + pos_local(j);
       if (pos >= Tn) continue;
 #pragma unroll
       for (int i = 0; i < RB; ++i)
@@ -728,7 +759,7 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       s[j] += __shfl_xor(s[j], 32, 64);
-      const int pos = j0 + wj * WJ + j * 32 + (l & 31);
+      const int pos = j0 + pos_local(j);
       if (pos >= Tn) s[j] = -__builtin_inff();
     }
   };
@@ -748,8 +779,8 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     for (int o = 16; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, 64);
   };
   // o over V blocks rb0 .. rb0+KB-1 with weights p, reduced over the 32 lanes
-  // of each half and written to the partial of (r, head, split).
-  auto values = [&](int rb0, int head, const float (&p)[CB], float m, float lsum) {
+  // of each half and written, with (m, lsum), to dst[0 .. DH+2).
+  auto values = [&](int rb0, float* dst, const float (&p)[CB], float m, float lsum) {
     constexpr int NV = KB * 16;
     float v[NV];
 #pragma unroll
@@ -762,7 +793,6 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
         v[kb * 16 + i] = t;
       }
     reduce_scatter32<NV>(v, l);
-    float* dst = a.part + (((size_t)r * a.H + head) * a.S + split) * (DH + 2);
     if (l == 0) { dst[0] = m; dst[1] = lsum; }
     constexpr int FL = NV >= 32 ? NV / 32 : 1;
     if (NV >= 32 || (l & 1) == 0) {
@@ -775,7 +805,48 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     }
   };
 
-  if constexpr (!kCross) {
+  auto part_of = [&](int head, int sp) -> float* {
+    return a.part + (((size_t)r * a.H + head) * a.S + sp) * (DH + 2);
+  };
+  if constexpr (B_REG) {
+    // Every wave holds all heads of the tile for its positions: each writes
+    // its (max, sum, o) per head to LDS (a wave with no position < T writes
+    // the neutral partial), and one partial per (row, head, tile) is formed by
+    // combining the waves in order w = 0, 1, ...
+    static_assert(!kCross, "copied-operand tiles hold whole heads");
+    float* comb = (float*)comb_lds;   // [NWV][HPW][DH + 2]
+#pragma unroll
+    for (int g = 0; g < HPW; ++g) {
+      float* dst = comb + (wave * HPW + g) * (DH + 2);
+      if (wave_live) {
+        const int head = hg * (BF / (2 * DH)) + g;
+        float s[CB], m, lsum;
+        scores(g * 2 * KB, head, s);
+        softmax(s, m, lsum);
+        values(g * 2 * KB + KB, dst, s, m, lsum);
+      } else {
+        for (int e = l; e < DH + 2; e += 64) dst[e] = e == 0 ? -__builtin_inff() : 0.f;
+      }
+    }
+    lds_sync();
+    if (tid < HPW * DH) {
+      const int g = tid / DH, dim = tid % DH;
+      float M = comb[g * (DH + 2)];
+#pragma unroll
+      for (int w = 1; w < NWV; ++w) M = fmaxf(M, comb[(w * HPW + g) * (DH + 2)]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        const float* c = comb + (w * HPW + g) * (DH + 2);
+        const float e = c[0] == -__builtin_inff() ? 0.f : exp2f((c[0] - M) * kLog2e);
+        L = fmaf(c[1], e, L);
+        O = fmaf(c[2 + dim], e, O);
+      }
+      float* dst = part_of(hg * (BF / (2 * DH)) + g, ptile);
+      if (dim == 0) { dst[0] = M; dst[1] = L; }
+      dst[2 + dim] = O;
+    }
+  } else if constexpr (!kCross) {
     if (!wave_live) return;
 #pragma unroll
     for (int g = 0; g < HPW; ++g) {
@@ -783,7 +854,7 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
       float s[CB], m, lsum;
       scores(g * 2 * KB, head, s);
       softmax(s, m, lsum);
-      values(g * 2 * KB + KB, head, s, m, lsum);
+      values(g * 2 * KB + KB, part_of(head, split), s, m, lsum);
     }
   } else {
     // K rows live in wave wf = 0, V rows in wf = 1 (same positions): pass the
@@ -808,7 +879,7 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
       float p[CB];
 #pragma unroll
       for (int j = 0; j < CB; ++j) p[j] = ex[wj * WJ + j * 32 + (l & 31)];
-      values(0, head, p, ex[WJN * WJ + 2 * wj], ex[WJN * WJ + 2 * wj + 1]);
+      values(0, part_of(head, split), p, ex[WJN * WJ + 2 * wj], ex[WJN * WJ + 2 * wj + 1]);
     }
   }
 }
@@ -841,7 +912,12 @@ hipError_t dispatch(const ModelView& m, const KArgs& k, int grid, hipStream_t s,
 
 }  // namespace
 
-int recon_split_len(const ModelView& m) {
+bool combined_splits(const ModelView& m, int mode) {
+  return m.dtype == TL_DTYPE_F16 && (mode == TL_CACHE_H_INT4 || mode == TL_CACHE_H_INT8);
+}
+
+int recon_split_len(const ModelView& m, int mode) {
+  if (combined_splits(m, mode)) return Cfg<half_t, TL_CACHE_H_INT4>::BJ;
   return m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::WJ : Cfg<half_t, TL_CACHE_H_F16>::WJ;
 }
 

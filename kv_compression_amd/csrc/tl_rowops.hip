@@ -197,9 +197,27 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
 __device__ int block_argmax(const float* lg, int V) {
   __shared__ float sv[kRowThreads / 64];
   __shared__ int si[kRowThreads / 64];
-  float best = -__builtin_inff();
-  int bi = 0x7fffffff;
-  for (int j = threadIdx.x; j < V; j += blockDim.x) argmax_merge(best, bi, lg[j], j);
+  // eight independent (value, index) pairs so the loads of a thread are all in
+  // flight together; the merge (larger value, then lower index) is
+  // order-independent, so the result is the same as a sequential scan
+  float bv[8];
+  int bx[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) { bv[u] = -__builtin_inff(); bx[u] = 0x7fffffff; }
+  const int step = blockDim.x;
+  int j = threadIdx.x;
+  for (; j + 7 * step < V; j += 8 * step) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = lg[j + u * step];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) argmax_merge(bv[u], bx[u], v[u], j + u * step);
+  }
+  for (; j < V; j += step) argmax_merge(bv[0], bx[0], lg[j], j);
+  float best = bv[0];
+  int bi = bx[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) argmax_merge(best, bi, bv[u], bx[u]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float v2 = __shfl_xor(best, o, 64);
