@@ -521,6 +521,13 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     AppendArgs a{};
     a.src = HS_NORM; a.n = rows; a.layer = layer; a.x = ws.x; a.gain = W.norm1;
     a.row_lane = ws.row_lane; a.row_pos = ws.row_pos; a.status = ws.status; a.h_out = ws.h;
+    if (layer > mv.n_pre) {
+      // the residual entering this layer is the one after loop iteration
+      // layer - 1 - n_pre: its safety check runs here (rows still active)
+      a.check_iter = layer - 1 - mv.n_pre;
+      a.norms = ws.norms; a.status_w = ws.status; a.l_max = c->l_max;
+      a.check = check ? 1 : 0; a.thr = safety_threshold;
+    }
     TL_HIP(launch_norm_append(mv, c->cv, a, s));
     ReconArgs ra{};
     ra.cache = c->cv; ra.layer = layer; ra.w_qkv = W.w_qkv; ra.n_rows = rows; ra.t_ub = t_ub;
@@ -566,11 +573,14 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     GemmArgs gd = gemm_args(W.w_down, mv.F, ws.a, mv.F, rows, D, mv.F, EPI_ADD_F32, ws.x, D);
     gd.row_lane = ws.row_lane; gd.status = ws.status;
     TL_HIP(launch_gemm(mv, gd, s));
-    if (layer >= mv.n_pre)
-      TL_HIP(launch_resid_norm(mv, rows, ws.x, ws.row_lane, ws.status, ws.norms, c->l_max,
-                               layer - mv.n_pre, check ? 1 : 0, safety_threshold, s));
   }
-  TL_HIP(launch_rmsnorm(mv, n, ws.x, mv.final_norm, ws.z, ws.row_lane, ws.status, s));
+  // every row's last loop iteration is checked with the final norm (the
+  // earlier ones were checked on entry to the next layer)
+  NormCheck fc{};
+  fc.norms = ws.norms; fc.status = ws.status; fc.l_max = c->l_max;
+  fc.check = check ? 1 : 0; fc.thr = safety_threshold;
+  for (int r = 0; r < n; ++r) fc.iter[r] = loops[order[r]] - 1;
+  TL_HIP(launch_rmsnorm(mv, n, ws.x, mv.final_norm, ws.z, ws.row_lane, ws.status, s, &fc));
   float* lg = d_logits ? d_logits : ws.logits;
   GemmArgs gh = gemm_args(mv.lm_head, D, ws.z, D, n, mv.V, D, EPI_LOGITS, lg, mv.V);
   gh.row_lane = ws.row_lane; gh.status = ws.status; gh.row_slot = d_logits ? ws.row_slot : nullptr;

@@ -138,19 +138,36 @@ struct AppendArgs {
   int fixed_lane, pos0;
   const int32_t* status;     // nullable
   void* h_out;               // nullable
+  // HS_NORM, decode: the residual entering this layer is the one after loop
+  // iteration check_iter (-1: none); its FP32 norm goes to norms[lane, iter]
+  // and, if check and !(norm <= thr), the lane aborts before this layer
+  int check_iter = -1;
+  float* norms = nullptr;
+  int32_t* status_w = nullptr;
+  int l_max = 0, check = 0;
+  float thr = 0.f;
 };
 hipError_t launch_norm_append(const ModelView& m, const CacheView& c, const AppendArgs& a,
                               hipStream_t s);
 
-// out[row] = dtype(RMSNorm(x[row]) * g) for rows 0..n-1 (skips aborted rows).
-hipError_t launch_rmsnorm(const ModelView& m, int n, const float* x, const void* gain, void* out,
-                          const int32_t* row_lane, const int32_t* status, hipStream_t s);
+// Safety check folded into a row norm: row r holds the residual after loop
+// iteration iter[r]; its FP32 norm goes to norms[lane, iter[r]] and, if check
+// and !(norm <= thr), the lane aborts.
+struct NormCheck {
+  float* norms;
+  int32_t* status;
+  int l_max, check;
+  float thr;
+  int32_t iter[kMaxBatch];
+};
 
-// Per row: norm = sqrt(sum x^2) (fp32); norms[lane, iter] = norm; if check and
-// !(norm <= thr): status[lane] = ABORTED.
-hipError_t launch_resid_norm(const ModelView& m, int n, const float* x, const int32_t* row_lane,
-                             int32_t* status, float* norms, int l_max, int iter, int check,
-                             float thr, hipStream_t s);
+// out[row] = dtype(RMSNorm(x[row]) * g) for rows 0..n-1 (skips aborted rows);
+// with chk, also the safety check of each row (a row that aborts is skipped).
+hipError_t launch_rmsnorm(const ModelView& m, int n, const float* x, const void* gain, void* out,
+                          const int32_t* row_lane, const int32_t* status, hipStream_t s,
+                          const NormCheck* chk = nullptr);
+
+
 
 // Skinny / prefill GEMM: Y[row, f] = sum_k W[f, k] X[row, k] for rows < M,
 // f < N, then the epilogue.

@@ -71,6 +71,16 @@ __global__ __launch_bounds__(kRowThreads) void norm_append_kernel(ModelView m, C
       ss += xv[i] * xv[i];
     }
     ss = block_sum(ss, red);
+    if (a.check_iter >= 0) {
+      // safety check of the previous loop iteration (every thread holds the
+      // same sum, so the early exit is uniform)
+      const float nrm = __fsqrt_rn(ss);
+      if (threadIdx.x == 0) a.norms[(size_t)lane * a.l_max + a.check_iter] = nrm;
+      if (a.check && !(nrm <= a.thr)) {
+        if (threadIdx.x == 0) a.status_w[lane] = TL_LANE_ABORTED;
+        return;
+      }
+    }
     const float inv = __fdiv_rn(1.f, __fsqrt_rn(__fdiv_rn(ss, (float)D) + m.eps));
     const T* g = (const T*)a.gain;
 #pragma unroll
@@ -141,11 +151,11 @@ __global__ __launch_bounds__(kRowThreads) void norm_append_kernel(ModelView m, C
   }
 }
 
-template <typename T, int EPT>
+template <typename T, int EPT, bool CHECK>
 __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(ModelView m, const float* x,
                                                               const void* gain, void* out,
                                                               const int32_t* row_lane,
-                                                              const int32_t* status) {
+                                                              const int32_t* status, NormCheck chk) {
   __shared__ float red[kRowThreads / 64];
   const int r = blockIdx.x;
   if (status && status[row_lane[r]] == TL_LANE_ABORTED) return;
@@ -157,36 +167,20 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(ModelView m, const
     ss += xv[i] * xv[i];
   }
   ss = block_sum(ss, red);
+  if constexpr (CHECK) {
+    const int lane = row_lane[r];
+    const float nrm = __fsqrt_rn(ss);
+    if (threadIdx.x == 0) chk.norms[(size_t)lane * chk.l_max + chk.iter[r]] = nrm;
+    if (chk.check && !(nrm <= chk.thr)) {
+      if (threadIdx.x == 0) chk.status[lane] = TL_LANE_ABORTED;
+      return;
+    }
+  }
   const float inv = __fdiv_rn(1.f, __fsqrt_rn(__fdiv_rn(ss, (float)D) + m.eps));
   const T* g = (const T*)gain;
   T* o = (T*)out + (size_t)r * D;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) o[e0 + i] = from_f<T>(xv[i] * inv * to_f(g[e0 + i]));
-}
-
-template <int EPT>
-__global__ __launch_bounds__(kRowThreads) void resid_norm_kernel(int D, const float* x,
-                                                                 const int32_t* row_lane,
-                                                                 int32_t* status, float* norms,
-                                                                 int l_max, int iter, int check,
-                                                                 float thr) {
-  __shared__ float red[kRowThreads / 64];
-  const int r = blockIdx.x;
-  const int lane = row_lane[r];
-  if (status[lane] == TL_LANE_ABORTED) return;
-  const int e0 = threadIdx.x * EPT;
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const float v = x[(size_t)r * D + e0 + i];
-    ss += v * v;
-  }
-  ss = block_sum(ss, red);
-  if (threadIdx.x == 0) {
-    const float nrm = __fsqrt_rn(ss);
-    norms[(size_t)lane * l_max + iter] = nrm;
-    if (check && !(nrm <= thr)) status[lane] = TL_LANE_ABORTED;
-  }
 }
 
 // argmax with ties to the lowest index: (value, index) pairs, larger value
@@ -370,35 +364,23 @@ hipError_t launch_norm_append(const ModelView& m, const CacheView& c, const Appe
 }
 
 hipError_t launch_rmsnorm(const ModelView& m, int n, const float* x, const void* gain, void* out,
-                          const int32_t* row_lane, const int32_t* status, hipStream_t s) {
+                          const int32_t* row_lane, const int32_t* status, hipStream_t s,
+                          const NormCheck* chk) {
   const int nt = row_threads(m.D);
   const int ept = m.D / nt;
-  if (m.dtype == TL_DTYPE_F32 && ept == 1)
-    rmsnorm_kernel<float, 1><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status);
-  else if (m.dtype == TL_DTYPE_F16 && ept == 1)
-    rmsnorm_kernel<half_t, 1><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status);
-  else if (m.dtype == TL_DTYPE_F16 && ept == 4)
-    rmsnorm_kernel<half_t, 4><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status);
-  else if (m.dtype == TL_DTYPE_F16 && ept == 8)
-    rmsnorm_kernel<half_t, 8><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_resid_norm(const ModelView& m, int n, const float* x, const int32_t* row_lane,
-                             int32_t* status, float* norms, int l_max, int iter, int check,
-                             float thr, hipStream_t s) {
-  const int nt = row_threads(m.D);
-  const int ept = m.D / nt;
-  if (ept == 1)
-    resid_norm_kernel<1><<<n, nt, 0, s>>>(m.D, x, row_lane, status, norms, l_max, iter, check, thr);
-  else if (ept == 4)
-    resid_norm_kernel<4><<<n, nt, 0, s>>>(m.D, x, row_lane, status, norms, l_max, iter, check, thr);
-  else if (ept == 8)
-    resid_norm_kernel<8><<<n, nt, 0, s>>>(m.D, x, row_lane, status, norms, l_max, iter, check, thr);
-  else
-    return hipErrorInvalidValue;
+  NormCheck c{};
+  if (chk) c = *chk;
+#define TL_RN(T_, E_)                                                                        \
+  do {                                                                                       \
+    if (chk) rmsnorm_kernel<T_, E_, true><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status, c); \
+    else rmsnorm_kernel<T_, E_, false><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status, c);   \
+  } while (0)
+  if (m.dtype == TL_DTYPE_F32 && ept == 1) TL_RN(float, 1);
+  else if (m.dtype == TL_DTYPE_F16 && ept == 1) TL_RN(half_t, 1);
+  else if (m.dtype == TL_DTYPE_F16 && ept == 4) TL_RN(half_t, 4);
+  else if (m.dtype == TL_DTYPE_F16 && ept == 8) TL_RN(half_t, 8);
+  else return hipErrorInvalidValue;
+#undef TL_RN
   return hipGetLastError();
 }
 
