@@ -211,15 +211,21 @@ def prior_h(seed: int, layer: int, lane: int, positions, d_model: int) -> np.nda
     """
     pos = np.asarray(positions, dtype=np.uint32).reshape(-1)
     k = np.arange(d_model, dtype=np.uint32)
-    ctr = np.empty((pos.size, d_model, 4), dtype=np.uint32)
-    ctr[..., 0] = k[None, :]
-    ctr[..., 1] = pos[:, None]
-    ctr[..., 2] = np.uint32(lane)
-    ctr[..., 3] = np.uint32(layer)
     key = np.array([seed, PHILOX_H_KEY1], dtype=np.uint32)
-    out = philox4x32_10(ctr, key)                     # [P, D, 4] uint32
-    lo = (out & np.uint32(0xFFFF)).astype(np.int64)
-    hi = (out >> np.uint32(16)).astype(np.int64)
-    s = lo.sum(axis=-1) + hi.sum(axis=-1)             # sum of eight 16-bit uniforms
-    centred = (s - 262140).astype(np.float32)         # exact: |value| < 2**24
-    return centred * NORMAL_SCALE_F32                 # one fp32 rounding
+    res = np.empty((pos.size, d_model), dtype=np.float32)
+    # chunks of positions keep the generator's temporaries in cache
+    step = max(1, (1 << 16) // max(d_model, 1))
+    for p0 in range(0, pos.size, step):
+        pc = pos[p0:p0 + step]
+        ctr = np.empty((pc.size, d_model, 4), dtype=np.uint32)
+        ctr[..., 0] = k[None, :]
+        ctr[..., 1] = pc[:, None]
+        ctr[..., 2] = np.uint32(lane)
+        ctr[..., 3] = np.uint32(layer)
+        out = philox4x32_10(ctr, key)                     # [P, D, 4] uint32
+        lo = (out & np.uint32(0xFFFF)).astype(np.int64)
+        hi = (out >> np.uint32(16)).astype(np.int64)
+        s = lo.sum(axis=-1) + hi.sum(axis=-1)             # sum of eight 16-bit uniforms
+        centred = (s - 262140).astype(np.float32)         # exact: |value| < 2**24
+        res[p0:p0 + pc.size] = centred * NORMAL_SCALE_F32  # one fp32 rounding
+    return res

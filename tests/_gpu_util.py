@@ -59,6 +59,18 @@ class GpuModel:
         return self.tl.Cache(self.model, mode, n_lanes, max_seq, l_max)
 
 
+_MODELS = {}
+
+
+def gpu_model(shape, seed=0, random_gains=False):
+    """Seeded weights (numpy) and their device model, shared by the GPU tests."""
+    key = (shape.name, seed, random_gains)
+    if key not in _MODELS:
+        w = synth.make_weights(shape, seed, random_gains=random_gains)
+        _MODELS[key] = (w, GpuModel(shape, w))
+    return _MODELS[key]
+
+
 def decode(tlc, lanes, loops, tokens, threshold=math.inf, want_logits=True):
     """One tl_decode_step; returns host (tokens, logits, status)."""
     import torch

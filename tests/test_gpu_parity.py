@@ -11,24 +11,13 @@ import pytest
 import synth
 import oracle
 from oracle import looped
-from tests._gpu_util import GpuModel, decode, record, rel_err, token_ok, torch_gpu, REL_TOL
+from tests._gpu_util import decode, gpu_model, record, rel_err, token_ok, torch_gpu, REL_TOL
 
 pytestmark = pytest.mark.gpu
 
 S407 = synth.SHAPES["407m"]
 S2B = synth.SHAPES["2b"]
 TINY = synth.SHAPES["tiny"]
-
-_models = {}
-
-
-def gpu_model(shape, seed=0, random_gains=False):
-    key = (shape.name, seed, random_gains)
-    if key not in _models:
-        w = synth.make_weights(shape, seed, random_gains=random_gains)
-        _models[key] = (w, GpuModel(shape, w))
-    return _models[key]
-
 
 # ------------------------------------------------------------------ codec
 @pytest.mark.parametrize("mode", ["int4", "int8", "f16"])
