@@ -40,23 +40,37 @@ namespace {
 //   LDS reads of the next.
 //   fp16 h (staged through LDS from registers): 8 waves, 2 per SIMD, 128 x 64.
 //   fp32: 4 waves of 64 x 64.
-template <typename T, int MODE> struct Cfg {
-  static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 64, BK = 64;
+// OCC: workgroups resident per CU (waves per SIMD), which sets the register
+// budget of a wave (512 / OCC, accumulators included).
+template <typename T, int MODE, int DH> struct Cfg {
+  static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
-template <> struct Cfg<half_t, TL_CACHE_H_INT4> {
-  static constexpr int BF = 256, BJ = 256, WF = 256, WJ = 64, BK = 64;
+// integer codes: every wave covers all BF features of its positions
+template <int MODE, int DH> struct CfgCodes {
+  static constexpr int BF = 256, BJ = 256, WF = 256, WJ = 64, BK = 64, OCC = 1;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
-template <> struct Cfg<half_t, TL_CACHE_H_INT8> : Cfg<half_t, TL_CACHE_H_INT4> {};
-template <int MODE> struct Cfg<float, MODE> {
-  static constexpr int BF = 128, BJ = 128, WF = 64, WJ = 64, BK = 64;
+template <int DH> struct Cfg<half_t, TL_CACHE_H_INT8, DH> : CfgCodes<TL_CACHE_H_INT8, DH> {};
+template <int DH> struct Cfg<half_t, TL_CACHE_H_INT4, DH> : CfgCodes<TL_CACHE_H_INT4, DH> {};
+// INT4 codes with 64-wide heads: one head (K and V rows) per workgroup and two
+// workgroups per CU, so one workgroup's prologue and epilogue run under the
+// other's MFMAs, and a dispatch round that is only partly filled still
+// spreads over twice as many CUs
+template <> struct Cfg<half_t, TL_CACHE_H_INT4, 64> {
+  static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 2;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
-// every fp16 configuration shares BF, BJ and WJ (grid shape and split length)
-static_assert(Cfg<half_t, TL_CACHE_H_INT4>::BF == Cfg<half_t, TL_CACHE_H_F16>::BF &&
-              Cfg<half_t, TL_CACHE_H_INT4>::BJ == Cfg<half_t, TL_CACHE_H_F16>::BJ &&
-              Cfg<half_t, TL_CACHE_H_INT4>::WJ == Cfg<half_t, TL_CACHE_H_F16>::WJ, "fp16 tiles");
+template <int MODE, int DH> struct Cfg<float, MODE, DH> {
+  static constexpr int BF = 128, BJ = 128, WF = 64, WJ = 64, BK = 64, OCC = 1;
+  static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+};
+// every fp16 configuration shares BJ and WJ (split length)
+static_assert(Cfg<half_t, TL_CACHE_H_INT4, 64>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
+              Cfg<half_t, TL_CACHE_H_INT4, 128>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
+              Cfg<half_t, TL_CACHE_H_INT8, 64>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
+              Cfg<half_t, TL_CACHE_H_INT4, 64>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ &&
+              Cfg<half_t, TL_CACHE_H_INT8, 64>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ, "fp16 tiles");
 
 enum { EPI_ATTN = 0, EPI_KVSTORE = 1 };
 
@@ -101,34 +115,78 @@ template <int MODE> struct HLoad { static constexpr int NCH = 1, CPP = 1; };
 template <> struct HLoad<TL_CACHE_H_F16> { static constexpr int NCH = 4, CPP = 8; };   // 512 threads
 template <> struct HLoad<TL_CACHE_H_F32> { static constexpr int NCH = 8, CPP = 16; };  // 256 threads
 
-// One level of a reduce-scatter over lane bit O: the lanes with that bit set
-// keep the upper half of v, the others the lower half, each adding its
+// Value of lane partner(l) for a data-parallel-primitive pattern within each
+// row of 16 lanes: row_mirror (l ^ 15), row_half_mirror (l ^ 7) and the quad
+// permutations l ^ 2 and l ^ 1. Lane bit 4 goes through the LDS crossbar.
+constexpr int kDppRowMirror = 0x140, kDppHalfMirror = 0x141, kDppXor2 = 0x4E, kDppXor1 = 0xB1;
+template <int CTRL>
+__device__ __forceinline__ float lane_swap(float x) {
+  if constexpr (CTRL == 16) return __shfl_xor(x, 16, 64);
+  else return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Lane bits of a 32-lane half-wave in the order the reductions visit them,
+// with the partner pattern of each: the partner differs in the visited bit and
+// agrees in the bits visited before it, which is all a butterfly needs.
+constexpr int kRsBit[5] = {3, 2, 1, 0, 4};
+constexpr int kRsCtrl[5] = {kDppRowMirror, kDppHalfMirror, kDppXor2, kDppXor1, 16};
+
+// One level of a reduce-scatter over lane bit kRsBit[LV]: the lanes with that
+// bit set keep the upper half of v, the others the lower half, each adding its
 // partner's copy. LEN is the current length (compile time, so v stays in
-// registers).
-template <int LEN, int O>
+// registers); at LEN 1 the level is a plain all-reduce.
+template <int LEN, int LV>
 __device__ __forceinline__ void rs_level(float* v, int l) {
+  constexpr int CTRL = kRsCtrl[LV];
   if constexpr (LEN >= 2) {
-    const bool up = (l & O) != 0;
+    const bool up = (l >> kRsBit[LV]) & 1;
 #pragma unroll
     for (int e = 0; e < LEN / 2; ++e) {
       const float keep = up ? v[e + LEN / 2] : v[e];
       const float send = up ? v[e] : v[e + LEN / 2];
-      v[e] = keep + __shfl_xor(send, O, 64);
+      v[e] = keep + lane_swap<CTRL>(send);
     }
   } else {
-    v[0] += __shfl_xor(v[0], O, 64);
+    v[0] += lane_swap<CTRL>(v[0]);
   }
 }
-// Sum v[0..NV) over the 32 lanes of each half-wave; lane l ends with
-// max(NV / 32, 1) values: indices (l % 32) * (NV / 32) + k (NV >= 32) or
-// (l % 32) / 2 (NV == 16, lanes l and l ^ 1 hold the same value).
+// Sum v[0..NV) over the 32 lanes of each half-wave. Lane l ends with
+// max(NV / 32, 1) values, v[k] holding index rs_index<NV>(l, k); for NV == 16
+// lanes l and l ^ 16 hold the same value.
 template <int NV>
 __device__ __forceinline__ void reduce_scatter32(float* v, int l) {
-  rs_level<NV, 16>(v, l);
-  rs_level<(NV >> 1), 8>(v, l);
-  rs_level<(NV >> 2), 4>(v, l);
-  rs_level<(NV >> 3), 2>(v, l);
-  rs_level<(NV >> 4), 1>(v, l);
+  rs_level<NV, 0>(v, l);
+  rs_level<(NV >> 1), 1>(v, l);
+  rs_level<(NV >> 2), 2>(v, l);
+  rs_level<(NV >> 3), 3>(v, l);
+  rs_level<(NV >> 4), 4>(v, l);
+}
+template <int NV>
+__device__ __forceinline__ int rs_index(int l, int k) {
+  int idx = 0, len = NV;
+#pragma unroll
+  for (int lv = 0; lv < 5; ++lv)
+    if (len >= 2) {
+      len >>= 1;
+      idx += ((l >> kRsBit[lv]) & 1) * len;
+    }
+  return idx + k;
+}
+// All-reduce (max or sum) over the 32 lanes of each half-wave.
+template <bool MAX>
+__device__ __forceinline__ float allreduce32(float x) {
+#pragma unroll
+  for (int lv = 0; lv < 5; ++lv) {
+    float y;
+    switch (lv) {
+      case 0: y = lane_swap<kRsCtrl[0]>(x); break;
+      case 1: y = lane_swap<kRsCtrl[1]>(x); break;
+      case 2: y = lane_swap<kRsCtrl[2]>(x); break;
+      case 3: y = lane_swap<kRsCtrl[3]>(x); break;
+      default: y = lane_swap<kRsCtrl[4]>(x); break;
+    }
+    x = MAX ? fmaxf(x, y) : x + y;
+  }
+  return x;
 }
 
 // Call f(integral_constant<int, n>) for the run-time n in [0, CB].
@@ -205,8 +263,8 @@ __device__ __forceinline__ void lds_sync() {
 __device__ __forceinline__ int w_swz(int R) { return ((R >> 1) ^ (R << 2)) & 7; }
 
 template <typename T, int MODE, int DH, int EPI>
-__global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
-  typedef Cfg<T, MODE> C;
+__global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) void recon_kernel(KArgs a) {
+  typedef Cfg<T, MODE, DH> C;
   constexpr int BF = C::BF, BJ = C::BJ, WF = C::WF, WJ = C::WJ, BK = C::BK, NT = C::NT;
   constexpr int WJN = BJ / WJ;                // waves along positions
   constexpr int ES = sizeof(T);
@@ -228,6 +286,8 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
   constexpr int NWV = NT / 64;
   constexpr int HPW_T = 2 * DH > WF ? 1 : WF / (2 * DH);
   __shared__ __attribute__((aligned(16))) float comb_lds[B_REG && EPI == EPI_ATTN ? NWV * HPW_T * (DH + 2) : 1];
+  // the queries of the workgroup's heads, staged at the start
+  __shared__ __attribute__((aligned(16))) float q_lds[B_REG && EPI == EPI_ATTN ? HPW_T * DH : 1];
 
   const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
   const int wf = wave / WJN, wj = wave % WJN;
@@ -594,6 +654,10 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
       }
     };
 
+    // the workgroup's queries ride along with the first copies
+    float qpre = 0.f;
+    if constexpr (EPI == EPI_ATTN)
+      if (tid < HPW_T * DH) qpre = a.q[(size_t)r * D + hg * HPW_T * DH + tid];
     // stages 0 and 1 and part A of stage 2 are issued back to back and drained
     // here: entering the loop with no copy in flight lets the compiler see
     // that each read waits on nothing beyond the explicit per-stage waits
@@ -601,6 +665,8 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     issue(std::integral_constant<int, 1>{}, min(1, nst - 1));
     issue_ops(std::integral_constant<int, 2>{}, IA0{}, IA1{}, min(2, nst - 1));   // parts B, C: stage 0
     dma_sync<0>();
+    if constexpr (EPI == EPI_ATTN)
+      if (tid < HPW_T * DH) q_lds[tid] = qpre;   // read after the loop's barriers
     auto loop = [&](auto nb_c) {
       constexpr int NB = decltype(nb_c)::value;
       Frag ca[RB];
@@ -744,8 +810,7 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
   constexpr int HPW = kCross ? 1 : WF / (2 * DH);   // heads per wave
   constexpr int KB = DH / 32;                        // row blocks per K (or V) of a head
 
-  auto scores = [&](int rb0, int head, float (&s)[CB]) {
-    const float* qh = a.q + (size_t)r * D + head * DH;
+  auto scores = [&](int rb0, const float* qh, float (&s)[CB]) {
 #pragma unroll
     for (int j = 0; j < CB; ++j) s[j] = 0.f;
 #pragma unroll
@@ -767,16 +832,14 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     m = s[0];
 #pragma unroll
     for (int j = 1; j < CB; ++j) m = fmaxf(m, s[j]);
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = allreduce32<true>(m);
     lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       s[j] = s[j] == -__builtin_inff() ? 0.f : exp2f((s[j] - m) * kLog2e);
       lsum += s[j];
     }
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, 64);
+    lsum = allreduce32<false>(lsum);
   };
   // o over V blocks rb0 .. rb0+KB-1 with weights p, reduced over the 32 lanes
   // of each half and written, with (m, lsum), to dst[0 .. DH+2).
@@ -795,10 +858,10 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     reduce_scatter32<NV>(v, l);
     if (l == 0) { dst[0] = m; dst[1] = lsum; }
     constexpr int FL = NV >= 32 ? NV / 32 : 1;
-    if (NV >= 32 || (l & 1) == 0) {
+    if (NV >= 32 || (l & 16) == 0) {
 #pragma unroll
       for (int k = 0; k < FL; ++k) {
-        const int idx = NV >= 32 ? (l & 31) * FL + k : (l & 31) >> 1;
+        const int idx = rs_index<NV>(l, k);
         const int kb = idx >> 4, i = idx & 15;
         dst[2 + kb * 32 + 8 * (i >> 2) + 4 * half_id + (i & 3)] = v[k];
       }
@@ -819,9 +882,8 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     for (int g = 0; g < HPW; ++g) {
       float* dst = comb + (wave * HPW + g) * (DH + 2);
       if (wave_live) {
-        const int head = hg * (BF / (2 * DH)) + g;
         float s[CB], m, lsum;
-        scores(g * 2 * KB, head, s);
+        scores(g * 2 * KB, q_lds + g * DH, s);
         softmax(s, m, lsum);
         values(g * 2 * KB + KB, dst, s, m, lsum);
       } else {
@@ -852,7 +914,7 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     for (int g = 0; g < HPW; ++g) {
       const int head = hg * (BF / (2 * DH)) + wf * HPW + g;
       float s[CB], m, lsum;
-      scores(g * 2 * KB, head, s);
+      scores(g * 2 * KB, a.q + (size_t)r * D + head * DH, s);
       softmax(s, m, lsum);
       values(g * 2 * KB + KB, part_of(head, split), s, m, lsum);
     }
@@ -867,7 +929,7 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
     __syncthreads();
     if (wf == 0 && wave_live) {
       float s[CB], m, lsum;
-      scores(0, head, s);
+      scores(0, a.q + (size_t)r * D + head * DH, s);
       softmax(s, m, lsum);
       if (l < 32)
 #pragma unroll
@@ -886,8 +948,8 @@ __global__ __launch_bounds__((Cfg<T, MODE>::NT), 1) void recon_kernel(KArgs a) {
 
 template <typename T, int MODE, int DH>
 hipError_t launch_mode(const KArgs& k, int grid, hipStream_t s, int epi) {
-  if (epi == EPI_ATTN) recon_kernel<T, MODE, DH, EPI_ATTN><<<grid, Cfg<T, MODE>::NT, 0, s>>>(k);
-  else recon_kernel<T, MODE, DH, EPI_KVSTORE><<<grid, Cfg<T, MODE>::NT, 0, s>>>(k);
+  if (epi == EPI_ATTN) recon_kernel<T, MODE, DH, EPI_ATTN><<<grid, Cfg<T, MODE, DH>::NT, 0, s>>>(k);
+  else recon_kernel<T, MODE, DH, EPI_KVSTORE><<<grid, Cfg<T, MODE, DH>::NT, 0, s>>>(k);
   return hipGetLastError();
 }
 
@@ -917,13 +979,28 @@ bool combined_splits(const ModelView& m, int mode) {
 }
 
 int recon_split_len(const ModelView& m, int mode) {
-  if (combined_splits(m, mode)) return Cfg<half_t, TL_CACHE_H_INT4>::BJ;
-  return m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::WJ : Cfg<half_t, TL_CACHE_H_F16>::WJ;
+  if (combined_splits(m, mode)) return Cfg<half_t, TL_CACHE_H_INT4, 64>::BJ;
+  return m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32, 32>::WJ : Cfg<half_t, TL_CACHE_H_F16, 64>::WJ;
+}
+
+// features (K and V rows) per workgroup and positions per tile of the
+// configuration dispatch() picks
+static int recon_bf(const ModelView& m, int mode) {
+  if (m.dtype == TL_DTYPE_F32) return Cfg<float, TL_CACHE_H_F32, 32>::BF;
+  if (mode == TL_CACHE_H_INT4 && m.dh == 64) return Cfg<half_t, TL_CACHE_H_INT4, 64>::BF;
+  static_assert(Cfg<half_t, TL_CACHE_H_INT4, 128>::BF == 256 && Cfg<half_t, TL_CACHE_H_INT8, 64>::BF == 256 &&
+                    Cfg<half_t, TL_CACHE_H_INT8, 128>::BF == 256 && Cfg<half_t, TL_CACHE_H_F16, 64>::BF == 256 &&
+                    Cfg<half_t, TL_CACHE_H_F16, 128>::BF == 256,
+                "other fp16 configurations");
+  return 256;
+}
+static int recon_bj(const ModelView& m) {
+  return m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32, 32>::BJ : Cfg<half_t, TL_CACHE_H_F16, 64>::BJ;
 }
 
 hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t s) {
-  const int BF = m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::BF : Cfg<half_t, TL_CACHE_H_F16>::BF;
-  const int BJ = m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::BJ : Cfg<half_t, TL_CACHE_H_F16>::BJ;
+  const int BF = recon_bf(m, r.cache.mode);
+  const int BJ = recon_bj(m);
   KArgs k{};
   k.cache = r.cache;
   k.layer = r.layer;
@@ -958,8 +1035,8 @@ hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t
 hipError_t launch_recon_store(const ModelView& m, const CacheView& c, int layer, int lane, int T,
                               const void* w_qkv, void* kvbuf, const int32_t* status,
                               hipStream_t s) {
-  const int BF = m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::BF : Cfg<half_t, TL_CACHE_H_F16>::BF;
-  const int BJ = m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32>::BJ : Cfg<half_t, TL_CACHE_H_F16>::BJ;
+  const int BF = recon_bf(m, c.mode);
+  const int BJ = recon_bj(m);
   KArgs k{};
   k.cache = c;
   k.layer = layer;
