@@ -518,57 +518,62 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
   for (int layer = 0; layer < n_layers; ++layer) {
     while (rows > 0 && mv.n_pre + loops[order[rows - 1]] <= layer) --rows;
     const LayerW& W = layer_w(c, layer);
-    AppendArgs a{};
-    a.src = HS_NORM; a.n = rows; a.layer = layer; a.x = ws.x; a.gain = W.norm1;
-    a.row_lane = ws.row_lane; a.row_pos = ws.row_pos; a.status = ws.status; a.h_out = ws.h;
-    if (layer > mv.n_pre) {
-      // the residual entering this layer is the one after loop iteration
-      // layer - 1 - n_pre: its safety check runs here (rows still active)
-      a.check_iter = layer - 1 - mv.n_pre;
-      a.norms = ws.norms; a.status_w = ws.status; a.l_max = c->l_max;
-      a.check = check ? 1 : 0; a.thr = safety_threshold;
-    }
-    TL_HIP(launch_norm_append(mv, c->cv, a, s));
+    // the attention input projection forms h = RMSNorm1(x) itself and does
+    // the row work before it: the safety check of the residual entering this
+    // layer (the one after loop iteration layer - 1 - n_pre) and the append
+    // of h to the cache
+    auto row_work = [&](GemmArgs& g) {
+      g.norm_gain = W.norm1; g.row_tasks = 1; g.check_iter = -1;
+      g.cache = c->cv; g.layer = layer; g.row_pos = ws.row_pos;
+      g.row_lane = ws.row_lane; g.status = ws.status;
+      if (layer > mv.n_pre) {
+        g.check_iter = layer - 1 - mv.n_pre;
+        g.norms = ws.norms; g.status_w = ws.status; g.l_max = c->l_max;
+        g.check = check ? 1 : 0; g.thr = safety_threshold;
+      }
+    };
     ReconArgs ra{};
     ra.cache = c->cv; ra.layer = layer; ra.w_qkv = W.w_qkv; ra.n_rows = rows; ra.t_ub = t_ub;
     ra.row_lane = ws.row_lane; ra.row_pos = ws.row_pos; ra.status = ws.status; ra.q = ws.q;
     ra.part = ws.part; ra.S = ws.S;
     int split_len;
-    hipEvent_t ev_stop = nullptr;
     if (c->prof_on) {
       while (c->prof_ev.size() < c->prof_used + 2) {
         hipEvent_t e;
         TL_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
         c->prof_ev.push_back(e);
       }
-      TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
-      ev_stop = c->prof_ev[c->prof_used + 1];
-      c->prof_used += 2;
     }
+    // the profiling events bracket the attention kernel alone
     if (c->mode == TL_CACHE_KV) {
-      GemmArgs g = gemm_args(W.w_qkv, D, ws.h, D, rows, 3 * D, D, EPI_QKV, ws.q, D);
-      g.scale = qscale; g.q_is_t = 0; g.cache = c->cv; g.layer = layer;
-      g.row_lane = ws.row_lane; g.status = ws.status; g.row_pos = ws.row_pos;
+      GemmArgs g = gemm_args(W.w_qkv, D, ws.x, D, rows, 3 * D, D, EPI_QKV, ws.q, D);
+      g.scale = qscale; g.q_is_t = 0;
+      row_work(g);
       TL_HIP(launch_gemm(mv, g, s));
-      if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used - 2], s));
+      if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
       TL_HIP(launch_kv_attn(mv, ra, s));
       split_len = kKvSplit;
     } else {
-      GemmArgs g = gemm_args(W.w_qkv, D, ws.h, D, rows, D, D, EPI_STORE_F32, ws.q, D);
-      g.scale = qscale; g.row_lane = ws.row_lane; g.status = ws.status;
+      GemmArgs g = gemm_args(W.w_qkv, D, ws.x, D, rows, D, D, EPI_STORE_F32, ws.q, D);
+      g.scale = qscale;
+      row_work(g);
       TL_HIP(launch_gemm(mv, g, s));
+      if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
       TL_HIP(launch_recon_attn(mv, ra, s));
       split_len = recon_split_len(mv, c->mode);
     }
-    if (ev_stop) TL_HIP(hipEventRecord(ev_stop, s));
+    if (c->prof_on) {
+      TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
+      c->prof_used += 2;
+    }
     TL_HIP(launch_attn_merge(mv, rows, ws.row_lane, ws.row_pos, ws.status, ws.part, ws.S, split_len,
                              ws.o, s));
     GemmArgs go = gemm_args(W.w_o, D, ws.o, D, rows, D, D, EPI_ADD_F32, ws.x, D);
     go.row_lane = ws.row_lane; go.status = ws.status;
     TL_HIP(launch_gemm(mv, go, s));
-    TL_HIP(launch_rmsnorm(mv, rows, ws.x, W.norm2, ws.u, ws.row_lane, ws.status, s));
-    GemmArgs gu = gemm_args(W.w_up, D, ws.u, D, rows, mv.F, D, EPI_GELU_T, ws.a, mv.F);
-    gu.row_lane = ws.row_lane; gu.status = ws.status;
+    // MLP: the up projection forms RMSNorm2(x) itself
+    GemmArgs gu = gemm_args(W.w_up, D, ws.x, D, rows, mv.F, D, EPI_GELU_T, ws.a, mv.F);
+    gu.row_lane = ws.row_lane; gu.status = ws.status; gu.row_pos = ws.row_pos; gu.norm_gain = W.norm2;
     TL_HIP(launch_gemm(mv, gu, s));
     GemmArgs gd = gemm_args(W.w_down, mv.F, ws.a, mv.F, rows, D, mv.F, EPI_ADD_F32, ws.x, D);
     gd.row_lane = ws.row_lane; gd.status = ws.status;

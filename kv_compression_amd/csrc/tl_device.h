@@ -114,6 +114,66 @@ __device__ __forceinline__ half4 int8_dequant4(uint32_t w, half_t s) {
   return r;
 }
 
+// Store elements e0 .. e0+EPT-1 of h (already rounded to the model dtype) of
+// one cache entry (layer, lane, pos) in the cache's h codec. The threads of a
+// row hold consecutive runs of EPT elements, so an INT4 group is 32 / EPT
+// consecutive lanes and an 8-code INT4 word 8 / EPT of them; rowmax(v) returns
+// the maximum of v over all threads of the row (the INT8 per-token scale) and
+// must be called by all of them.
+template <typename T, int EPT, typename RowMax>
+__device__ __forceinline__ void cache_store_h(const CacheView& c, int layer, int lane, int pos,
+                                              int e0, const float (&h)[EPT], RowMax&& rowmax) {
+  const int kb = e0 / kKBlock, w = e0 % kKBlock;
+  char* row = c.code_row(layer, lane, kb, pos);
+  if (c.mode == TL_CACHE_H_F32 || c.mode == TL_CACHE_H_F16) {
+    T* dst = (T*)row + w;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) dst[i] = from_f<T>(h[i]);
+    return;
+  }
+  if (c.mode == TL_CACHE_H_INT8) {
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) am = fmaxf(am, fabsf(h[i]));
+    am = rowmax(am);
+    const half_t s = codec_scale(am, 127.f);
+    const float sf = (float)s;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      ((int8_t*)row)[code_group(w + i) * 8 + ((w + i) & 7)] = (int8_t)codec_code(h[i], sf, -127.f, 127.f);
+    if (e0 == 0) *c.int8_scale(layer, lane, pos) = h_bits(s);
+    return;
+  }
+  // INT4: group of 32 elements = 32 / EPT consecutive threads
+  constexpr int TPG = kInt4Group / EPT;
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) am = fmaxf(am, fabsf(h[i]));
+#pragma unroll
+  for (int o = 1; o < TPG; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+  const half_t s = codec_scale(am, 7.f);
+  const float sf = (float)s;
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int q = codec_code(h[i], sf, -8.f, 7.f);
+    word |= (uint32_t)(q + 8) << int4_shift((e0 + i) & 7);
+  }
+  static_assert(EPT <= 8, "one INT4 word per thread at most");
+  if constexpr (EPT < 8) {
+    constexpr int TPW = 8 / EPT;   // threads sharing one word
+#pragma unroll
+    for (int o = 1; o < TPW; o <<= 1) word |= __shfl_xor(word, o, 64);
+    if ((e0 & 7) == 0) ((uint32_t*)row)[code_group(w)] = word;
+  } else {
+    ((uint32_t*)row)[code_group(w)] = word;
+  }
+  if ((e0 % kInt4Group) == 0) {
+    const int g = e0 / kInt4Group;
+    c.int4_scale(layer, lane, g / 2, pos)[g & 1] = h_bits(s);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) for synthetic inputs
 // ---------------------------------------------------------------------------

@@ -5,12 +5,25 @@
 //
 // Decode runs them with a handful of rows (one per active lane), so the kernel
 // is built for weight streaming: a workgroup owns 16 output features and up to
-// 64 rows; its four waves split the reduction dimension into four contiguous
-// quarters, each issuing 16-byte row loads of W straight into
+// 64 rows; its KS waves split the reduction dimension into KS contiguous
+// parts, each issuing 16-byte row loads of W straight into
 // v_mfma_f32_16x16x32_f16 operands (fp32 models: eight v_mfma_f32_16x16x4_f32
-// per 32-deep step), and the quarters are summed in LDS in a fixed order. The
-// result of an output element therefore never depends on how many rows the
-// call has or where the row sits in it.
+// per 32-deep step), and the parts are summed in LDS in a fixed order. KS is 4,
+// or 16 when there are too few 16-feature groups to give every CU a
+// workgroup (the d_model-wide outputs), so that more weight loads are in
+// flight. KS depends only on the matrix shape, so the result of an output
+// element never depends on how many rows the call has or where the row sits.
+//
+// With XS_NORM the operand rows are RMSNorm(x) * gain of fp32 residual rows
+// (the attention and MLP inputs), formed as x is loaded. The workgroup's waves
+// together load every element of its rows, so each row's sum of squares is
+// reduced from the operand loads themselves in a fixed order (a lane's own
+// elements in k order, then the four lanes of the row, then the waves in
+// order), the same in every workgroup and for any batch. For the
+// attention input the same kernel does the row work that precedes the
+// projection: the safety check of the previous loop iteration on the entering
+// residual (every workgroup evaluates it from its own sums, so all agree on
+// which rows stop) and the append of h to the cache, one row per workgroup.
 #include "tl_device.h"
 
 namespace tl {
@@ -18,6 +31,15 @@ namespace tl {
 namespace {
 
 constexpr int kRowsPerBlock = 64;
+enum { XS_PLAIN = 0, XS_NORM = 1 };
+
+// 32-deep steps per load batch: the weight loads a wave keeps in flight.
+// With fp32 operand rows (XS_NORM) NU, the exact number of steps of a wave's
+// k range, is a template argument and one batch covers it, so the row sums
+// can be taken from the operand loads.
+constexpr int gemm_batch(int KS, int XS, int NU) {
+  return XS == XS_NORM ? NU : (KS >= 16 ? 4 : 8);
+}
 
 template <typename T> struct Frag;
 template <> struct Frag<half_t> {
@@ -68,39 +90,243 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, int D, int row, int 
   }
 }
 
-template <typename T, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(ModelView m, GemmArgs g) {
-  __shared__ float4v red[4][4][64];
+// Row work of the attention input for rows m0 .. m0+nrows-1, row m0+r done by
+// workgroup r (r, r + gridDim.x, ...): the safety check of loop iteration
+// check_iter (norm of the entering residual, written to norms; a failure
+// stops the lane) and, in the h modes, h = RMSNorm(x) * gain appended to the
+// cache at the row's position. Thread t holds elements t*EPT .. t*EPT+EPT-1.
+// The first row's lane status, x and gain elements come prefetched.
+template <typename T, int EPT>
+struct TaskPre {
+  int status;
+  float x[EPT];
+  T gn[EPT];
+};
+template <typename T, int EPT>
+__device__ __forceinline__ void task_load(const ModelView& m, const GemmArgs& g, int row, TaskPre<T, EPT>& p) {
+  const int e0 = threadIdx.x * EPT;
+  const float* xr = (const float*)g.X + (size_t)row * g.ldx;
+  const T* gn = (const T*)g.norm_gain;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    p.x[i] = e0 < m.D ? xr[e0 + i] : 0.f;
+    p.gn[i] = e0 < m.D ? gn[e0 + i] : from_f<T>(0.f);
+  }
+}
+template <typename T, int EPT>
+__device__ void row_tasks_ept(const ModelView& m, const GemmArgs& g, int m0, int nrows,
+                              const float* rss, const float* rinv, const int* rdead, float* rmax,
+                              TaskPre<T, EPT> pre) {
+  const int D = m.D, e0 = threadIdx.x * EPT;
+  const bool holds = e0 < D;
+  for (int rr = blockIdx.x; rr < nrows; rr += gridDim.x) {
+    const int row = m0 + rr;
+    if (rr != (int)blockIdx.x) {
+      pre.status = g.status[g.row_lane[row]];
+      task_load<T, EPT>(m, g, row, pre);
+    }
+    // rows that had stopped before this layer (at an earlier layer of this
+    // step, or before the step) are left alone
+    if (g.row_pos[row] < 0 || pre.status == TL_LANE_ABORTED) continue;
+    const int lane = g.row_lane[row];
+    if (g.check_iter >= 0) {
+      const float nrm = __fsqrt_rn(rss[rr]);
+      if (threadIdx.x == 0) g.norms[(size_t)lane * g.l_max + g.check_iter] = nrm;
+      if (rdead[rr]) {
+        if (threadIdx.x == 0) g.status_w[lane] = TL_LANE_ABORTED;
+        continue;
+      }
+    }
+    if (g.cache.mode == TL_CACHE_KV) continue;   // the K|V rows are the projection's own output
+    float h[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) h[i] = holds ? to_f(from_f<T>(pre.x[i] * rinv[rr] * to_f(pre.gn[i]))) : 0.f;
+    auto rowmax = [&](float v) { return block_max(v, rmax); };
+    if (holds) {
+      cache_store_h<T, EPT>(g.cache, g.layer, lane, g.row_pos[row], e0, h, rowmax);
+    } else if (g.cache.mode == TL_CACHE_H_INT8) {
+      rowmax(0.f);   // threads past the row still join the INT8 scale reduction
+    }
+  }
+}
+
+template <typename T, int EPI, int KS, int XS, int NU>
+__global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) {
+  __shared__ float4v red[KS][4][64];
+  __shared__ float rinv[XS == XS_NORM ? kRowsPerBlock : 1];
+  __shared__ float rss[XS == XS_NORM ? kRowsPerBlock : 1];
+  __shared__ int rdead[XS == XS_NORM ? kRowsPerBlock : 1];
+  __shared__ float rmax[XS == XS_NORM ? 16 : 1];
+  __shared__ float rpart[XS == XS_NORM ? kRowsPerBlock * KS * 4 : 1];
   typedef Frag<T> F;
   const int f0 = blockIdx.x * 16;
   const int m0 = blockIdx.y * kRowsPerBlock;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int kq = g.K >> 2;
+  const int kq = g.K / KS;
   const int kbeg = wave * kq;
   int ng = (g.M - m0 + 15) >> 4;
   ng = ng > 4 ? 4 : ng;
   const T* W = (const T*)g.W + (size_t)(f0 + (l & 15)) * g.ldw + 8 * (l >> 4) + kbeg;
-  const T* X[4];
+  // operand rows of the four row groups (fp32 residual rows for XS_NORM)
+  typedef typename std::conditional<XS == XS_NORM, float, T>::type XT;
+  const XT* X[4];
   bool ok[4];
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
     const int row = m0 + 16 * gi + (l & 15);
     ok[gi] = row < g.M;
-    X[gi] = (const T*)g.X + (size_t)(ok[gi] ? row : 0) * g.ldx + 8 * (l >> 4) + kbeg;
+    X[gi] = (const XT*)g.X + (size_t)(ok[gi] ? row : 0) * g.ldx + 8 * (l >> 4) + kbeg;
   }
+  const T* gain = XS == XS_NORM ? (const T*)g.norm_gain + 8 * (l >> 4) + kbeg : nullptr;
+  // XS_NORM operand parts of row group gi at k (8 consecutive elements of the
+  // row and of the gain), loaded apart from forming them so the loads can be
+  // in flight while the row norms are reduced
+  struct XRaw {
+    float4v x0, x1;
+    typename F::type gv;
+  };
+  auto xraw = [&](int gi, int k) -> XRaw {
+    XRaw r;
+    r.x0 = *(const float4v*)((const float*)X[gi] + k);
+    r.x1 = *(const float4v*)((const float*)X[gi] + k + 4);
+    r.gv = F::load(gain + k);
+    return r;
+  };
+  auto xform = [&](int gi, const XRaw& r) -> typename F::type {
+    const float inv = rinv[16 * gi + (l & 15)];
+    typename F::type v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = from_f<T>(r.x0[e] * inv * to_f(r.gv[e]));
+      v[e + 4] = from_f<T>(r.x1[e] * inv * to_f(r.gv[e + 4]));
+    }
+    return v;
+  };
+  // operand fragment of row group gi at k
+  auto xfrag = [&](int gi, int k) -> typename F::type {
+    if constexpr (XS == XS_NORM) return xform(gi, xraw(gi, k));
+    else return F::load((const T*)X[gi] + k);
+  };
   float4v acc[4] = {};
   // U 32-deep steps per batch: all their loads are issued before the first
   // MFMA, so a wave keeps U weight loads in flight (decode is latency-bound).
-  // The MFMAs still run in k order, so the sums do not depend on U.
-  constexpr int U = 8;
-  for (int k = 0; k < kq; k += 32 * U) {
-    typename F::type a[U];
+  // The MFMAs still run in k order, so the sums do not depend on U. With
+  // XS_NORM one batch covers the wave's whole k range (the row sums need it).
+  constexpr int U = gemm_batch(KS, XS, NU);
+  typename F::type a[U];
+  XRaw xr[XS == XS_NORM ? U : 1];
+  auto load_a = [&](int k) {
+    if constexpr (XS == XS_NORM) {
+      // kq == 32 * U: the whole range in one batch, no guards
 #pragma unroll
-    for (int u = 0; u < U; ++u) a[u] = k + 32 * u < kq ? F::load(W + k + 32 * u) : F::zero();
+      for (int u = 0; u < U; ++u) a[u] = F::load(W + 32 * u);
+      if (ng == 1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) xr[u] = xraw(0, 32 * u);   // rows past M read row 0
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) a[u] = k + 32 * u < kq ? F::load(W + k + 32 * u) : F::zero();
+    }
+  };
+  const int nrows = min(kRowsPerBlock, g.M - m0);
+  const bool task = XS == XS_NORM && g.row_tasks && (int)blockIdx.x < nrows;
+  // row work: thread t holds elements 2t and 2t + 1 (threads past the row idle)
+  TaskPre<T, 2> pre{};
+  int task_lane = 0, rpos_l = 0;
+  if constexpr (XS == XS_NORM) {
+    // position of row l % 16 of the first row group (negative: stopped), and
+    // the row-work inputs, which are only used after the products
+    rpos_l = g.row_pos[m0 + min(l & 15, nrows - 1)];
+    if (task) {
+      task_lane = g.row_lane[m0 + blockIdx.x];
+      task_load<T, 2>(m, g, m0 + blockIdx.x, pre);
+    }
+  }
+  load_a(0);
+  if constexpr (XS == XS_NORM) {
+    // the rows' sums of squares, inverse RMS and dead flags; a row is dead
+    // when its lane stopped before the step (negative position) or fails this
+    // layer's safety check (a lane that stopped at an earlier layer of the
+    // step kept its residual, so it fails again)
+    auto finish_row = [&](int rr, float ss, int rpos) {
+      rss[rr] = ss;
+      rinv[rr] = __fdiv_rn(1.f, __fsqrt_rn(__fdiv_rn(ss, (float)g.K) + m.eps));
+      rdead[rr] = rpos < 0 || (g.row_tasks && g.check_iter >= 0 && g.check && !(__fsqrt_rn(ss) <= g.thr));
+    };
+    if (ng == 1) {
+      // from the operand loads: lane l holds 8 elements of row l % 16 per step
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps += xr[u].x0[e] * xr[u].x0[e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps += xr[u].x1[e] * xr[u].x1[e];
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      if (l < 16) rpart[wave * 16 + l] = ps;
+      __syncthreads();
+      if (wave == 0 && l < nrows) {
+        float ss = 0.f;
+#pragma unroll
+        for (int w = 0; w < KS; ++w) ss += rpart[w * 16 + l];
+        finish_row(l, ss, rpos_l);
+      }
+    } else {
+      // more than 16 rows: the same partial sums (wave w, lane group q) formed
+      // by threads from x, then combined in the same order
+      const int ntask = nrows * KS * 4;
+      for (int t = threadIdx.x; t < ntask; t += blockDim.x) {
+        const int rr = t / (KS * 4), w = (t / 4) % KS, q = t % 4;
+        const float* base = (const float*)g.X + (size_t)(m0 + rr) * g.ldx + w * kq + 8 * q;
+        float p = 0.f;
+        for (int u = 0; 32 * u < kq; ++u)
+          for (int e = 0; e < 8; ++e) {
+            const float v = base[32 * u + e];
+            p += v * v;
+          }
+        rpart[t] = p;
+      }
+      __syncthreads();
+      for (int rr = threadIdx.x; rr < nrows; rr += blockDim.x) {
+        float ss = 0.f;
+        for (int w = 0; w < KS; ++w) {
+          const float* pp = rpart + (rr * KS + w) * 4;
+          ss += (pp[0] + pp[1]) + (pp[2] + pp[3]);
+        }
+        finish_row(rr, ss, g.row_pos[m0 + rr]);
+      }
+    }
+    __syncthreads();
+    if (task) pre.status = g.status[task_lane];
+  }
+  if constexpr (XS == XS_NORM) {
+    // one batch, loaded above (kq == 32 * U)
+    if (ng == 1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const typename F::type b = ok[0] ? xform(0, xr[u]) : F::zero();
+        acc[0] = F::mma(a[u], b, acc[0]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+          if (gi < ng) {
+            const typename F::type b = ok[gi] ? xfrag(gi, 32 * u) : F::zero();
+            acc[gi] = F::mma(a[u], b, acc[gi]);
+          }
+    }
+  } else {
+  for (int k = 0; k < kq; k += 32 * U) {
+    if (k > 0) load_a(k);
     if (ng == 1) {
       typename F::type b[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) b[u] = (ok[0] && k + 32 * u < kq) ? F::load(X[0] + k + 32 * u) : F::zero();
+      for (int u = 0; u < U; ++u) b[u] = (ok[0] && k + 32 * u < kq) ? xfrag(0, k + 32 * u) : F::zero();
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (k + 32 * u < kq) acc[0] = F::mma(a[u], b[u], acc[0]);
@@ -111,43 +337,88 @@ __global__ __launch_bounds__(256) void gemm_kernel(ModelView m, GemmArgs g) {
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
           if (gi < ng) {
-            const typename F::type b = ok[gi] ? F::load(X[gi] + k + 32 * u) : F::zero();
+            const typename F::type b = ok[gi] ? xfrag(gi, k + 32 * u) : F::zero();
             acc[gi] = F::mma(a[u], b, acc[gi]);
           }
         }
       }
     }
   }
+  }
+  if constexpr (XS == XS_NORM) {
+    if (g.row_tasks) row_tasks_ept<T, 2>(m, g, m0, nrows, rss, rinv, rdead, rmax, pre);
+  }
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) red[wave][gi][l] = acc[gi];
   __syncthreads();
   const int gi = threadIdx.x >> 6;
-  if (gi >= ng) return;
+  if (gi >= 4 || gi >= ng) return;
   const int row = m0 + 16 * gi + (l & 15);
   if (row >= g.M) return;
-  if (g.status && g.status[g.row_lane[row]] == TL_LANE_ABORTED) return;
+  if constexpr (XS == XS_NORM) {
+    if (rdead[row - m0]) return;
+  } else {
+    if (g.status && g.status[g.row_lane[row]] == TL_LANE_ABORTED) return;
+  }
   float4v v = red[0][gi][l];
-  v += red[1][gi][l];
-  v += red[2][gi][l];
-  v += red[3][gi][l];
+#pragma unroll
+  for (int w = 1; w < KS; ++w) v += red[w][gi][l];
   const int fb = f0 + 4 * (l >> 4);
 #pragma unroll
   for (int i = 0; i < 4; ++i) epilogue<T, EPI>(g, m.D, row, fb + i, v[i]);
 }
 
-template <typename T>
-hipError_t launch_t(const ModelView& m, const GemmArgs& g, hipStream_t s) {
-  dim3 grid(g.N / 16, (g.M + kRowsPerBlock - 1) / kRowsPerBlock);
+template <typename T, int KS, int NU>
+hipError_t launch_norm(const ModelView& m, const GemmArgs& g, dim3 grid, hipStream_t s) {
   switch (g.epi) {
-    case EPI_STORE_F32: gemm_kernel<T, EPI_STORE_F32><<<grid, 256, 0, s>>>(m, g); break;
-    case EPI_STORE_T: gemm_kernel<T, EPI_STORE_T><<<grid, 256, 0, s>>>(m, g); break;
-    case EPI_ADD_F32: gemm_kernel<T, EPI_ADD_F32><<<grid, 256, 0, s>>>(m, g); break;
-    case EPI_GELU_T: gemm_kernel<T, EPI_GELU_T><<<grid, 256, 0, s>>>(m, g); break;
-    case EPI_LOGITS: gemm_kernel<T, EPI_LOGITS><<<grid, 256, 0, s>>>(m, g); break;
-    case EPI_QKV: gemm_kernel<T, EPI_QKV><<<grid, 256, 0, s>>>(m, g); break;
+    case EPI_GELU_T: gemm_kernel<T, EPI_GELU_T, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_STORE_F32: gemm_kernel<T, EPI_STORE_F32, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_QKV: gemm_kernel<T, EPI_QKV, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T, int KS>
+hipError_t launch_ks(const ModelView& m, const GemmArgs& g, hipStream_t s) {
+  dim3 grid(g.N / 16, (g.M + kRowsPerBlock - 1) / kRowsPerBlock);
+  if (g.norm_gain) {
+    // RMSNorm-input products: the attention input projection (with its row
+    // work) and the MLP up projection
+    // the rows' positions (negative: stopped) are read by every workgroup
+    if (g.K != m.D || m.D % 64 || g.K % (32 * KS) || !g.row_pos) return hipErrorInvalidValue;
+    if (g.row_tasks && (64 * KS * 2 < m.D || !g.row_lane || !g.status ||
+                        (g.check_iter >= 0 && (!g.norms || (g.check && !g.status_w)))))
+      return hipErrorInvalidValue;
+    // steps per wave: 1 (d_model 128), 2 / 4 (d_model 1024 / 2048 over 16
+    // waves), 8 / 16 (over 4 waves)
+    switch (g.K / KS / 32) {
+      case 1: return launch_norm<T, KS, 1>(m, g, grid, s);
+      case 2: return launch_norm<T, KS, 2>(m, g, grid, s);
+      case 4: return launch_norm<T, KS, 4>(m, g, grid, s);
+      case 8: return launch_norm<T, KS, 8>(m, g, grid, s);
+      case 16: return launch_norm<T, KS, 16>(m, g, grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (g.epi) {
+    case EPI_STORE_F32: gemm_kernel<T, EPI_STORE_F32, KS, XS_PLAIN, 0><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_STORE_T: gemm_kernel<T, EPI_STORE_T, KS, XS_PLAIN, 0><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_ADD_F32: gemm_kernel<T, EPI_ADD_F32, KS, XS_PLAIN, 0><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_GELU_T: gemm_kernel<T, EPI_GELU_T, KS, XS_PLAIN, 0><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_LOGITS: gemm_kernel<T, EPI_LOGITS, KS, XS_PLAIN, 0><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_QKV: gemm_kernel<T, EPI_QKV, KS, XS_PLAIN, 0><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+constexpr int kCUs = 256;
+
+template <typename T>
+hipError_t launch_t(const ModelView& m, const GemmArgs& g, hipStream_t s) {
+  if (g.N / 16 < kCUs && g.K % (32 * 16) == 0) return launch_ks<T, 16>(m, g, s);
+  return launch_ks<T, 4>(m, g, s);
 }
 
 }  // namespace

@@ -196,6 +196,18 @@ struct GemmArgs {
   const int32_t* row_pos;
   int fixed_lane, pos0;
   int f_offset;              // EPI_QKV: global feature index = f + f_offset
+  // nullable: X holds fp32 residual rows and the operand is fp16 / fp32
+  // RMSNorm(X) * norm_gain, formed on the fly exactly as rmsnorm_kernel forms it
+  const void* norm_gain;
+  // with norm_gain, the pre-QKV row work of the attention input: the safety
+  // check of loop iteration check_iter (>= 0) on the entering residual, then
+  // (h modes) the append of h to the cache at (layer, row_lane, row_pos)
+  int row_tasks;
+  int check_iter;
+  float* norms;              // [lanes, l_max]
+  int32_t* status_w;
+  int l_max, check;
+  float thr;
 };
 hipError_t launch_gemm(const ModelView& m, const GemmArgs& g, hipStream_t s);
 

@@ -658,13 +658,14 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) vo
     float qpre = 0.f;
     if constexpr (EPI == EPI_ATTN)
       if (tid < HPW_T * DH) qpre = a.q[(size_t)r * D + hg * HPW_T * DH + tid];
-    // stages 0 and 1 and part A of stage 2 are issued back to back and drained
-    // here: entering the loop with no copy in flight lets the compiler see
-    // that each read waits on nothing beyond the explicit per-stage waits
+    // stages 0 and 1 and part A of stage 2 are issued back to back; the loop
+    // starts once stage 0 has landed, with the rest in flight exactly as at
+    // the end of every stage (the counter drains in issue order, so the
+    // queries, issued first, have arrived too)
     issue(std::integral_constant<int, 0>{}, 0);
     issue(std::integral_constant<int, 1>{}, min(1, nst - 1));
     issue_ops(std::integral_constant<int, 2>{}, IA0{}, IA1{}, min(2, nst - 1));   // parts B, C: stage 0
-    dma_sync<0>();
+    dma_sync<DMA_PER_STAGE + PA>();
     if constexpr (EPI == EPI_ATTN)
       if (tid < HPW_T * DH) q_lds[tid] = qpre;   // read after the loop's barriers
     auto loop = [&](auto nb_c) {

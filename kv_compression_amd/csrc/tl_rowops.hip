@@ -100,55 +100,7 @@ __global__ __launch_bounds__(kRowThreads) void norm_append_kernel(ModelView m, C
     for (int i = 0; i < EPT; ++i) ho[e0 + i] = from_f<T>(h[i]);
   }
   if (c.mode == TL_CACHE_KV) return;
-  const int kb = e0 / kKBlock, w = e0 % kKBlock;
-  char* row = c.code_row(a.layer, lane, kb, pos);
-  if (c.mode == TL_CACHE_H_F32 || c.mode == TL_CACHE_H_F16) {
-    T* dst = (T*)row + w;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) dst[i] = from_f<T>(h[i]);
-    return;
-  }
-  if (c.mode == TL_CACHE_H_INT8) {
-    float am = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) am = fmaxf(am, fabsf(h[i]));
-    am = block_max(am, red);
-    const half_t s = codec_scale(am, 127.f);
-    const float sf = (float)s;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i)
-      ((int8_t*)row)[code_group(w + i) * 8 + ((w + i) & 7)] = (int8_t)codec_code(h[i], sf, -127.f, 127.f);
-    if (threadIdx.x == 0) *c.int8_scale(a.layer, lane, pos) = h_bits(s);
-    return;
-  }
-  // INT4: group of 32 elements = 32 / EPT consecutive threads
-  constexpr int TPG = kInt4Group / EPT;
-  float am = 0.f;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) am = fmaxf(am, fabsf(h[i]));
-#pragma unroll
-  for (int o = 1; o < TPG; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-  const half_t s = codec_scale(am, 7.f);
-  const float sf = (float)s;
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int q = codec_code(h[i], sf, -8.f, 7.f);
-    word |= (uint32_t)(q + 8) << int4_shift((e0 + i) & 7);
-  }
-  static_assert(EPT <= 8, "one INT4 word per thread at most");
-  if constexpr (EPT < 8) {
-    constexpr int TPW = 8 / EPT;   // threads sharing one word
-#pragma unroll
-    for (int o = 1; o < TPW; o <<= 1) word |= __shfl_xor(word, o, 64);
-    if ((threadIdx.x % TPW) == 0) ((uint32_t*)row)[code_group(w)] = word;
-  } else {
-    ((uint32_t*)row)[code_group(w)] = word;
-  }
-  if ((e0 % kInt4Group) == 0) {
-    const int g = e0 / kInt4Group;
-    c.int4_scale(a.layer, lane, g / 2, pos)[g & 1] = h_bits(s);
-  }
+  cache_store_h<T, EPT>(c, a.layer, lane, pos, e0, h, [&](float v) { return block_max(v, red); });
 }
 
 template <typename T, int EPT, bool CHECK>
