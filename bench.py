@@ -124,44 +124,17 @@ def cpu_baseline(shape, w, mode, context, loops, budget_s=12.0, max_steps=8):
                       "(%.1f s)" % (steps, context, mode, L, dt)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--mode", default="int4", choices=["int4", "int8", "f16", "kv"])
-    ap.add_argument("--workload", default="407m-int4h-ctx4096-b4")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-profile-pass", action="store_true")
-    ap.add_argument("--calib-copy", action="store_true",
-                    help="end with a 64 MiB device copy (calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py runs on one GPU: the decode step is measured per GPU; "
-              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import synth
-    from kv_compression_amd import tl
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    tl.load()
-    wl = synth.workload(args.workload)
-    shape = wl.shape
+def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile):
+    """Prefill the workload's lanes in `mode`, time K decode steps after W
+    warm-up steps (inputs resident in HBM), then, if `profile`, time the
+    attention kernel alone over another K steps with HIP events on its stream.
+    Returns (tok/s, wall s, roofline, extra, prefill s, cache bytes)."""
     lanes = list(range(wl.lanes))
     loops = wl.lane_loops()
-    K, W = args.steps, args.warmup
     context = wl.context
     max_seq = context + max(K, W) + 1
-    log("weights %s seed %d" % (shape.name, wl.seed_weights))
-    w = synth.make_weights(shape, wl.seed_weights)
-    model = tl.Model(shape, tl.upload_weights(shape, w))
-    cache = tl.Cache(model, args.mode, wl.lanes, max_seq, wl.l_max)
-    prompts = synth.make_prompts(shape.vocab, wl.lanes, context, wl.seed_prompt)
-    log("prefill %d lanes x %d tokens (%s)" % (wl.lanes, context, args.mode))
+    cache = tl.Cache(model, mode, wl.lanes, max_seq, wl.l_max)
+    log("prefill %d lanes x %d tokens (%s)" % (wl.lanes, context, mode))
     torch.cuda.synchronize()
     tp0 = time.perf_counter()
     first = torch.empty(wl.lanes, dtype=torch.int32, device="cuda")
@@ -198,33 +171,32 @@ def main():
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    last = run(K)
+    run(K)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
     st_host = st.cpu().numpy()
     assert np.all(st_host == 0), "a lane aborted during the benchmark"
-    tokens = wl.lanes * K
-    value = tokens / wall
-    log("decode %d steps: %.1f ms wall, %.1f ms events, %.0f tok/s" % (K, wall * 1e3, gpu_ms, value))
+    value = wl.lanes * K / wall
+    log("%s decode %d steps: %.1f ms wall, %.1f ms events, %.0f tok/s" % (mode, K, wall * 1e3, gpu_ms, value))
 
     roof = None
     extra = {}
-    if not args.no_profile_pass:
+    if profile:
         reset()
         torch.cuda.synchronize()
         cache.tl_profile_start()
         run(K)
         kern_ms, launches = cache.tl_profile_stop()
-        import oracle.looped as _ol  # entry-size closed form only (no oracle arithmetic)
-        eb = _ol.entry_bytes(args.mode, shape.d_model) if args.mode != "kv" else 4 * shape.d_model
+        # bytes per (token, layer) entry, from the library's own cache size
+        eb = cache.cache_bytes / ((shape.n_pre + wl.l_max) * wl.lanes * max_seq)
         t_values = [context + 1 + s for s in range(K)]
         flops, hbytes, n_launch = recon_flops_bytes(shape, eb, lanes, loops, t_values)
         assert n_launch == launches, (n_launch, launches)
         avg_ms = kern_ms / launches
-        traffic = load_traffic(wl.name, args.mode)
-        if args.mode == "kv":
+        traffic = load_traffic(wl.name, mode)
+        if mode == "kv":
             achieved = hbytes / (kern_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
@@ -232,13 +204,71 @@ def main():
             achieved = flops / (kern_ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": traffic}
-        extra = {"kernel": "recon_attn" if args.mode != "kv" else "kv_attn",
+        extra = {"kernel": "recon_attn" if mode != "kv" else "kv_attn",
                  "kernel_avg_us": round(avg_ms * 1e3, 2), "kernel_launches": launches,
                  "kernel_share_of_step": round(kern_ms / gpu_ms, 3),
                  "flops_per_launch": flops / launches,
                  "h_bytes_per_launch": hbytes / launches,
                  "h_stream_GBs": round(hbytes / (kern_ms * 1e-3) / 1e9, 1)}
-        log("kernel: %d launches, avg %.1f us, %s" % (launches, avg_ms * 1e3, roof))
+        log("%s kernel: %d launches, avg %.1f us, %s" % (mode, launches, avg_ms * 1e3, roof))
+    kv_bytes = cache.cache_bytes
+    del cache
+    torch.cuda.synchronize()
+    return value, wall, roof, extra, prefill_s, kv_bytes
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--mode", default="int4", choices=["int4", "int8", "f16", "kv"])
+    ap.add_argument("--workload", default="407m-int4h-ctx4096-b4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile-pass", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="measure only --mode (skip the workload's other cache modes)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="end with a 64 MiB device copy (calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: the decode step is measured per GPU; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from kv_compression_amd import tl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tl.load()
+    wl = synth.workload(args.workload)
+    shape = wl.shape
+    loops = wl.lane_loops()
+    K, W = args.steps, args.warmup
+    context = wl.context
+    log("weights %s seed %d" % (shape.name, wl.seed_weights))
+    w = synth.make_weights(shape, wl.seed_weights)
+    model = tl.Model(shape, tl.upload_weights(shape, w))
+    prompts = synth.make_prompts(shape.vocab, wl.lanes, context, wl.seed_prompt)
+
+    value, wall, roof, extra, prefill_s, kv_bytes = measure_mode(
+        torch, tl, model, wl, shape, args.mode, prompts, K, W, not args.no_profile_pass)
+
+    # the other cache modes of the workload (fewer steps), each with its own
+    # attention kernel roofline
+    modes = {}
+    if not args.headline_only:
+        for md in wl.modes:
+            if md == args.mode:
+                continue
+            v2, _, r2, x2, p2, b2 = measure_mode(torch, tl, model, wl, shape, md, prompts,
+                                                 min(K, 32), min(W, 2), True)
+            modes[md] = {"decode_tok_s": round(v2, 2), "prefill_s": round(p2, 3), "kv_bytes": b2,
+                         "attention_kernel": x2.get("kernel"), "kernel_avg_us": x2.get("kernel_avg_us"),
+                         "roofline": r2}
 
     if args.calib_copy:
         src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
@@ -271,10 +301,11 @@ def main():
         "config": {"workload": wl.name, "model_shape": shape.name, "cache_mode": args.mode,
                    "lanes": wl.lanes, "loops": loops[0] if len(set(loops)) == 1 else loops,
                    "context": context, "decode_steps": K,
-                   "kv_bytes": cache.cache_bytes, "prefill_s": round(prefill_s, 3)},
+                   "kv_bytes": kv_bytes, "prefill_s": round(prefill_s, 3)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,
+        "modes": modes,
     }
     print(json.dumps(out), flush=True)
 

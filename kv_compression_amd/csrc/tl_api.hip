@@ -141,7 +141,10 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
   const size_t D = c->d_model, F = c->d_mlp, V = c->vocab, es = dtype_size(c->dtype);
   L.Bmax = std::min(n_lanes, kMaxBatch);
   L.R = std::max(L.Bmax, kMaxChunk);
-  L.S = (max_seq + 63) / 64;   // the shortest split (64 positions)
+  // splits per row: the shortest split is kKvSplit positions (stored K/V),
+  // 64 in the h modes
+  const int min_split = mode == TL_CACHE_KV ? kKvSplit : 64;
+  L.S = (max_seq + min_split - 1) / min_split;
   const size_t sizes[17] = {
       (size_t)n_lanes * 4,                        // len
       (size_t)n_lanes * 4,                        // status

@@ -14,90 +14,108 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T, int EPT> struct Vec;
-template <> struct Vec<half_t, 4> {
-  static __device__ __forceinline__ void load(const half_t* p, float* v) {
-    const half4 x = *(const half4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (float)x[i];
-  }
-};
-template <> struct Vec<half_t, 8> {
-  static __device__ __forceinline__ void load(const half_t* p, float* v) {
-    const half8 x = *(const half8*)p;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
-  }
-};
-template <> struct Vec<float, 1> {
-  static __device__ __forceinline__ void load(const float* p, float* v) { v[0] = *p; }
-};
+// All-reduce (sum) over aligned groups of N lanes (N = 8 or 16) with row-level
+// data-parallel moves: partners l ^ 1, l ^ 2 (quad permutations), l ^ 7
+// (row_half_mirror) and, for 16, l ^ 15 (row_mirror) together reach every lane
+// of the group.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "8 or 16 lanes");
+  x += dpp_mov<0xB1>(x);                         // l ^ 1
+  x += dpp_mov<0x4E>(x);                         // l ^ 2
+  x += dpp_mov<0x141>(x);                        // l ^ 7
+  if constexpr (N == 16) x += dpp_mov<0x140>(x); // l ^ 15
+  return x;
+}
 
-// One block per (row, split of kKvSplit positions); thread t owns d_model
-// elements [t*EPT, t*EPT + EPT) of q, K and V.
-template <typename T, int EPT, int DH>
-__global__ __launch_bounds__(256) void kv_attn_kernel(ModelView m, ReconArgs a, int n_splits) {
-  constexpr int TPH = DH / EPT;   // threads per head
+// Decode attention over stored K|V rows. One workgroup per (row, split of
+// kKvSplit positions). Thread t reads 16 bytes (EPT elements) of a K row and
+// of a V row: TPR = D / EPT threads cover one position, and the workgroup's
+// PPS = NT / TPR position groups take positions j0 + PPS*i + g. Every K and V
+// load of the split is issued before the first score, so the whole split is
+// in flight at once; the scores of a head are summed over its TPH = DH / EPT
+// threads, each thread keeps an online softmax over its STEPS positions, and
+// the position groups are combined in LDS in group order into one
+// (max, sum, o) partial per (row, head, split).
+template <typename T, int D, int DH, int NT>
+__global__ __launch_bounds__(NT) void kv_attn_kernel(ModelView m, ReconArgs a, int n_splits) {
+  constexpr int EPT = 16 / (int)sizeof(T);
+  constexpr int TPR = D / EPT, PPS = NT / TPR, STEPS = kKvSplit / PPS, TPH = DH / EPT;
+  static_assert(NT % TPR == 0 && kKvSplit % PPS == 0 && DH % EPT == 0, "tiling");
+  typedef T vec_t __attribute__((ext_vector_type(EPT)));
+  __shared__ float comb[PPS][TPR][EPT + 2];
   const int r = blockIdx.x / n_splits, split = blockIdx.x % n_splits;
   const int lane = a.row_lane[r];
   if (a.status[lane] == TL_LANE_ABORTED) return;
   const int Tn = a.row_pos[r] + 1;
   const int j0 = split * kKvSplit;
   if (j0 >= Tn) return;
-  const int jn = min(kKvSplit, Tn - j0);
-  const int D = m.D, t = threadIdx.x, e0 = t * EPT, head = e0 / DH;
+  const int t = threadIdx.x, g = t / TPR, c = t % TPR, e0 = c * EPT, head = e0 / DH;
+  const T* kv = (const T*)a.cache.kv_row(a.layer, lane, 0);
+  // all loads of the split first (positions past T read position T-1)
+  vec_t kr[STEPS], vr[STEPS];
+#pragma unroll
+  for (int i = 0; i < STEPS; ++i) {
+    const int j = min(j0 + PPS * i + g, Tn - 1);
+    const T* row = kv + (size_t)j * 2 * D + e0;
+    kr[i] = *(const vec_t*)row;
+    vr[i] = *(const vec_t*)(row + D);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first use
   float q[EPT];
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) q[i] = a.q[(size_t)r * D + e0 + i];
-  const T* kv = (const T*)a.cache.kv_row(a.layer, lane, j0);
-  float mx = -__builtin_inff(), lsum = 0.f, o[EPT];
+  for (int e = 0; e < EPT; ++e) q[e] = a.q[(size_t)r * D + e0 + e];
+  float s[STEPS];
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) o[i] = 0.f;
-  constexpr int U = 16;
-  for (int jj = 0; jj < jn; jj += U) {
-    float sc[U];
+  for (int i = 0; i < STEPS; ++i) {
+    float d = 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float d = 0.f;
-      if (jj + u < jn) {
-        float k[EPT];
-        Vec<T, EPT>::load(kv + (size_t)(jj + u) * 2 * D + e0, k);
+    for (int e = 0; e < EPT; ++e) d = fmaf(q[e], to_f(kr[i][e]), d);
+    if constexpr (TPH == 1) s[i] = d;
+    else s[i] = group_sum<TPH>(d);
+    if (j0 + PPS * i + g >= Tn) s[i] = -__builtin_inff();
+  }
+  float mx = s[0];
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) d = fmaf(q[i], k[i], d);
-      }
-      sc[u] = d;
-    }
+  for (int i = 1; i < STEPS; ++i) mx = fmaxf(mx, s[i]);
+  float lsum = 0.f, o[EPT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+  for (int e = 0; e < EPT; ++e) o[e] = 0.f;
 #pragma unroll
-      for (int off = 1; off < TPH; off <<= 1) sc[u] += __shfl_xor(sc[u], off, 64);
-      if (jj + u >= jn) sc[u] = -__builtin_inff();
-    }
-    float cm = sc[0];
+  for (int i = 0; i < STEPS; ++i) {
+    const float p = s[i] == -__builtin_inff() ? 0.f : exp2f((s[i] - mx) * kLog2e);
+    lsum += p;
 #pragma unroll
-    for (int u = 1; u < U; ++u) cm = fmaxf(cm, sc[u]);
-    const float mn = fmaxf(mx, cm);
-    const float corr = mx == -__builtin_inff() ? 0.f : exp2f((mx - mn) * kLog2e);
-    lsum *= corr;
+    for (int e = 0; e < EPT; ++e) o[e] = fmaf(p, to_f(vr[i][e]), o[e]);
+  }
+  comb[g][c][0] = mx;
+  comb[g][c][1] = lsum;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) o[i] *= corr;
+  for (int e = 0; e < EPT; ++e) comb[g][c][2 + e] = o[e];
+  __syncthreads();
+  if (g != 0) return;
+  float M = comb[0][c][0];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (jj + u < jn) {
-        const float p = exp2f((sc[u] - mn) * kLog2e);
-        lsum += p;
-        float v[EPT];
-        Vec<T, EPT>::load(kv + (size_t)(jj + u) * 2 * D + D + e0, v);
+  for (int k = 1; k < PPS; ++k) M = fmaxf(M, comb[k][c][0]);
+  float L = 0.f, O[EPT];
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) o[i] = fmaf(p, v[i], o[i]);
-      }
-    }
-    mx = mn;
+  for (int e = 0; e < EPT; ++e) O[e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < PPS; ++k) {
+    const float mk = comb[k][c][0];
+    const float w = mk == -__builtin_inff() ? 0.f : exp2f((mk - M) * kLog2e);
+    L = fmaf(comb[k][c][1], w, L);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) O[e] = fmaf(comb[k][c][2 + e], w, O[e]);
   }
   float* dst = a.part + (((size_t)r * m.H + head) * a.S + split) * (DH + 2);
-  if ((t % TPH) == 0) { dst[0] = mx; dst[1] = lsum; }
+  if ((c % TPH) == 0) { dst[0] = M; dst[1] = L; }
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) dst[2 + (e0 % DH) + i] = o[i];
+  for (int e = 0; e < EPT; ++e) dst[2 + (e0 % DH) + e] = O[e];
 }
 
 // One block of 256 threads per (row, head). The split weights exp(m_s - M)
@@ -227,16 +245,17 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(ModelView m, int n, i
 hipError_t launch_kv_attn(const ModelView& m, const ReconArgs& a, hipStream_t s) {
   const int n_splits = (a.t_ub + kKvSplit - 1) / kKvSplit;
   const int grid = n_splits * a.n_rows;
+  if (n_splits > a.S) return hipErrorInvalidValue;
   if (m.dtype == TL_DTYPE_F32 && m.D == 128 && m.dh == 32)
-    kv_attn_kernel<float, 1, 32><<<grid, 128, 0, s>>>(m, a, n_splits);
+    kv_attn_kernel<float, 128, 32, 256><<<grid, 256, 0, s>>>(m, a, n_splits);
   else if (m.dtype == TL_DTYPE_F16 && m.D == 1024 && m.dh == 64)
-    kv_attn_kernel<half_t, 4, 64><<<grid, 256, 0, s>>>(m, a, n_splits);
+    kv_attn_kernel<half_t, 1024, 64, 256><<<grid, 256, 0, s>>>(m, a, n_splits);
   else if (m.dtype == TL_DTYPE_F16 && m.D == 2048 && m.dh == 128)
-    kv_attn_kernel<half_t, 8, 128><<<grid, 256, 0, s>>>(m, a, n_splits);
+    kv_attn_kernel<half_t, 2048, 128, 512><<<grid, 512, 0, s>>>(m, a, n_splits);
   else if (m.dtype == TL_DTYPE_F16 && m.D == 2048 && m.dh == 64)
-    kv_attn_kernel<half_t, 8, 64><<<grid, 256, 0, s>>>(m, a, n_splits);
+    kv_attn_kernel<half_t, 2048, 64, 512><<<grid, 512, 0, s>>>(m, a, n_splits);
   else if (m.dtype == TL_DTYPE_F16 && m.D == 1024 && m.dh == 128)
-    kv_attn_kernel<half_t, 4, 128><<<grid, 256, 0, s>>>(m, a, n_splits);
+    kv_attn_kernel<half_t, 1024, 128, 256><<<grid, 256, 0, s>>>(m, a, n_splits);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

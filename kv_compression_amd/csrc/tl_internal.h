@@ -14,7 +14,7 @@ constexpr int kMaxBatch = 256;        // lanes per decode call
 constexpr int kMaxChunk = 512;        // tokens per prefill call
 constexpr int kKBlock = 64;           // d_model elements per tiled cache block
 constexpr int kInt4Group = 32;        // INT4-h scale group along d_model
-constexpr int kKvSplit = 64;          // positions per split in the stored-K/V attention
+constexpr int kKvSplit = 32;          // positions per split in the stored-K/V attention
 
 typedef _Float16 half_t;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
