@@ -167,77 +167,127 @@ __global__ __launch_bounds__(256) void merge_kernel(int D, int H, const int32_t*
   ((T*)out)[(size_t)r * D + head * DH + dim] = from_f<T>(__fdiv_rn(o, L));
 }
 
-// One block per (head, 64 queries); four threads per query, each owning
-// DH/4 dimensions. K|V rows are staged through LDS 32 keys at a time.
+// Causal attention of a prefill chunk on fp32 MFMA (v_mfma_f32_16x16x4_f32).
+// One workgroup per (head, 64 queries); wave w owns queries 16w .. 16w+15 of
+// the tile and computes, per tile of 32 keys staged in LDS,
+//   S^T = K Q^T   (A: K rows from LDS, B: the wave's queries in registers),
+// so lane l holds S^T[key 16kb + 4*(l/16) + i][query l%16] (kb = 0, 1;
+// i = 0..3): all of a lane's scores belong to one query. The online softmax
+// reduces each query over its 8 values and the 4 lane groups, and
+//   O^T += V^T P^T   (A: V^T from LDS, B: P^T straight from the registers),
+// pairs k-slot j of k-step (kb, i) with key 16kb + 4j + i, which is exactly
+// the key lane group j holds, so P needs no transpose. K and V stay in fp32
+// (the rebuilt K|V buffer; stored-K/V caches are widened on the way in), and
+// the next tile's loads are in flight while the current tile is multiplied.
 template <typename T, typename KT, int DH>
 __global__ __launch_bounds__(256) void prefill_attn_kernel(ModelView m, int n, int pos0,
                                                            const float* q, const KT* kv, T* out,
                                                            int lane, const int32_t* status) {
-  constexpr int QB = 64, KC = 32, DPT = DH / 4;
-  __shared__ float Ks[KC][DH + 1];
-  __shared__ float Vs[KC][DH + 1];
+  constexpr int QB = 64, KC = 32, KS = DH / 4, DB = DH / 16;
+  constexpr int LD = DH + 1;                  // padded LDS rows (floats)
+  constexpr int PER = KC * DH / 256;          // tile elements per thread (K, and V)
+  __shared__ float Ks[KC * LD];
+  __shared__ float Vs[KC * LD];
   if (status && status[lane] == TL_LANE_ABORTED) return;
   const int D = m.D;
   const int head = blockIdx.x % m.H, qb = blockIdx.x / m.H;
-  const int t = threadIdx.x, qi = t >> 2, sub = t & 3;
-  const int i = qb * QB + qi;
-  const bool qv = i < n;
-  const int qpos = pos0 + i;
-  float qr[DPT], o[DPT];
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63, lq = l & 15, lg = l >> 4;
+  const int qi = qb * QB + wave * 16 + lq;    // this lane's query (B operand / output column)
+  const bool qv = qi < n;
+  const int qpos = pos0 + qi;
+  // Q^T as B operand: k-step s holds dim 4s + lg of query lq
+  float qb_op[KS];
 #pragma unroll
-  for (int d = 0; d < DPT; ++d) {
-    qr[d] = qv ? q[(size_t)i * D + head * DH + sub * DPT + d] : 0.f;
-    o[d] = 0.f;
-  }
+  for (int s = 0; s < KS; ++s) qb_op[s] = qv ? q[(size_t)qi * D + head * DH + 4 * s + lg] : 0.f;
+  float4v ot[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) ot[d] = float4v{0.f, 0.f, 0.f, 0.f};
   float mx = -__builtin_inff(), lsum = 0.f;
   const int last_q = min(n, qb * QB + QB) - 1;
-  const int kend = pos0 + last_q + 1;   // keys 0 .. kend-1
+  const int kend = pos0 + last_q + 1;         // keys 0 .. kend-1
+  // tile loads: thread t takes elements e = t + 256 p of the KC x DH tile
+  float kreg[PER], vreg[PER];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = t + 256 * p, kk = e / DH, d = e % DH;
+      const int kp = min(k0 + kk, kend - 1);
+      kreg[p] = to_f(kv[(size_t)kp * 2 * D + head * DH + d]);
+      vreg[p] = to_f(kv[(size_t)kp * 2 * D + D + head * DH + d]);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = t + 256 * p, kk = e / DH, d = e % DH;
+      Ks[kk * LD + d] = kreg[p];
+      Vs[kk * LD + d] = vreg[p];
+    }
+  };
+  load_tile(0);
   for (int k0 = 0; k0 < kend; k0 += KC) {
+    __syncthreads();   // the previous tile is no longer read
+    store_tile();
     __syncthreads();
-    for (int e = t; e < KC * DH; e += 256) {
-      const int kk = e / DH, d = e % DH;
-      const int kp = k0 + kk;
-      float kvk = 0.f, kvv = 0.f;
-      if (kp < kend) {
-        kvk = to_f(kv[(size_t)kp * 2 * D + head * DH + d]);
-        kvv = to_f(kv[(size_t)kp * 2 * D + D + head * DH + d]);
+    if (k0 + KC < kend) load_tile(k0 + KC);   // next tile in flight under this one
+    // S^T for key blocks kb = 0, 1
+    float4v st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      st[kb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float a = Ks[(16 * kb + lq) * LD + 4 * s + lg];
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qb_op[s], st[kb], 0, 0, 0);
       }
-      Ks[kk][d] = kvk;
-      Vs[kk][d] = kvv;
     }
-    __syncthreads();
-    float sc[KC];
+    // mask and online softmax of query lq (keys 16kb + 4lg + i)
+    float cm = -__builtin_inff();
 #pragma unroll
-    for (int u = 0; u < KC; ++u) {
-      float s = 0.f;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int d = 0; d < DPT; ++d) s = fmaf(qr[d], Ks[u][sub * DPT + d], s);
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      sc[u] = (k0 + u <= qpos && k0 + u < kend) ? s : -__builtin_inff();
-    }
-    float cm = sc[0];
-#pragma unroll
-    for (int u = 1; u < KC; ++u) cm = fmaxf(cm, sc[u]);
-    if (cm == -__builtin_inff()) continue;
+      for (int i = 0; i < 4; ++i) {
+        const int kp = k0 + 16 * kb + 4 * lg + i;
+        if (kp > qpos || kp >= kend) st[kb][i] = -__builtin_inff();
+        cm = fmaxf(cm, st[kb][i]);
+      }
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
     const float mn = fmaxf(mx, cm);
     const float corr = mx == -__builtin_inff() ? 0.f : exp2f((mx - mn) * kLog2e);
-    lsum *= corr;
+    float ps = 0.f;
 #pragma unroll
-    for (int d = 0; d < DPT; ++d) o[d] *= corr;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int u = 0; u < KC; ++u) {
-      const float p = sc[u] == -__builtin_inff() ? 0.f : exp2f((sc[u] - mn) * kLog2e);
-      lsum += p;
-#pragma unroll
-      for (int d = 0; d < DPT; ++d) o[d] = fmaf(p, Vs[u][sub * DPT + d], o[d]);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const float p = st[kb][i] == -__builtin_inff() ? 0.f : exp2f((st[kb][i] - mn) * kLog2e);
+        st[kb][i] = p;
+        ps += p;
+      }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lsum = lsum * corr + ps;
     mx = mn;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) ot[d] *= corr;
+    // O^T += V^T P^T: k-step (kb, i), A = V[16kb + 4lg + i][16d + lq]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          const float a = Vs[(16 * kb + 4 * lg + i) * LD + 16 * d + lq];
+          ot[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, st[kb][i], ot[d], 0, 0, 0);
+        }
   }
   if (!qv) return;
+  // lane l holds O^T[dim 16d + 4lg + i][query lq]
 #pragma unroll
-  for (int d = 0; d < DPT; ++d)
-    out[(size_t)i * D + head * DH + sub * DPT + d] = from_f<T>(__fdiv_rn(o[d], lsum));
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[(size_t)qi * D + head * DH + 16 * d + 4 * lg + i] = from_f<T>(__fdiv_rn(ot[d][i], lsum));
 }
 
 }  // namespace
