@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 
 
 def log(msg: str):
@@ -211,6 +212,26 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile):
                  "h_bytes_per_launch": hbytes / launches,
                  "h_stream_GBs": round(hbytes / (kern_ms * 1e-3) / 1e9, 1)}
         log("%s kernel: %d launches, avg %.1f us, %s" % (mode, launches, avg_ms * 1e3, roof))
+    if profile:
+        # the prefill's causal attention kernel over one lane's prompt, timed
+        # alone: algorithmic work sum over positions of (keys seen) * 4 * D
+        # flops per layer on fp32 MFMA
+        cache.tl_cache_reset_lane(0)
+        torch.cuda.synchronize()
+        cache.tl_profile_start()
+        cache.prefill(0, prompts[0], loops[0])
+        pa_ms, pa_launches = cache.tl_profile_stop()
+        n_layers0 = shape.n_pre + loops[0]
+        pa_flops = n_layers0 * 4.0 * shape.d_model * context * (context + 1) / 2.0
+        pa_tf = pa_flops / (pa_ms * 1e-3) / 1e12
+        extra["prefill"] = {
+            "tok_s": round(wl.lanes * context / prefill_s, 1),
+            "attention_kernel_avg_us": round(pa_ms * 1e3 / pa_launches, 2),
+            "attention_launches": pa_launches,
+            "roofline": {"bound": "mfma", "achieved": round(pa_tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(pa_tf / PEAK_FP32_MFMA_TFLOPS, 4)}}
+        log("%s prefill attention: %d launches, avg %.1f us, %.1f TFLOP/s" %
+            (mode, pa_launches, pa_ms * 1e3 / pa_launches, pa_tf))
     kv_bytes = cache.cache_bytes
     del cache
     torch.cuda.synchronize()
@@ -268,7 +289,7 @@ def main():
                                                  min(K, 32), min(W, 2), True)
             modes[md] = {"decode_tok_s": round(v2, 2), "prefill_s": round(p2, 3), "kv_bytes": b2,
                          "attention_kernel": x2.get("kernel"), "kernel_avg_us": x2.get("kernel_avg_us"),
-                         "roofline": r2}
+                         "roofline": r2, "prefill": x2.get("prefill")}
 
     if args.calib_copy:
         src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")

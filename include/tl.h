@@ -208,8 +208,9 @@ tl_status tl_cache_reset_lane(tl_cache* c, int lane, void* stream);
 
 /* Kernel timing for measurement: between tl_profile_start and tl_profile_stop
  * every launch of the decode attention kernel (store-h reconstruction +
- * attention, or the stored-K/V streaming attention) made by tl_decode_step is
- * bracketed with HIP events recorded on the call's stream. tl_profile_stop
+ * attention, or the stored-K/V streaming attention) made by tl_decode_step,
+ * and of the causal attention kernel made by tl_prefill_chunk, is bracketed
+ * with HIP events recorded on the call's stream. tl_profile_stop
  * waits for the last event and returns the summed kernel time in milliseconds
  * and the number of launches. Host-side events only; no device memory. */
 tl_status tl_profile_start(tl_cache* c);

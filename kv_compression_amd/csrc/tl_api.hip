@@ -448,8 +448,21 @@ tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_to
       TL_HIP(launch_recon_store(mv, c->cv, layer, lane, T, W.w_qkv, ws.kvbuf, ws.status, s));
       kv = ws.kvbuf;
     }
+    if (c->prof_on) {
+      // profiling: events around the prefill attention kernel alone
+      while (c->prof_ev.size() < c->prof_used + 2) {
+        hipEvent_t e;
+        TL_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
+        c->prof_ev.push_back(e);
+      }
+      TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
+    }
     TL_HIP(launch_prefill_attn(mv, n, pos0, ws.q, kv, c->mode != TL_CACHE_KV, ws.o, lane,
                                ws.status, s));
+    if (c->prof_on) {
+      TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
+      c->prof_used += 2;
+    }
     GemmArgs go = gemm_args(W.w_o, D, ws.o, D, n, D, D, EPI_ADD_F32, ws.x, D);
     go.row_lane = ws.row_lane; go.status = ws.status;
     TL_HIP(launch_gemm(mv, go, s));
