@@ -145,7 +145,7 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
   // 64 in the h modes
   const int min_split = mode == TL_CACHE_KV ? kKvSplit : 64;
   L.S = (max_seq + min_split - 1) / min_split;
-  const size_t sizes[17] = {
+  const size_t sizes[18] = {
       (size_t)n_lanes * 4,                        // len
       (size_t)n_lanes * 4,                        // status
       (size_t)n_lanes * l_max * 4,                // norms
@@ -161,9 +161,10 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
       (size_t)L.Bmax * V * 4,                     // logits
       (size_t)L.Bmax * c->n_heads * L.S * (c->d_head + 2) * 4,   // part
       mode == TL_CACHE_KV ? 0 : (size_t)max_seq * 2 * D * 4,     // kvbuf (f32)
+      (size_t)L.R * 4,                            // row_dead
   };
   size_t o = 0;
-  for (int i = 0; i < 17; ++i) {
+  for (int i = 0; i < 18; ++i) {
     L.off[i] = o;
     o = align256(o + sizes[i]);
   }
@@ -285,6 +286,7 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   s.logits = (float*)(w + L.off[14]);
   s.part = (float*)(w + L.off[15]);
   s.kvbuf = mode == TL_CACHE_KV ? nullptr : w + L.off[16];
+  s.row_dead = (int32_t*)(w + L.off[17]);
   s.R = L.R; s.Bmax = L.Bmax; s.S = L.S;
   c->host_len.assign(n_lanes, 0);
   c->layers_valid.assign(n_lanes, 0);
@@ -438,12 +440,12 @@ tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_to
     if (c->mode == TL_CACHE_KV) {
       GemmArgs g = gemm_args(W.w_qkv, D, ws.h, D, n, 3 * D, D, EPI_QKV, ws.q, D);
       g.scale = qscale; g.q_is_t = 0; g.cache = c->cv; g.layer = layer;
-      g.row_lane = ws.row_lane; g.status = ws.status; g.row_pos = ws.row_pos;
+      g.row_lane = ws.row_lane; g.status = ws.status; g.row_dead = ws.row_dead; g.row_pos = ws.row_pos;
       TL_HIP(launch_gemm(mv, g, s));
       kv = c->cv.kv_row(layer, lane, 0);
     } else {
       GemmArgs g = gemm_args(W.w_qkv, D, ws.h, D, n, D, D, EPI_STORE_F32, ws.q, D);
-      g.scale = qscale; g.row_lane = ws.row_lane; g.status = ws.status;
+      g.scale = qscale; g.row_lane = ws.row_lane; g.status = ws.status; g.row_dead = ws.row_dead;
       TL_HIP(launch_gemm(mv, g, s));
       TL_HIP(launch_recon_store(mv, c->cv, layer, lane, T, W.w_qkv, ws.kvbuf, ws.status, s));
       kv = ws.kvbuf;
@@ -464,14 +466,14 @@ tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_to
       c->prof_used += 2;
     }
     GemmArgs go = gemm_args(W.w_o, D, ws.o, D, n, D, D, EPI_ADD_F32, ws.x, D);
-    go.row_lane = ws.row_lane; go.status = ws.status;
+    go.row_lane = ws.row_lane; go.status = ws.status; go.row_dead = ws.row_dead;
     TL_HIP(launch_gemm(mv, go, s));
     TL_HIP(launch_rmsnorm(mv, n, ws.x, W.norm2, ws.u, ws.row_lane, ws.status, s));
     GemmArgs gu = gemm_args(W.w_up, D, ws.u, D, n, mv.F, D, EPI_GELU_T, ws.a, mv.F);
-    gu.row_lane = ws.row_lane; gu.status = ws.status;
+    gu.row_lane = ws.row_lane; gu.status = ws.status; gu.row_dead = ws.row_dead;
     TL_HIP(launch_gemm(mv, gu, s));
     GemmArgs gd = gemm_args(W.w_down, mv.F, ws.a, mv.F, n, D, mv.F, EPI_ADD_F32, ws.x, D);
-    gd.row_lane = ws.row_lane; gd.status = ws.status;
+    gd.row_lane = ws.row_lane; gd.status = ws.status; gd.row_dead = ws.row_dead;
     TL_HIP(launch_gemm(mv, gd, s));
   }
   // the last position's token
@@ -479,7 +481,7 @@ tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_to
                         ws.status, s));
   float* lg = d_last_logits ? d_last_logits : ws.logits;
   GemmArgs gh = gemm_args(mv.lm_head, D, ws.z, D, 1, mv.V, D, EPI_STORE_F32, lg, mv.V);
-  gh.row_lane = ws.row_lane; gh.status = ws.status;
+  gh.row_lane = ws.row_lane; gh.status = ws.status; gh.row_dead = ws.row_dead;
   TL_HIP(launch_gemm(mv, gh, s));
   TL_HIP(launch_prefill_finish(mv, ws, lane, T, lg, d_next_token, s));
   (void)es;
@@ -541,7 +543,7 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     auto row_work = [&](GemmArgs& g) {
       g.norm_gain = W.norm1; g.row_tasks = 1; g.check_iter = -1;
       g.cache = c->cv; g.layer = layer; g.row_pos = ws.row_pos;
-      g.row_lane = ws.row_lane; g.status = ws.status;
+      g.row_lane = ws.row_lane; g.status = ws.status; g.row_dead = ws.row_dead;
       if (layer > mv.n_pre) {
         g.check_iter = layer - 1 - mv.n_pre;
         g.norms = ws.norms; g.status_w = ws.status; g.l_max = c->l_max;
@@ -585,14 +587,14 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     TL_HIP(launch_attn_merge(mv, rows, ws.row_lane, ws.row_pos, ws.status, ws.part, ws.S, split_len,
                              ws.o, s));
     GemmArgs go = gemm_args(W.w_o, D, ws.o, D, rows, D, D, EPI_ADD_F32, ws.x, D);
-    go.row_lane = ws.row_lane; go.status = ws.status;
+    go.row_lane = ws.row_lane; go.status = ws.status; go.row_dead = ws.row_dead;
     TL_HIP(launch_gemm(mv, go, s));
     // MLP: the up projection forms RMSNorm2(x) itself
     GemmArgs gu = gemm_args(W.w_up, D, ws.x, D, rows, mv.F, D, EPI_GELU_T, ws.a, mv.F);
-    gu.row_lane = ws.row_lane; gu.status = ws.status; gu.row_pos = ws.row_pos; gu.norm_gain = W.norm2;
+    gu.row_lane = ws.row_lane; gu.status = ws.status; gu.row_dead = ws.row_dead; gu.row_pos = ws.row_pos; gu.norm_gain = W.norm2;
     TL_HIP(launch_gemm(mv, gu, s));
     GemmArgs gd = gemm_args(W.w_down, mv.F, ws.a, mv.F, rows, D, mv.F, EPI_ADD_F32, ws.x, D);
-    gd.row_lane = ws.row_lane; gd.status = ws.status;
+    gd.row_lane = ws.row_lane; gd.status = ws.status; gd.row_dead = ws.row_dead;
     TL_HIP(launch_gemm(mv, gd, s));
   }
   // every row's last loop iteration is checked with the final norm (the
@@ -604,7 +606,7 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
   TL_HIP(launch_rmsnorm(mv, n, ws.x, mv.final_norm, ws.z, ws.row_lane, ws.status, s, &fc));
   float* lg = d_logits ? d_logits : ws.logits;
   GemmArgs gh = gemm_args(mv.lm_head, D, ws.z, D, n, mv.V, D, EPI_LOGITS, lg, mv.V);
-  gh.row_lane = ws.row_lane; gh.status = ws.status; gh.row_slot = d_logits ? ws.row_slot : nullptr;
+  gh.row_lane = ws.row_lane; gh.status = ws.status; gh.row_dead = ws.row_dead; gh.row_slot = d_logits ? ws.row_slot : nullptr;
   TL_HIP(launch_gemm(mv, gh, s));
   TL_HIP(launch_finish(mv, ws, n, lg, mv.V, d_logits ? 1 : 0, d_tokens_out, d_lane_status,
                        d_logits, s));

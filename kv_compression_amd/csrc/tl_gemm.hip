@@ -31,14 +31,17 @@ namespace tl {
 namespace {
 
 constexpr int kRowsPerBlock = 64;
-enum { XS_PLAIN = 0, XS_NORM = 1 };
+// XS_ONE: plain operand rows, at most 16 of them (one row group), a wave's
+// whole k range (NU <= 8 steps) in one batch with the operand rows, and the
+// epilogue's inputs (row_dead, the residual it adds to) loaded up front
+enum { XS_PLAIN = 0, XS_NORM = 1, XS_ONE = 2 };
 
 // 32-deep steps per load batch: the weight loads a wave keeps in flight.
 // With fp32 operand rows (XS_NORM) NU, the exact number of steps of a wave's
 // k range, is a template argument and one batch covers it, so the row sums
 // can be taken from the operand loads.
 constexpr int gemm_batch(int KS, int XS, int NU) {
-  return XS == XS_NORM ? NU : (KS >= 16 ? 4 : 8);
+  return XS != XS_PLAIN ? NU : (KS >= 16 ? 4 : 8);
 }
 
 template <typename T> struct Frag;
@@ -133,7 +136,10 @@ __device__ void row_tasks_ept(const ModelView& m, const GemmArgs& g, int m0, int
       const float nrm = __fsqrt_rn(rss[rr]);
       if (threadIdx.x == 0) g.norms[(size_t)lane * g.l_max + g.check_iter] = nrm;
       if (rdead[rr]) {
-        if (threadIdx.x == 0) g.status_w[lane] = TL_LANE_ABORTED;
+        if (threadIdx.x == 0) {
+          g.status_w[lane] = TL_LANE_ABORTED;
+          if (g.row_dead) g.row_dead[row] = 1;
+        }
         continue;
       }
     }
@@ -166,6 +172,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   const int kbeg = wave * kq;
   int ng = (g.M - m0 + 15) >> 4;
   ng = ng > 4 ? 4 : ng;
+  if constexpr (XS == XS_ONE) ng = 1;   // M <= 16
   const T* W = (const T*)g.W + (size_t)(f0 + (l & 15)) * g.ldw + 8 * (l >> 4) + kbeg;
   // operand rows of the four row groups (fp32 residual rows for XS_NORM)
   typedef typename std::conditional<XS == XS_NORM, float, T>::type XT;
@@ -215,8 +222,14 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   constexpr int U = gemm_batch(KS, XS, NU);
   typename F::type a[U];
   XRaw xr[XS == XS_NORM ? U : 1];
+  typename F::type xb[XS == XS_ONE ? U : 1];
   auto load_a = [&](int k) {
-    if constexpr (XS == XS_NORM) {
+    if constexpr (XS == XS_ONE) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) a[u] = F::load(W + 32 * u);
+#pragma unroll
+      for (int u = 0; u < U; ++u) xb[u] = F::load((const T*)X[0] + 32 * u);   // rows past M read row 0
+    } else if constexpr (XS == XS_NORM) {
       // kq == 32 * U: the whole range in one batch, no guards
 #pragma unroll
       for (int u = 0; u < U; ++u) a[u] = F::load(W + 32 * u);
@@ -244,6 +257,18 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
     }
   }
   load_a(0);
+  // XS_ONE: wave 0 finishes row l % 16; its status and (EPI_ADD_F32) the four
+  // residual values it adds to are fetched before the weights
+  // (row_dead when given: one load, no dependent status lookup)
+  int one_dead = 0;
+  float4v one_x = float4v{0.f, 0.f, 0.f, 0.f};
+  if constexpr (XS == XS_ONE) {
+    if (wave == 0 && ok[0]) {
+      const int row = m0 + (l & 15);
+      if constexpr (EPI == EPI_ADD_F32) one_x = *(const float4v*)((float*)g.out + (size_t)row * g.ldo + f0 + 4 * (l >> 4));
+      one_dead = g.row_dead[row];
+    }
+  }
   if constexpr (XS == XS_NORM) {
     // the rows' sums of squares, inverse RMS and dead flags; a row is dead
     // when its lane stopped before the step (negative position) or fails this
@@ -302,7 +327,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
     __syncthreads();
     if (task) pre.status = g.status[task_lane];
   }
-  if constexpr (XS == XS_NORM) {
+  if constexpr (XS == XS_ONE) {
+    // one batch, loaded above (kq == 32 * U)
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[0] = F::mma(a[u], ok[0] ? xb[u] : F::zero(), acc[0]);
+  } else if constexpr (XS == XS_NORM) {
     // one batch, loaded above (kq == 32 * U)
     if (ng == 1) {
 #pragma unroll
@@ -357,6 +386,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   if (row >= g.M) return;
   if constexpr (XS == XS_NORM) {
     if (rdead[row - m0]) return;
+  } else if constexpr (XS == XS_ONE) {
+    if (one_dead) return;
   } else {
     if (g.status && g.status[g.row_lane[row]] == TL_LANE_ABORTED) return;
   }
@@ -364,6 +395,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
 #pragma unroll
   for (int w = 1; w < KS; ++w) v += red[w][gi][l];
   const int fb = f0 + 4 * (l >> 4);
+  if constexpr (XS == XS_ONE && EPI == EPI_ADD_F32) {
+    *(float4v*)((float*)g.out + (size_t)row * g.ldo + fb) = one_x + v;
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) epilogue<T, EPI>(g, m.D, row, fb + i, v[i]);
 }
@@ -374,6 +409,20 @@ hipError_t launch_norm(const ModelView& m, const GemmArgs& g, dim3 grid, hipStre
     case EPI_GELU_T: gemm_kernel<T, EPI_GELU_T, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     case EPI_STORE_F32: gemm_kernel<T, EPI_STORE_F32, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     case EPI_QKV: gemm_kernel<T, EPI_QKV, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int KS, int NU>
+hipError_t launch_one(const ModelView& m, const GemmArgs& g, dim3 grid, hipStream_t s) {
+  switch (g.epi) {
+    case EPI_STORE_F32: gemm_kernel<T, EPI_STORE_F32, KS, XS_ONE, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_STORE_T: gemm_kernel<T, EPI_STORE_T, KS, XS_ONE, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_ADD_F32: gemm_kernel<T, EPI_ADD_F32, KS, XS_ONE, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_GELU_T: gemm_kernel<T, EPI_GELU_T, KS, XS_ONE, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_LOGITS: gemm_kernel<T, EPI_LOGITS, KS, XS_ONE, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_QKV: gemm_kernel<T, EPI_QKV, KS, XS_ONE, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -399,6 +448,17 @@ hipError_t launch_ks(const ModelView& m, const GemmArgs& g, hipStream_t s) {
       case 8: return launch_norm<T, KS, 8>(m, g, grid, s);
       case 16: return launch_norm<T, KS, 16>(m, g, grid, s);
       default: return hipErrorInvalidValue;
+    }
+  }
+  // at most 16 rows with row_dead flags: the one-batch variant (its steps
+  // per wave, 1..8, as a template argument)
+  const int steps = g.K % (32 * KS) ? 0 : g.K / KS / 32;
+  if (g.M <= 16 && g.row_dead && (steps == 1 || steps == 2 || steps == 4 || steps == 8)) {
+    switch (steps) {
+      case 1: return launch_one<T, KS, 1>(m, g, grid, s);
+      case 2: return launch_one<T, KS, 2>(m, g, grid, s);
+      case 4: return launch_one<T, KS, 4>(m, g, grid, s);
+      default: return launch_one<T, KS, 8>(m, g, grid, s);
     }
   }
   switch (g.epi) {

@@ -77,6 +77,7 @@ struct Workspace {
   int32_t* row_lane;   // [R]   decode: row -> lane id
   int32_t* row_slot;   // [R]   decode: row -> caller slot
   int32_t* row_pos;    // [R]   position the row writes / attends from
+  int32_t* row_dead;   // [R]   1 once the row's lane has stopped (before or during the step)
   float* x;            // [R, D]   residual
   void* h;             // [R, D]   model dtype
   float* q;            // [R, D]   f32 queries (decode) / model dtype (prefill)
@@ -196,6 +197,9 @@ struct GemmArgs {
   const int32_t* row_pos;
   int fixed_lane, pos0;
   int f_offset;              // EPI_QKV: global feature index = f + f_offset
+  // nullable: 1 when the row's lane has stopped (read instead of status by
+  // the products of at most 16 rows; the attention input's safety check sets it)
+  int32_t* row_dead;
   // nullable: X holds fp32 residual rows and the operand is fp16 / fp32
   // RMSNorm(X) * norm_gain, formed on the fly exactly as rmsnorm_kernel forms it
   const void* norm_gain;

@@ -27,6 +27,7 @@ __global__ __launch_bounds__(kRowThreads) void step_setup_kernel(ModelView m, Wo
     ws.row_lane[r] = lane;
     ws.row_slot[r] = slot;
     ws.row_pos[r] = st == TL_LANE_ABORTED ? -1 : ws.len[lane];
+    ws.row_dead[r] = st == TL_LANE_ABORTED ? 1 : 0;
   }
   if (st == TL_LANE_ABORTED) return;
   for (int i = threadIdx.x; i < l_max; i += blockDim.x) ws.norms[(size_t)lane * l_max + i] = __builtin_nanf("");
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(kRowThreads) void prefill_setup_kernel(ModelView m,
   if (threadIdx.x == 0) {
     ws.row_lane[r] = lane;
     ws.row_pos[r] = pos0 + r;
+    ws.row_dead[r] = ws.status[lane] == TL_LANE_ABORTED ? 1 : 0;
   }
   const int tok = min(max(tokens[r], 0), m.V - 1);
   const T* e = (const T*)m.embed + (size_t)tok * m.D;
