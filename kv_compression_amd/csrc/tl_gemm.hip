@@ -4,8 +4,9 @@
 // introduction: the loop block's W_q, W_k, W_v, W_o and MLP matrices).
 //
 // Decode runs them with a handful of rows (one per active lane), so the kernel
-// is built for weight streaming: a workgroup owns 16 output features and up to
-// 64 rows; its KS waves split the reduction dimension into KS contiguous
+// is built for weight streaming: a workgroup owns fb output features (16, or 8
+// or 4 when the output is too narrow to give every CU a workgroup; the MFMA
+// rows past fb load nothing and are not written) and up to 64 rows; its KS waves split the reduction dimension into KS contiguous
 // parts, each issuing 16-byte row loads of W straight into
 // v_mfma_f32_16x16x32_f16 operands (fp32 models: eight v_mfma_f32_16x16x4_f32
 // per 32-deep step), and the parts are summed in LDS in a fixed order. KS is 4,
@@ -165,15 +166,17 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   __shared__ float rmax[XS == XS_NORM ? 16 : 1];
   __shared__ float rpart[XS == XS_NORM ? kRowsPerBlock * KS * 4 : 1];
   typedef Frag<T> F;
-  const int f0 = blockIdx.x * 16;
+  const int fbk = g.fb, f0 = blockIdx.x * fbk;
   const int m0 = blockIdx.y * kRowsPerBlock;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const bool wrow = (l & 15) < fbk;       // this lane's A row is a feature of the block
+  const bool wout = 4 * (l >> 4) < fbk;   // this lane's accumulator rows are features of it
   const int kq = g.K / KS;
   const int kbeg = wave * kq;
   int ng = (g.M - m0 + 15) >> 4;
   ng = ng > 4 ? 4 : ng;
   if constexpr (XS == XS_ONE) ng = 1;   // M <= 16
-  const T* W = (const T*)g.W + (size_t)(f0 + (l & 15)) * g.ldw + 8 * (l >> 4) + kbeg;
+  const T* W = (const T*)g.W + (size_t)(f0 + (wrow ? (l & 15) : 0)) * g.ldw + 8 * (l >> 4) + kbeg;
   // operand rows of the four row groups (fp32 residual rows for XS_NORM)
   typedef typename std::conditional<XS == XS_NORM, float, T>::type XT;
   const XT* X[4];
@@ -226,20 +229,20 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   auto load_a = [&](int k) {
     if constexpr (XS == XS_ONE) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = F::load(W + 32 * u);
+      for (int u = 0; u < U; ++u) a[u] = wrow ? F::load(W + 32 * u) : F::zero();
 #pragma unroll
       for (int u = 0; u < U; ++u) xb[u] = F::load((const T*)X[0] + 32 * u);   // rows past M read row 0
     } else if constexpr (XS == XS_NORM) {
       // kq == 32 * U: the whole range in one batch, no guards
 #pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = F::load(W + 32 * u);
+      for (int u = 0; u < U; ++u) a[u] = wrow ? F::load(W + 32 * u) : F::zero();
       if (ng == 1) {
 #pragma unroll
         for (int u = 0; u < U; ++u) xr[u] = xraw(0, 32 * u);   // rows past M read row 0
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = k + 32 * u < kq ? F::load(W + k + 32 * u) : F::zero();
+      for (int u = 0; u < U; ++u) a[u] = (wrow && k + 32 * u < kq) ? F::load(W + k + 32 * u) : F::zero();
     }
   };
   const int nrows = min(kRowsPerBlock, g.M - m0);
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   int one_dead = 0;
   float4v one_x = float4v{0.f, 0.f, 0.f, 0.f};
   if constexpr (XS == XS_ONE) {
-    if (wave == 0 && ok[0]) {
+    if (wave == 0 && ok[0] && wout) {
       const int row = m0 + (l & 15);
       if constexpr (EPI == EPI_ADD_F32) one_x = *(const float4v*)((float*)g.out + (size_t)row * g.ldo + f0 + 4 * (l >> 4));
       one_dead = g.row_dead[row];
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   for (int gi = 0; gi < 4; ++gi) red[wave][gi][l] = acc[gi];
   __syncthreads();
   const int gi = threadIdx.x >> 6;
-  if (gi >= 4 || gi >= ng) return;
+  if (gi >= 4 || gi >= ng || !wout) return;
   const int row = m0 + 16 * gi + (l & 15);
   if (row >= g.M) return;
   if constexpr (XS == XS_NORM) {
@@ -430,7 +433,7 @@ hipError_t launch_one(const ModelView& m, const GemmArgs& g, dim3 grid, hipStrea
 
 template <typename T, int KS>
 hipError_t launch_ks(const ModelView& m, const GemmArgs& g, hipStream_t s) {
-  dim3 grid(g.N / 16, (g.M + kRowsPerBlock - 1) / kRowsPerBlock);
+  dim3 grid(g.N / g.fb, (g.M + kRowsPerBlock - 1) / kRowsPerBlock);
   if (g.norm_gain) {
     // RMSNorm-input products: the attention input projection (with its row
     // work) and the MLP up projection
@@ -483,8 +486,11 @@ hipError_t launch_t(const ModelView& m, const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm(const ModelView& m, const GemmArgs& g, hipStream_t s) {
-  if (g.N % 16 || g.K % 128 || g.M <= 0) return hipErrorInvalidValue;
+hipError_t launch_gemm(const ModelView& m, const GemmArgs& g0, hipStream_t s) {
+  if (g0.N % 16 || g0.K % 128 || g0.M <= 0) return hipErrorInvalidValue;
+  // features per workgroup: enough workgroups for every CU when possible
+  GemmArgs g = g0;
+  g.fb = g.N / 16 >= kCUs ? 16 : g.N / 8 >= kCUs ? 8 : 4;
   return m.dtype == TL_DTYPE_F32 ? launch_t<float>(m, g, s) : launch_t<half_t>(m, g, s);
 }
 
