@@ -488,9 +488,11 @@ hipError_t launch_t(const ModelView& m, const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_gemm(const ModelView& m, const GemmArgs& g0, hipStream_t s) {
   if (g0.N % 16 || g0.K % 128 || g0.M <= 0) return hipErrorInvalidValue;
-  // features per workgroup: enough workgroups for every CU when possible
+  // features per workgroup: enough workgroups (over all row blocks) for
+  // every CU when possible
   GemmArgs g = g0;
-  g.fb = g.N / 16 >= kCUs ? 16 : g.N / 8 >= kCUs ? 8 : 4;
+  const int by = (g.M + kRowsPerBlock - 1) / kRowsPerBlock;
+  g.fb = (g.N / 16) * by >= kCUs ? 16 : (g.N / 8) * by >= kCUs ? 8 : 4;
   return m.dtype == TL_DTYPE_F32 ? launch_t<float>(m, g, s) : launch_t<half_t>(m, g, s);
 }
 
