@@ -278,6 +278,34 @@ def main():
     value, wall, roof, extra, prefill_s, kv_bytes = measure_mode(
         torch, tl, model, wl, shape, args.mode, prompts, K, W, not args.no_profile_pass)
 
+    # warm start mid-loop on one lane of the workload: prefill at L/2 keeping
+    # the residuals, deepen to L from them, against a fresh prefill at L
+    resume = None
+    if not args.headline_only and max(loops) >= 2:
+        L = max(loops)
+        rc = tl.Cache(model, args.mode, 1, context + 1, wl.l_max)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        rc.prefill(0, prompts[0], L)
+        torch.cuda.synchronize()
+        t_fresh = time.perf_counter() - t0
+        rc.tl_cache_reset_lane(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, _, xs = rc.prefill_x(0, prompts[0], L // 2)
+        torch.cuda.synchronize()
+        t_half = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        rc.extend_depth(0, xs, L // 2, L)
+        torch.cuda.synchronize()
+        t_ext = time.perf_counter() - t0
+        resume = {"lane_tokens": context, "fresh_prefill_L%d_s" % L: round(t_fresh, 4),
+                  "prefill_L%d_s" % (L // 2): round(t_half, 4),
+                  "extend_%d_to_%d_s" % (L // 2, L): round(t_ext, 4),
+                  "extend_vs_fresh": round(t_ext / t_fresh, 3)}
+        log("warm start: fresh L=%d %.3f s, L=%d %.3f s, extend %.3f s" % (L, t_fresh, L // 2, t_half, t_ext))
+        del rc, xs
+
     # the other cache modes of the workload (fewer steps), each with its own
     # attention kernel roofline
     modes = {}
@@ -327,6 +355,7 @@ def main():
         "cpu_baseline": cpu,
         "extra": extra,
         "modes": modes,
+        "warm_start": resume,
     }
     print(json.dumps(out), flush=True)
 

@@ -143,6 +143,36 @@ tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_to
                            int n_tokens, int32_t* d_next_token, float* d_last_logits,
                            void* stream);
 
+/* tl_prefill_chunk that also returns the chunk's residuals after its last
+ * layer: d_x_out (nullable) device f32 [n_tokens, d_model], row i for the
+ * token at position len + i. Those rows are what tl_extend_depth resumes
+ * from. Errors as tl_prefill_chunk, and TL_E_ARG while a depth extension of
+ * the lane is in progress. */
+tl_status tl_prefill_chunk_x(tl_cache* c, int lane, int loops, const int32_t* d_tokens,
+                             int n_tokens, float* d_x_out, int32_t* d_next_token,
+                             float* d_last_logits, void* stream);
+
+/* Warm start mid-loop (features page, "Warm-start mid-loop"): a lane whose
+ * positions were all run at old_loops (its cache holds n_pre + old_loops
+ * layers) is deepened to new_loops without re-running the first old_loops
+ * iterations. Chunk by chunk, in position order starting at 0, positions
+ * pos0 .. pos0+n-1 (n in 1..512) run layers n_pre + old_loops ..
+ * n_pre + new_loops - 1 from their residual after iteration old_loops - 1,
+ * each layer appending h rows and attending causally over the positions
+ * before them (already deepened by the earlier chunks). d_x: device f32
+ * [n, d_model], in: those residuals (tl_prefill_chunk_x's d_x_out for the
+ * same positions), out: the residuals after iteration new_loops - 1, from
+ * which a later extension can resume. d_next_token / d_last_logits
+ * (nullable): the greedy token and logits after position pos0+n-1. The lane's
+ * length does not change; after the chunk that reaches it the lane holds
+ * n_pre + new_loops layers and decodes at up to new_loops. Until then the
+ * lane takes no prefill or decode call.
+ * Errors: TL_E_ARG (lane, loops not 1 <= old < new <= l_max, empty lane, n,
+ * a chunk out of order or of another extension), TL_E_CACHE_GAP (the lane
+ * does not hold exactly n_pre + old_loops layers). */
+tl_status tl_extend_depth(tl_cache* c, int lane, int pos0, int n, int old_loops, int new_loops,
+                          float* d_x, int32_t* d_next_token, float* d_last_logits, void* stream);
+
 /* One greedy decode step for n lanes (1..min(n_lanes, 256)), lane k running
  * loops[k] iterations of the loop block (features page, "L-aware batching";
  * lanes never interact, so a lane's result does not depend on its batch mates).

@@ -42,6 +42,8 @@ struct tl_cache {
   Workspace ws;
   std::vector<int> host_len;       // upper bound of each lane's length
   std::vector<int> layers_valid;   // layers filled for every position < length
+  // depth extension in progress: next position, loops from / to (-1: none)
+  std::vector<int> ext_next, ext_from, ext_to;
   bool prof_on = false;
   std::vector<hipEvent_t> prof_ev; // pool of events, pairs (start, stop)
   size_t prof_used = 0;
@@ -290,6 +292,9 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   s.R = L.R; s.Bmax = L.Bmax; s.S = L.S;
   c->host_len.assign(n_lanes, 0);
   c->layers_valid.assign(n_lanes, 0);
+  c->ext_next.assign(n_lanes, -1);
+  c->ext_from.assign(n_lanes, 0);
+  c->ext_to.assign(n_lanes, 0);
   hipError_t e = launch_lane_reset(s, 0, n_lanes, l_max, 0, (hipStream_t)stream);
   if (e != hipSuccess) {
     delete c;
@@ -307,6 +312,7 @@ tl_status tl_cache_reset_lane(tl_cache* c, int lane, void* stream) {
   TL_HIP(launch_lane_reset(c->ws, lane, 1, c->l_max, 0, (hipStream_t)stream));
   c->host_len[lane] = 0;
   c->layers_valid[lane] = 0;
+  c->ext_next[lane] = -1;
   return TL_OK;
 }
 
@@ -318,6 +324,7 @@ tl_status tl_cache_set_length(tl_cache* c, int lane, int length, int layers_vali
   TL_HIP(launch_lane_reset(c->ws, lane, 1, c->l_max, length, (hipStream_t)stream));
   c->host_len[lane] = length;
   c->layers_valid[lane] = length ? layers_valid : 0;
+  c->ext_next[lane] = -1;
   return TL_OK;
 }
 
@@ -409,28 +416,26 @@ tl_status tl_lane_residual(const tl_cache* c, int lane, float* d_out, void* stre
   return TL_OK;
 }
 
-tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_tokens, int n_tokens,
-                           int32_t* d_next_token, float* d_last_logits, void* stream) {
-  tl_status st = check_lane(c, lane);
-  if (st) return st;
-  if (loops < 1 || loops > c->l_max) return fail(TL_E_ARG, "loops %d not in [1, %d]", loops, c->l_max);
-  if (n_tokens < 1 || n_tokens > kMaxChunk) return fail(TL_E_ARG, "n_tokens %d not in [1, %d]", n_tokens, kMaxChunk);
-  if (!d_tokens) return fail(TL_E_ARG, "null tokens");
-  const int pos0 = c->host_len[lane];
-  if (pos0 + n_tokens > c->max_seq) return fail(TL_E_CAPACITY, "lane %d: %d + %d positions exceed %d", lane, pos0, n_tokens, c->max_seq);
+static // One chunk of positions pos0 .. pos0+n-1 of `lane` through layers
+// layer_begin .. layer_end-1 (every layer appends its h rows before the
+// chunk's causal attention over positions 0 .. pos0+i reads them); then the
+// last position's next token. d_x_in: the residuals entering layer_begin
+// (resume) instead of the token embeddings; d_x_out: the residuals after
+// layer_end-1. Arguments are checked by the callers.
+tl_status run_chunk(tl_cache* c, int lane, int pos0, int n, int layer_begin, int layer_end,
+                    const int32_t* d_tokens, const float* d_x_in, float* d_x_out, int new_len,
+                    int32_t* d_next_token, float* d_last_logits, hipStream_t s) {
   const tl_model* m = c->m;
   const ModelView& mv = m->mv;
-  const int n_layers = mv.n_pre + loops;
-  if (pos0 > 0 && n_layers > c->layers_valid[lane])
-    return fail(TL_E_CACHE_GAP, "lane %d: layers %d.. miss earlier positions", lane, c->layers_valid[lane]);
-
-  hipStream_t s = (hipStream_t)stream;
   const Workspace& ws = c->ws;
-  const int n = n_tokens, T = pos0 + n, D = mv.D;
+  const int T = pos0 + n, D = mv.D;
   const size_t es = dtype_size(mv.dtype);
   const float qscale = (float)(1.0 / sqrt((double)mv.dh));
-  TL_HIP(launch_prefill_setup(mv, ws, lane, n, d_tokens, pos0, s));
-  for (int layer = 0; layer < n_layers; ++layer) {
+  // rows of the chunk: positions pos0 .. pos0+n-1; x from the token
+  // embeddings, or the caller's residuals when resuming mid-loop
+  TL_HIP(launch_prefill_setup(mv, ws, lane, n, d_x_in ? nullptr : d_tokens, pos0, s));
+  if (d_x_in) TL_HIP(launch_copy_f32(d_x_in, ws.x, (size_t)n * D, s));
+  for (int layer = layer_begin; layer < layer_end; ++layer) {
     const LayerW& W = layer_w(c, layer);
     AppendArgs a{};
     a.src = HS_NORM; a.n = n; a.layer = layer; a.x = ws.x; a.gain = W.norm1;
@@ -476,6 +481,7 @@ tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_to
     gd.row_lane = ws.row_lane; gd.status = ws.status; gd.row_dead = ws.row_dead;
     TL_HIP(launch_gemm(mv, gd, s));
   }
+  if (d_x_out) TL_HIP(launch_copy_f32(ws.x, d_x_out, (size_t)n * D, s));
   // the last position's token
   TL_HIP(launch_rmsnorm(mv, 1, ws.x + (size_t)(n - 1) * D, mv.final_norm, ws.z, ws.row_lane,
                         ws.status, s));
@@ -483,10 +489,70 @@ tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_to
   GemmArgs gh = gemm_args(mv.lm_head, D, ws.z, D, 1, mv.V, D, EPI_STORE_F32, lg, mv.V);
   gh.row_lane = ws.row_lane; gh.status = ws.status; gh.row_dead = ws.row_dead;
   TL_HIP(launch_gemm(mv, gh, s));
-  TL_HIP(launch_prefill_finish(mv, ws, lane, T, lg, d_next_token, s));
+  TL_HIP(launch_prefill_finish(mv, ws, lane, new_len, lg, d_next_token, s));
   (void)es;
+  return TL_OK;
+}
+
+tl_status tl_prefill_chunk(tl_cache* c, int lane, int loops, const int32_t* d_tokens, int n_tokens,
+                           int32_t* d_next_token, float* d_last_logits, void* stream) {
+  return tl_prefill_chunk_x(c, lane, loops, d_tokens, n_tokens, nullptr, d_next_token, d_last_logits,
+                            stream);
+}
+
+tl_status tl_prefill_chunk_x(tl_cache* c, int lane, int loops, const int32_t* d_tokens, int n_tokens,
+                             float* d_x_out, int32_t* d_next_token, float* d_last_logits,
+                             void* stream) {
+  tl_status st = check_lane(c, lane);
+  if (st) return st;
+  if (loops < 1 || loops > c->l_max) return fail(TL_E_ARG, "loops %d not in [1, %d]", loops, c->l_max);
+  if (n_tokens < 1 || n_tokens > kMaxChunk) return fail(TL_E_ARG, "n_tokens %d not in [1, %d]", n_tokens, kMaxChunk);
+  if (!d_tokens) return fail(TL_E_ARG, "null tokens");
+  if (c->ext_next[lane] >= 0) return fail(TL_E_ARG, "lane %d: a depth extension is in progress", lane);
+  const int pos0 = c->host_len[lane];
+  if (pos0 + n_tokens > c->max_seq) return fail(TL_E_CAPACITY, "lane %d: %d + %d positions exceed %d", lane, pos0, n_tokens, c->max_seq);
+  const ModelView& mv = c->m->mv;
+  const int n_layers = mv.n_pre + loops;
+  if (pos0 > 0 && n_layers > c->layers_valid[lane])
+    return fail(TL_E_CACHE_GAP, "lane %d: layers %d.. miss earlier positions", lane, c->layers_valid[lane]);
+  const int T = pos0 + n_tokens;
+  st = run_chunk(c, lane, pos0, n_tokens, 0, n_layers, d_tokens, nullptr, d_x_out, T, d_next_token,
+                 d_last_logits, (hipStream_t)stream);
+  if (st) return st;
   c->host_len[lane] = T;
   c->layers_valid[lane] = pos0 == 0 ? n_layers : std::min(c->layers_valid[lane], n_layers);
+  return TL_OK;
+}
+
+tl_status tl_extend_depth(tl_cache* c, int lane, int pos0, int n, int old_loops, int new_loops,
+                          float* d_x, int32_t* d_next_token, float* d_last_logits, void* stream) {
+  tl_status st = check_lane(c, lane);
+  if (st) return st;
+  const ModelView& mv = c->m->mv;
+  if (!(1 <= old_loops && old_loops < new_loops && new_loops <= c->l_max))
+    return fail(TL_E_ARG, "loops %d -> %d not 1 <= old < new <= %d", old_loops, new_loops, c->l_max);
+  if (!d_x) return fail(TL_E_ARG, "null residuals");
+  const int len = c->host_len[lane];
+  if (len < 1) return fail(TL_E_ARG, "lane %d is empty", lane);
+  if (n < 1 || n > kMaxChunk) return fail(TL_E_ARG, "n %d not in [1, %d]", n, kMaxChunk);
+  const int expect = c->ext_next[lane] >= 0 ? c->ext_next[lane] : 0;
+  if (pos0 != expect || pos0 + n > len)
+    return fail(TL_E_ARG, "lane %d: extension chunk at %d (+%d) but %d of %d positions done", lane, pos0, n, expect, len);
+  if (c->ext_next[lane] >= 0 && (c->ext_from[lane] != old_loops || c->ext_to[lane] != new_loops))
+    return fail(TL_E_ARG, "lane %d: extension %d -> %d in progress", lane, c->ext_from[lane], c->ext_to[lane]);
+  if (c->ext_next[lane] < 0 && c->layers_valid[lane] != mv.n_pre + old_loops)
+    return fail(TL_E_CACHE_GAP, "lane %d holds %d layers, not n_pre + %d", lane, c->layers_valid[lane], old_loops);
+  st = run_chunk(c, lane, pos0, n, mv.n_pre + old_loops, mv.n_pre + new_loops, nullptr, d_x, d_x, len,
+                 d_next_token, d_last_logits, (hipStream_t)stream);
+  if (st) return st;
+  if (pos0 + n == len) {
+    c->ext_next[lane] = -1;
+    c->layers_valid[lane] = mv.n_pre + new_loops;
+  } else {
+    c->ext_next[lane] = pos0 + n;
+    c->ext_from[lane] = old_loops;
+    c->ext_to[lane] = new_loops;
+  }
   return TL_OK;
 }
 
@@ -508,6 +574,7 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     if (lane < 0 || lane >= c->n_lanes) return fail(TL_E_ARG, "lane %d out of range", lane);
     if (seen[lane]) return fail(TL_E_ARG, "lane %d appears twice", lane);
     seen[lane] = 1;
+    if (c->ext_next[lane] >= 0) return fail(TL_E_ARG, "lane %d: a depth extension is in progress", lane);
     if (L < 1 || L > c->l_max) return fail(TL_E_ARG, "loops %d not in [1, %d]", L, c->l_max);
     if (c->host_len[lane] + 1 > c->max_seq) return fail(TL_E_CAPACITY, "lane %d is full", lane);
     if (c->host_len[lane] > 0 && mv.n_pre + L > c->layers_valid[lane])

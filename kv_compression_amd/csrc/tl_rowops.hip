@@ -47,6 +47,7 @@ __global__ __launch_bounds__(kRowThreads) void prefill_setup_kernel(ModelView m,
     ws.row_pos[r] = pos0 + r;
     ws.row_dead[r] = ws.status[lane] == TL_LANE_ABORTED ? 1 : 0;
   }
+  if (!tokens) return;   // resuming: the caller's residuals are copied in instead
   const int tok = min(max(tokens[r], 0), m.V - 1);
   const T* e = (const T*)m.embed + (size_t)tok * m.D;
   for (int i = threadIdx.x; i < m.D; i += blockDim.x) ws.x[(size_t)r * m.D + i] = to_f(e[i]);

@@ -54,7 +54,8 @@ EXPORTS = ("tl_version", "tl_last_error", "tl_model_create", "tl_model_destroy",
            "tl_cache_bytes", "tl_workspace_bytes", "tl_cache_alloc", "tl_cache_free",
            "tl_prefill_chunk", "tl_decode_step", "tl_residual_norms", "tl_lane_residual",
            "tl_cache_write_h", "tl_cache_fill_synthetic", "tl_cache_set_length",
-           "tl_cache_read", "tl_cache_reset_lane", "tl_profile_start", "tl_profile_stop")
+           "tl_cache_read", "tl_cache_reset_lane", "tl_profile_start", "tl_profile_stop",
+           "tl_prefill_chunk_x", "tl_extend_depth")
 
 
 def load(path: str = LIB_PATH):
@@ -77,6 +78,8 @@ def load(path: str = LIB_PATH):
         "tl_cache_alloc": (I, [P, I, I, I, I, P, S, P, S, P, ctypes.POINTER(P)]),
         "tl_cache_free": (None, [P]),
         "tl_prefill_chunk": (I, [P, I, I, P, I, P, P, P]),
+        "tl_prefill_chunk_x": (I, [P, I, I, P, I, P, P, P, P]),
+        "tl_extend_depth": (I, [P, I, I, I, I, I, P, P, P, P]),
         "tl_decode_step": (I, [P, I, P, P, P, F, P, P, P, P]),
         "tl_residual_norms": (I, [P, I, P, P]),
         "tl_lane_residual": (I, [P, I, P, P]),
@@ -202,6 +205,16 @@ class Cache:
         _check(_lib.tl_prefill_chunk(self.handle, lane, loops, _ptr(d_tokens), d_tokens.numel(),
                                      _ptr(next_token), _ptr(last_logits), _stream(stream)))
 
+    def tl_prefill_chunk_x(self, lane, loops, d_tokens, x_out=None, next_token=None, last_logits=None,
+                           stream=None):
+        _check(_lib.tl_prefill_chunk_x(self.handle, lane, loops, _ptr(d_tokens), d_tokens.numel(),
+                                       _ptr(x_out), _ptr(next_token), _ptr(last_logits), _stream(stream)))
+
+    def tl_extend_depth(self, lane, pos0, n, old_loops, new_loops, d_x, next_token=None,
+                        last_logits=None, stream=None):
+        _check(_lib.tl_extend_depth(self.handle, lane, pos0, n, old_loops, new_loops, _ptr(d_x),
+                                    _ptr(next_token), _ptr(last_logits), _stream(stream)))
+
     def tl_decode_step(self, lanes: Sequence[int], loops: Sequence[int], d_tokens_in, threshold,
                        d_tokens_out, d_logits, d_lane_status, stream=None):
         n = len(lanes)
@@ -254,4 +267,29 @@ class Cache:
         lg = torch.empty(self.model.shape.vocab, dtype=torch.float32, device="cuda")
         for p in range(0, tok.numel(), chunk):
             self.tl_prefill_chunk(lane, loops, tok[p:p + chunk], nxt, lg)
+        return nxt, lg
+
+    def prefill_x(self, lane: int, tokens, loops: int, chunk: int = MAX_CHUNK):
+        """prefill that also returns every prompt position's residual after its
+        last layer (device f32 [n, d_model]): the state tl_extend_depth resumes from."""
+        import torch
+        tok = torch.as_tensor(np.asarray(tokens, np.int32)).to("cuda")
+        x = torch.empty((tok.numel(), self.model.shape.d_model), dtype=torch.float32, device="cuda")
+        nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+        lg = torch.empty(self.model.shape.vocab, dtype=torch.float32, device="cuda")
+        for p in range(0, tok.numel(), chunk):
+            self.tl_prefill_chunk_x(lane, loops, tok[p:p + chunk], x[p:p + chunk], nxt, lg)
+        return nxt, lg, x
+
+    def extend_depth(self, lane: int, x, old_loops: int, new_loops: int, chunk: int = MAX_CHUNK):
+        """Deepen all of the lane's positions from old_loops to new_loops, chunk by
+        chunk; x (device f32 [length, d_model]) is updated in place to the new
+        residuals. Returns (next_token, last_logits) after the last position."""
+        import torch
+        nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+        lg = torch.empty(self.model.shape.vocab, dtype=torch.float32, device="cuda")
+        n = x.shape[0]
+        for p in range(0, n, chunk):
+            m = min(chunk, n - p)
+            self.tl_extend_depth(lane, p, m, old_loops, new_loops, x[p:p + m], nxt, lg)
         return nxt, lg
