@@ -238,6 +238,57 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile):
     return value, wall, roof, extra, prefill_s, kv_bytes
 
 
+def measure_spec(torch, tl, rc, shape, context, L, t0, draft=2, ahead=4, rounds=8):
+    """Self-speculative decoding on one lane holding `context` positions at L:
+    plain one-lane decoding, the shallow drafts alone, and rounds of
+    tl_spec_step (draft at `draft`, verify at L). With seeded random weights
+    the drafts rarely agree with the verifier, so the measured rate is the
+    rejection-bound one; the break-even figure is the tokens a round must emit
+    to match plain decoding."""
+    n_valid = shape.n_pre + L
+    tin = torch.tensor([t0], dtype=torch.int32, device="cuda")
+    tout = torch.empty(ahead + 1, dtype=torch.int32, device="cuda")
+    st = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def plain(loops, steps):
+        a, b = tin.clone(), torch.empty_like(tin)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            rc.tl_decode_step([0], [loops], a, math.inf, b, None, st)
+            a, b = b, a
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+        rc.tl_cache_set_length(0, context, n_valid)
+        return dt / steps
+
+    plain(L, 2)
+    t_plain = plain(L, 16)
+    t_draft = plain(draft, 16)
+    rc.tl_spec_step(0, draft, L, ahead, tin, tout)       # warm-up round
+    rc.tl_cache_set_length(0, context, n_valid)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    emitted = 0
+    for _ in range(rounds):
+        n = rc.tl_spec_step(0, draft, L, ahead, tin, tout)
+        emitted += n
+        tin.copy_(tout[n - 1:n])
+    t_rounds = (time.perf_counter() - t) / rounds
+    rc.tl_cache_set_length(0, context, n_valid)
+    out = {"lane_context": context, "draft_loops": draft, "verify_loops": L, "draft_ahead": ahead,
+           "plain_decode_ms": round(t_plain * 1e3, 4), "draft_step_ms": round(t_draft * 1e3, 4),
+           "round_ms": round(t_rounds * 1e3, 4),
+           "verify_ms": round((t_rounds - ahead * t_draft) * 1e3, 4),
+           "tokens_per_round": round(emitted / rounds, 3),
+           "tok_s": round(emitted / (rounds * t_rounds), 2),
+           "plain_tok_s": round(1.0 / t_plain, 2),
+           "break_even_tokens_per_round": round(t_rounds / t_plain, 3)}
+    log("speculative: plain %.3f ms/token, draft step %.3f ms, round %.3f ms, %.2f tokens/round"
+        % (t_plain * 1e3, t_draft * 1e3, t_rounds * 1e3, emitted / rounds))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,10 +331,10 @@ def main():
 
     # warm start mid-loop on one lane of the workload: prefill at L/2 keeping
     # the residuals, deepen to L from them, against a fresh prefill at L
-    resume = None
+    resume = spec = None
     if not args.headline_only and max(loops) >= 2:
         L = max(loops)
-        rc = tl.Cache(model, args.mode, 1, context + 1, wl.l_max)
+        rc = tl.Cache(model, args.mode, 1, context + 256, wl.l_max)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         rc.prefill(0, prompts[0], L)
@@ -296,7 +347,7 @@ def main():
         torch.cuda.synchronize()
         t_half = time.perf_counter() - t0
         t0 = time.perf_counter()
-        rc.extend_depth(0, xs, L // 2, L)
+        nxt, _ = rc.extend_depth(0, xs, L // 2, L)
         torch.cuda.synchronize()
         t_ext = time.perf_counter() - t0
         resume = {"lane_tokens": context, "fresh_prefill_L%d_s" % L: round(t_fresh, 4),
@@ -304,7 +355,9 @@ def main():
                   "extend_%d_to_%d_s" % (L // 2, L): round(t_ext, 4),
                   "extend_vs_fresh": round(t_ext / t_fresh, 3)}
         log("warm start: fresh L=%d %.3f s, L=%d %.3f s, extend %.3f s" % (L, t_fresh, L // 2, t_half, t_ext))
-        del rc, xs
+        del xs
+        spec = measure_spec(torch, tl, rc, shape, context, L, int(nxt.cpu()[0]))
+        del rc
 
     # the other cache modes of the workload (fewer steps), each with its own
     # attention kernel roofline
@@ -356,6 +409,7 @@ def main():
         "extra": extra,
         "modes": modes,
         "warm_start": resume,
+        "speculative": spec,
     }
     print(json.dumps(out), flush=True)
 

@@ -194,6 +194,34 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
                          int32_t* d_tokens_out, float* d_logits, int32_t* d_lane_status,
                          void* stream);
 
+/* Self-speculative decoding, chain mode (features page, "Self-speculative
+ * decoding"; the greedy-equality claim is in its "Tree speculative decoding"
+ * section): one round for `lane`, whose cache holds positions 0 .. len-1 at
+ * n_pre + verify_loops layers or more and whose token at position len is
+ * *d_token_in. The same weights draft and verify:
+ *  1. draft: draft_ahead greedy decode steps at draft_loops, each fed the
+ *     previous one's token (d_1 .. d_k, k = draft_ahead);
+ *  2. verify: the input token and d_1 .. d_k run as one chunk at
+ *     verify_loops from position len, giving the verifier's greedy token
+ *     v_j after each of the k + 1 positions;
+ *  3. accept the longest prefix with d_j == v_j (a drafts); the round emits
+ *     v_1 .. v_{a+1} and the lane's length becomes len + a + 1.
+ * The emitted tokens are those plain greedy decoding at verify_loops would
+ * produce; the last one is the token at the new length, the input of the
+ * next round. Cache entries past the new length are left behind and are
+ * overwritten by later calls. The safety check does not run (as in prefill).
+ * d_token_in: device int32 [1]. d_tokens_out: device int32 [draft_ahead + 1],
+ * the emitted tokens, then -1. n_out: host, the number emitted (1 ..
+ * draft_ahead + 1; 0 if the lane was aborted, which leaves it unchanged).
+ * Synchronises `stream` (the host needs the new length to place later
+ * chunks). Residual norms and tl_lane_residual afterwards describe the last
+ * draft step, not the verification.
+ * Errors: TL_E_ARG (lane, draft_ahead not in 1..15, not 1 <= draft_loops <=
+ * verify_loops <= l_max, null pointers, a depth extension in progress),
+ * TL_E_CAPACITY (len + draft_ahead + 1 > max_seq), TL_E_CACHE_GAP. */
+tl_status tl_spec_step(tl_cache* c, int lane, int draft_loops, int verify_loops, int draft_ahead,
+                       const int32_t* d_token_in, int32_t* d_tokens_out, int* n_out, void* stream);
+
 /* Residual norms of `lane`'s last decode step, one per loop iteration
  * (NaN for iterations that did not run). h_out: host float [l_max].
  * Synchronises `stream`. */

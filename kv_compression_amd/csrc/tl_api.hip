@@ -147,7 +147,9 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
   // 64 in the h modes
   const int min_split = mode == TL_CACHE_KV ? kKvSplit : 64;
   L.S = (max_seq + min_split - 1) / min_split;
-  const size_t sizes[18] = {
+  const size_t head_rows = std::max(L.Bmax, kSpecRows);
+  const size_t ppart = (size_t)kMaxChunk * c->n_heads * 8 * (c->d_head + 2);
+  const size_t sizes[20] = {
       (size_t)n_lanes * 4,                        // len
       (size_t)n_lanes * 4,                        // status
       (size_t)n_lanes * l_max * 4,                // norms
@@ -159,14 +161,16 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
       (size_t)L.R * D * es,                       // o
       (size_t)L.R * D * es,                       // u
       (size_t)L.R * F * es,                       // a
-      (size_t)L.Bmax * D * es,                    // z
-      (size_t)L.Bmax * V * 4,                     // logits
+      head_rows * D * es,                         // z
+      head_rows * V * 4,                          // logits
       (size_t)L.Bmax * c->n_heads * L.S * (c->d_head + 2) * 4,   // part
       mode == TL_CACHE_KV ? 0 : (size_t)max_seq * 2 * D * 4,     // kvbuf (f32)
       (size_t)L.R * 4,                            // row_dead
+      (size_t)(2 * kSpecRows + 2) * 4,            // spec
+      ppart * 4,                                  // ppart
   };
   size_t o = 0;
-  for (int i = 0; i < 18; ++i) {
+  for (int i = 0; i < 20; ++i) {
     L.off[i] = o;
     o = align256(o + sizes[i]);
   }
@@ -289,6 +293,9 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   s.part = (float*)(w + L.off[15]);
   s.kvbuf = mode == TL_CACHE_KV ? nullptr : w + L.off[16];
   s.row_dead = (int32_t*)(w + L.off[17]);
+  s.spec = (int32_t*)(w + L.off[18]);
+  s.ppart = (float*)(w + L.off[19]);
+  s.ppart_floats = (int)((size_t)kMaxChunk * cfg->n_heads * 8 * (cfg->d_head + 2));
   s.R = L.R; s.Bmax = L.Bmax; s.S = L.S;
   c->host_len.assign(n_lanes, 0);
   c->layers_valid.assign(n_lanes, 0);
@@ -424,7 +431,8 @@ static // One chunk of positions pos0 .. pos0+n-1 of `lane` through layers
 // layer_end-1. Arguments are checked by the callers.
 tl_status run_chunk(tl_cache* c, int lane, int pos0, int n, int layer_begin, int layer_end,
                     const int32_t* d_tokens, const float* d_x_in, float* d_x_out, int new_len,
-                    int32_t* d_next_token, float* d_last_logits, hipStream_t s) {
+                    int32_t* d_next_token, float* d_last_logits, hipStream_t s,
+                    int32_t* d_spec_out = nullptr) {
   const tl_model* m = c->m;
   const ModelView& mv = m->mv;
   const Workspace& ws = c->ws;
@@ -465,7 +473,7 @@ tl_status run_chunk(tl_cache* c, int lane, int pos0, int n, int layer_begin, int
       TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
     }
     TL_HIP(launch_prefill_attn(mv, n, pos0, ws.q, kv, c->mode != TL_CACHE_KV, ws.o, lane,
-                               ws.status, s));
+                               ws.status, ws.ppart, ws.ppart_floats, ws.row_lane, ws.row_pos, s));
     if (c->prof_on) {
       TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
       c->prof_used += 2;
@@ -482,6 +490,15 @@ tl_status run_chunk(tl_cache* c, int lane, int pos0, int n, int layer_begin, int
     TL_HIP(launch_gemm(mv, gd, s));
   }
   if (d_x_out) TL_HIP(launch_copy_f32(ws.x, d_x_out, (size_t)n * D, s));
+  if (d_spec_out) {
+    // speculative verification: every row's token, then the acceptance
+    TL_HIP(launch_rmsnorm(mv, n, ws.x, mv.final_norm, ws.z, ws.row_lane, ws.status, s));
+    GemmArgs gh = gemm_args(mv.lm_head, D, ws.z, D, n, mv.V, D, EPI_STORE_F32, ws.logits, mv.V);
+    gh.row_lane = ws.row_lane; gh.status = ws.status; gh.row_dead = ws.row_dead;
+    TL_HIP(launch_gemm(mv, gh, s));
+    TL_HIP(launch_spec_accept(mv, ws, lane, pos0, n - 1, ws.logits, d_spec_out, s));
+    return TL_OK;
+  }
   // the last position's token
   TL_HIP(launch_rmsnorm(mv, 1, ws.x + (size_t)(n - 1) * D, mv.final_norm, ws.z, ws.row_lane,
                         ws.status, s));
@@ -683,6 +700,60 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     c->layers_valid[lane] = c->host_len[lane] == 0 ? nl : std::min(c->layers_valid[lane], nl);
     c->host_len[lane] += 1;
   }
+  return TL_OK;
+}
+
+tl_status tl_spec_step(tl_cache* c, int lane, int draft_loops, int verify_loops, int draft_ahead,
+                       const int32_t* d_token_in, int32_t* d_tokens_out, int* n_out, void* stream) {
+  tl_status st = check_lane(c, lane);
+  if (st != TL_OK) return st;
+  if (!d_token_in || !d_tokens_out || !n_out) return fail(TL_E_ARG, "null argument");
+  *n_out = 0;
+  if (c->ext_next[lane] >= 0) return fail(TL_E_ARG, "lane %d: a depth extension is in progress", lane);
+  if (draft_ahead < 1 || draft_ahead > kSpecMax)
+    return fail(TL_E_ARG, "draft_ahead %d not in [1, %d]", draft_ahead, kSpecMax);
+  if (draft_loops < 1 || draft_loops > verify_loops || verify_loops > c->l_max)
+    return fail(TL_E_ARG, "need 1 <= draft_loops (%d) <= verify_loops (%d) <= %d", draft_loops,
+                verify_loops, c->l_max);
+  const ModelView& mv = c->m->mv;
+  const int pos0 = c->host_len[lane], valid = c->layers_valid[lane];
+  const int n = draft_ahead + 1;
+  if (pos0 + n > c->max_seq) return fail(TL_E_CAPACITY, "lane %d: %d + %d positions exceed %d", lane, pos0, n, c->max_seq);
+  if (pos0 > 0 && mv.n_pre + verify_loops > valid)
+    return fail(TL_E_CACHE_GAP, "lane %d: layers %d.. miss earlier positions", lane, valid);
+  hipStream_t s = (hipStream_t)stream;
+  const Workspace& ws = c->ws;
+  int32_t* chunk = ws.spec;   // the round's input token, then the drafts
+  TL_HIP(hipMemcpyAsync(chunk, d_token_in, sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  // drafts: greedy decode steps at the shallow depth, each fed the previous
+  // draft; they append positions pos0 .. pos0+k-1 in the first
+  // n_pre + draft_loops layers, which the verification rewrites identically
+  for (int j = 0; j < draft_ahead; ++j) {
+    st = tl_decode_step(c, 1, &lane, &draft_loops, chunk + j, INFINITY, chunk + j + 1, nullptr,
+                        ws.spec + 2 * kSpecRows + 1, stream);
+    if (st != TL_OK) {
+      c->host_len[lane] = pos0;
+      c->layers_valid[lane] = valid;
+      return st;
+    }
+  }
+  // verification: the input token and the drafts as one chunk at the full
+  // depth from pos0, every row's greedy token, the acceptance and the lane's
+  // new length
+  st = run_chunk(c, lane, pos0, n, 0, mv.n_pre + verify_loops, chunk, nullptr, nullptr, pos0 + n,
+                 nullptr, nullptr, s, d_tokens_out);
+  c->host_len[lane] = pos0;
+  c->layers_valid[lane] = valid;
+  if (st != TL_OK) return st;
+  int32_t got = 0;
+  TL_HIP(hipMemcpyAsync(&got, ws.spec + 2 * kSpecRows, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  TL_HIP(hipStreamSynchronize(s));
+  if (got > 0) {
+    const int nl = mv.n_pre + verify_loops;
+    c->layers_valid[lane] = pos0 == 0 ? nl : std::min(valid, nl);
+    c->host_len[lane] = pos0 + got;
+  }
+  *n_out = got;
   return TL_OK;
 }
 

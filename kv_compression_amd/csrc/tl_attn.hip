@@ -6,6 +6,8 @@
 //    head (split-T / flash-decoding merge) in a fixed order;
 //  * prefill_attn: causal attention of a prefill chunk over K|V rows (chunked
 //    prefill; features page, closing list of supported techniques).
+#include <algorithm>
+
 #include "tl_device.h"
 
 namespace tl {
@@ -179,10 +181,17 @@ __global__ __launch_bounds__(256) void merge_kernel(int D, int H, const int32_t*
 // the key lane group j holds, so P needs no transpose. K and V stay in fp32
 // (the rebuilt K|V buffer; stored-K/V caches are widened on the way in), and
 // the next tile's loads are in flight while the current tile is multiplied.
+// With S > 1 the keys are split into ranges of split_len: workgroup
+// (split, query block, head) covers one range and writes its (max, sum,
+// unnormalised o) per query to part [n][H][S][DH + 2], which the split merge
+// combines; blocks of one head and split sit 16 apart in the grid, on one XCD,
+// so its query blocks share that XCD's L2 copy of the keys.
 template <typename T, typename KT, int DH>
 __global__ __launch_bounds__(256) void prefill_attn_kernel(ModelView m, int n, int pos0,
                                                            const float* q, const KT* kv, T* out,
-                                                           int lane, const int32_t* status) {
+                                                           int lane, const int32_t* status,
+                                                           float* part, int S, int split_len,
+                                                           int n_qb) {
   constexpr int QB = 64, KC = 32, KS = DH / 4, DB = DH / 16;
   constexpr int LD = DH + 1;                  // padded LDS rows (floats)
   constexpr int PER = KC * DH / 256;          // tile elements per thread (K, and V)
@@ -190,7 +199,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(ModelView m, int n, i
   __shared__ float Vs[KC * LD];
   if (status && status[lane] == TL_LANE_ABORTED) return;
   const int D = m.D;
-  const int head = blockIdx.x % m.H, qb = blockIdx.x / m.H;
+  const int head = blockIdx.x % m.H, qb = (blockIdx.x / m.H) % n_qb, split = blockIdx.x / (m.H * n_qb);
   const int t = threadIdx.x, wave = t >> 6, l = t & 63, lq = l & 15, lg = l >> 4;
   const int qi = qb * QB + wave * 16 + lq;    // this lane's query (B operand / output column)
   const bool qv = qi < n;
@@ -204,7 +213,9 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(ModelView m, int n, i
   for (int d = 0; d < DB; ++d) ot[d] = float4v{0.f, 0.f, 0.f, 0.f};
   float mx = -__builtin_inff(), lsum = 0.f;
   const int last_q = min(n, qb * QB + QB) - 1;
-  const int kend = pos0 + last_q + 1;         // keys 0 .. kend-1
+  const int k_lo = split * split_len;
+  const int kend = min(pos0 + last_q + 1, k_lo + split_len);   // keys k_lo .. kend-1
+  if (k_lo >= kend) return;
   // tile loads: thread t takes elements e = t + 256 p of the KC x DH tile
   float kreg[PER], vreg[PER];
   auto load_tile = [&](int k0) {
@@ -224,8 +235,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(ModelView m, int n, i
       Vs[kk * LD + d] = vreg[p];
     }
   };
-  load_tile(0);
-  for (int k0 = 0; k0 < kend; k0 += KC) {
+  load_tile(k_lo);
+  for (int k0 = k_lo; k0 < kend; k0 += KC) {
     __syncthreads();   // the previous tile is no longer read
     store_tile();
     __syncthreads();
@@ -283,6 +294,18 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(ModelView m, int n, i
   }
   if (!qv) return;
   // lane l holds O^T[dim 16d + 4lg + i][query lq]
+  if (part) {
+    float* pp = part + (((size_t)qi * m.H + head) * S + split) * (DH + 2);
+    if (lg == 0) {
+      pp[0] = mx;
+      pp[1] = lsum;
+    }
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[2 + 16 * d + 4 * lg + i] = ot[d][i];
+    return;
+  }
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -326,13 +349,32 @@ hipError_t launch_attn_merge(const ModelView& m, int n_rows, const int32_t* row_
   return hipGetLastError();
 }
 
+int prefill_splits(const ModelView& m, int n, int pos0, int part_floats, int* split_len) {
+  constexpr int KC = 32;
+  const int n_qb = (n + 63) / 64;
+  const int tiles = (pos0 + n + KC - 1) / KC;            // key tiles of the last query block
+  // about four workgroups per CU, at least four key tiles per split, and the
+  // partials within their buffer
+  int S = (1024 + m.H * n_qb - 1) / (m.H * n_qb);
+  S = std::min(S, std::max(1, tiles / 4));
+  S = std::min(S, std::max(1, part_floats / (n * m.H * (m.dh + 2))));
+  *split_len = (tiles + S - 1) / S * KC;
+  return (pos0 + n + *split_len - 1) / *split_len;
+}
+
 hipError_t launch_prefill_attn(const ModelView& m, int n, int pos0, const float* q,
                                const void* kv, int kv_f32, void* o, int lane,
-                               const int32_t* status, hipStream_t s) {
-  const int grid = m.H * ((n + 63) / 64);
+                               const int32_t* status, float* part, int part_floats,
+                               const int32_t* row_lane, const int32_t* row_pos, hipStream_t s) {
+  const int n_qb = (n + 63) / 64;
+  int split_len = 0;
+  const int S = part ? prefill_splits(m, n, pos0, part_floats, &split_len) : 1;
+  if (S == 1) split_len = pos0 + n;
+  float* pp = S > 1 ? part : nullptr;
+  const int grid = m.H * n_qb * S;
 #define TL_PA(T_, KT_, DH_)                                                                  \
   prefill_attn_kernel<T_, KT_, DH_><<<grid, 256, 0, s>>>(m, n, pos0, q, (const KT_*)kv, (T_*)o, \
-                                                          lane, status)
+                                                          lane, status, pp, S, split_len, n_qb)
   if (m.dtype == TL_DTYPE_F32 && m.dh == 32) TL_PA(float, float, 32);
   else if (m.dtype == TL_DTYPE_F16 && m.dh == 64 && kv_f32) TL_PA(half_t, float, 64);
   else if (m.dtype == TL_DTYPE_F16 && m.dh == 64) TL_PA(half_t, half_t, 64);
@@ -340,7 +382,9 @@ hipError_t launch_prefill_attn(const ModelView& m, int n, int pos0, const float*
   else if (m.dtype == TL_DTYPE_F16 && m.dh == 128) TL_PA(half_t, half_t, 128);
   else return hipErrorInvalidValue;
 #undef TL_PA
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  return launch_attn_merge(m, n, row_lane, row_pos, status, part, S, split_len, o, s);
 }
 
 }  // namespace tl

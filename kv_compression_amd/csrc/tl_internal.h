@@ -15,6 +15,8 @@ constexpr int kMaxChunk = 512;        // tokens per prefill call
 constexpr int kKBlock = 64;           // d_model elements per tiled cache block
 constexpr int kInt4Group = 32;        // INT4-h scale group along d_model
 constexpr int kKvSplit = 32;          // positions per split in the stored-K/V attention
+constexpr int kSpecMax = 15;          // drafted tokens per speculative round
+constexpr int kSpecRows = 16;         // verification rows of a round (kSpecMax + 1)
 
 typedef _Float16 half_t;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -84,10 +86,15 @@ struct Workspace {
   void* o;             // [R, D]   model dtype
   void* u;             // [R, D]
   void* a;             // [R, F]
-  void* z;             // [Bmax, D]
-  float* logits;       // [Bmax, V]
+  void* z;             // [max(Bmax, kSpecRows), D]
+  float* logits;       // [max(Bmax, kSpecRows), V]
   float* part;         // [Bmax, H, S, d + 2]
   void* kvbuf;         // [max_seq, 2D] f32 (prefill K/V rebuilt from h)
+  float* ppart;        // [kMaxChunk * H * 8 * (d + 2)] prefill key-split partials
+  int ppart_floats;
+  int32_t* spec;       // speculative round: [0, kSpecRows) input token then drafts,
+                       // [kSpecRows, 2 kSpecRows) verified tokens, [2 kSpecRows] count,
+                       // [2 kSpecRows + 1] draft lane status
   int R, Bmax, S;      // rows, decode rows, splits per (row, head)
 };
 
@@ -251,9 +258,13 @@ hipError_t launch_attn_merge(const ModelView& m, int n_rows, const int32_t* row_
 // Causal prefill attention: query i (position pos0+i) over K|V rows 0..pos0+i.
 // q: [n, D] f32 (scaled); o: [n, D] model dtype; kv: rows of 2D elements
 // (K | V), f32 when kv_f32 (rebuilt from h) else the model dtype (stored K/V).
+// part (part_floats floats) takes the key-split partials; the split count
+// adapts to the chunk (one split writes o directly). row_lane / row_pos: the
+// chunk's rows, for the merge.
 hipError_t launch_prefill_attn(const ModelView& m, int n, int pos0, const float* q,
                                const void* kv, int kv_f32, void* o, int lane,
-                               const int32_t* status, hipStream_t s);
+                               const int32_t* status, float* part, int part_floats,
+                               const int32_t* row_lane, const int32_t* row_pos, hipStream_t s);
 
 // Per decode row: argmax of logits (lowest index on ties) -> tokens_out[slot],
 // lane_status[slot]; len[lane] += 1 unless aborted; xres[lane] = x[row].
@@ -263,6 +274,14 @@ hipError_t launch_finish(const ModelView& m, const Workspace& ws, int n, const f
 // Prefill: argmax of the last row's logits -> next_token; len[lane] = new_len.
 hipError_t launch_prefill_finish(const ModelView& m, const Workspace& ws, int lane, int new_len,
                                  const float* logits, int32_t* next_token, hipStream_t s);
+
+// Speculative round over the k + 1 verification rows (drafts d_1..d_k at
+// spec[1..k]): every row's argmax -> spec[kSpecRows + j]; the leading drafts
+// equal to the verified tokens are accepted; tokens_out[0..n) = the verified
+// tokens through the first mismatch (n = accepted + 1, or 0 for an aborted
+// lane), -1 after; spec[2 kSpecRows] = n; len[lane] = pos0 + n.
+hipError_t launch_spec_accept(const ModelView& m, const Workspace& ws, int lane, int pos0, int k,
+                              const float* logits, int32_t* tokens_out, hipStream_t s);
 
 // Fill lane state: len, status for lanes [l0, l0+n) and norms to NaN.
 hipError_t launch_lane_reset(const Workspace& ws, int l0, int n, int l_max, int length,

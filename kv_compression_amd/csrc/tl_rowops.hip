@@ -226,6 +226,32 @@ __global__ __launch_bounds__(kRowThreads) void prefill_finish_kernel(ModelView m
   }
 }
 
+// One block per verification row: the verifier's greedy token after it.
+__global__ __launch_bounds__(kRowThreads) void spec_argmax_kernel(ModelView m, Workspace ws,
+                                                                  int lane, const float* logits) {
+  if (ws.status[lane] == TL_LANE_ABORTED) return;
+  const int r = blockIdx.x;
+  const int tok = block_argmax(logits + (size_t)r * m.V, m.V);
+  if (threadIdx.x == 0) ws.spec[kSpecRows + r] = tok;
+}
+
+__global__ void spec_accept_kernel(Workspace ws, int lane, int pos0, int k, int32_t* tokens_out) {
+  const int32_t* drafted = ws.spec;               // [0] the round's input token, [1..k] drafts
+  const int32_t* verified = ws.spec + kSpecRows;  // [j]: the verifier's token after row j
+  int n = 0;
+  if (ws.status[lane] != TL_LANE_ABORTED) {
+    int acc = 0;
+    while (acc < k && drafted[acc + 1] == verified[acc]) ++acc;
+    n = acc + 1;
+  }
+  const int j = threadIdx.x;
+  if (j <= k) tokens_out[j] = j < n ? verified[j] : -1;
+  if (j == 0) {
+    ws.spec[2 * kSpecRows] = n;
+    if (n) ws.len[lane] = pos0 + n;
+  }
+}
+
 __global__ void lane_reset_kernel(Workspace ws, int l0, int n, int l_max, int length) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -350,6 +376,16 @@ hipError_t launch_finish(const ModelView& m, const Workspace& ws, int n, const f
 hipError_t launch_prefill_finish(const ModelView& m, const Workspace& ws, int lane, int new_len,
                                  const float* logits, int32_t* next_token, hipStream_t s) {
   prefill_finish_kernel<<<1, kRowThreads, 0, s>>>(m, ws, lane, new_len, logits, next_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_spec_accept(const ModelView& m, const Workspace& ws, int lane, int pos0, int k,
+                              const float* logits, int32_t* tokens_out, hipStream_t s) {
+  if (k < 1 || k > kSpecMax) return hipErrorInvalidValue;
+  spec_argmax_kernel<<<k + 1, kRowThreads, 0, s>>>(m, ws, lane, logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  spec_accept_kernel<<<1, 64, 0, s>>>(ws, lane, pos0, k, tokens_out);
   return hipGetLastError();
 }
 

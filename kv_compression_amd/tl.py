@@ -55,7 +55,7 @@ EXPORTS = ("tl_version", "tl_last_error", "tl_model_create", "tl_model_destroy",
            "tl_prefill_chunk", "tl_decode_step", "tl_residual_norms", "tl_lane_residual",
            "tl_cache_write_h", "tl_cache_fill_synthetic", "tl_cache_set_length",
            "tl_cache_read", "tl_cache_reset_lane", "tl_profile_start", "tl_profile_stop",
-           "tl_prefill_chunk_x", "tl_extend_depth")
+           "tl_prefill_chunk_x", "tl_extend_depth", "tl_spec_step")
 
 
 def load(path: str = LIB_PATH):
@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH):
         "tl_prefill_chunk_x": (I, [P, I, I, P, I, P, P, P, P]),
         "tl_extend_depth": (I, [P, I, I, I, I, I, P, P, P, P]),
         "tl_decode_step": (I, [P, I, P, P, P, F, P, P, P, P]),
+        "tl_spec_step": (I, [P, I, I, I, I, P, P, ctypes.POINTER(I), P]),
         "tl_residual_norms": (I, [P, I, P, P]),
         "tl_lane_residual": (I, [P, I, P, P]),
         "tl_cache_write_h": (I, [P, I, I, I, I, P, P]),
@@ -224,6 +225,13 @@ class Cache:
                                    _ptr(d_tokens_out), _ptr(d_logits), _ptr(d_lane_status),
                                    _stream(stream)))
 
+    def tl_spec_step(self, lane, draft_loops, verify_loops, draft_ahead, d_token_in, d_tokens_out,
+                     stream=None) -> int:
+        n = ctypes.c_int()
+        _check(_lib.tl_spec_step(self.handle, lane, draft_loops, verify_loops, draft_ahead,
+                                 _ptr(d_token_in), _ptr(d_tokens_out), ctypes.byref(n), _stream(stream)))
+        return n.value
+
     def tl_residual_norms(self, lane, stream=None) -> np.ndarray:
         out = np.empty(self.l_max, np.float32)
         _check(_lib.tl_residual_norms(self.handle, lane, out.ctypes.data, _stream(stream)))
@@ -293,3 +301,22 @@ class Cache:
             m = min(chunk, n - p)
             self.tl_extend_depth(lane, p, m, old_loops, new_loops, x[p:p + m], nxt, lg)
         return nxt, lg
+
+    def generate_speculative(self, lane: int, token: int, max_tokens: int, draft_loops: int,
+                             verify_loops: int, draft_ahead: int):
+        """Greedy tokens after ``token`` (the token at the lane's current length)
+        by rounds of tl_spec_step until at least ``max_tokens`` are emitted.
+        Returns (tokens, emitted per round) as host lists; the last token is at
+        the lane's new length."""
+        import torch
+        tin = torch.tensor([token], dtype=torch.int32, device="cuda")
+        tout = torch.empty(draft_ahead + 1, dtype=torch.int32, device="cuda")
+        out, rounds = [], []
+        while len(out) < max_tokens:
+            n = self.tl_spec_step(lane, draft_loops, verify_loops, draft_ahead, tin, tout)
+            rounds.append(n)
+            if n == 0:
+                break
+            out.extend(int(t) for t in tout[:n].cpu())
+            tin.copy_(tout[n - 1:n])
+        return out, rounds

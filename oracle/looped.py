@@ -431,6 +431,50 @@ class LoopedOracle:
             out_tok[k] = argmax_lowest(r["logits"][0])
         return dict(tokens=out_tok, logits=out_logits, status=out_status, x=out_x)
 
+    def spec_step(self, lane: int, token: int, draft_loops: int, verify_loops: int,
+                  draft_ahead: int) -> dict:
+        """One round of self-speculative decoding in chain mode (features page,
+        "Self-speculative decoding"): the same weights draft at the shallow depth
+        and verify at the deep one.
+
+        ``token`` sits at the lane's current length. The drafter proposes
+        ``draft_ahead`` greedy tokens, one decode at ``draft_loops`` each; then the
+        input token and the drafts go through ``verify_loops`` in one pass, which
+        gives the verifier's greedy token after every one of them. The longest
+        run of drafts that the verifier agrees with is kept, followed by the
+        verifier's own token at the first disagreement (or after the last
+        draft), so the emitted tokens are those greedy decoding at
+        ``verify_loops`` produces (the greedy-equality claim of the page's "Tree
+        speculative decoding" section, chain mode). The lane's length grows by
+        the number emitted; cache entries past it are stale and get overwritten.
+        """
+        if not (1 <= draft_loops <= verify_loops <= self.l_max):
+            raise ValueError("loops out of range")
+        if not draft_ahead >= 1:
+            raise ValueError("draft_ahead must be positive")
+        pos0, valid = self.length[lane], self.layers_valid[lane]
+        if pos0 + draft_ahead + 1 > self.max_seq:
+            raise CapacityError("cache full")
+        if pos0 > 0 and self.n_pre + verify_loops > valid:
+            raise CacheGapError("layers above %d miss earlier positions" % valid)
+        if self.status[lane] == LANE_ABORTED:
+            return dict(tokens=[], drafts=[], verified=[], logits=None)
+        drafts, t = [], token
+        for _ in range(draft_ahead):
+            r = self.forward(lane, [t], draft_loops, check_safety=False)
+            t = argmax_lowest(r["logits"][0])
+            drafts.append(t)
+        # back to the round's start: the verification writes the same positions
+        self.length[lane], self.layers_valid[lane] = pos0, valid
+        r = self.forward(lane, [token] + drafts, verify_loops, check_safety=False)
+        verified = [argmax_lowest(row) for row in r["logits"]]
+        agree = 0
+        while agree < draft_ahead and drafts[agree] == verified[agree]:
+            agree += 1
+        n = agree + 1
+        self.length[lane] = pos0 + n
+        return dict(tokens=verified[:n], drafts=drafts, verified=verified, logits=r["logits"][:n])
+
     def reset_lane(self, lane: int) -> None:
         self.length[lane] = 0
         self.layers_valid[lane] = 0

@@ -343,6 +343,60 @@ def test_prefill_equals_token_by_token():
     assert np.allclose(ra["logits"][-1], last, rtol=0, atol=1e-12 * np.abs(last).max())
 
 
+def _greedy(o, lane, token, loops, n):
+    out = []
+    while len(out) < n:
+        token = int(o.decode_step([lane], [loops], [token])["tokens"][0])
+        out.append(token)
+    return out
+
+
+@pytest.mark.parametrize("draft,verify,ahead", [(1, 4, 3), (2, 3, 4), (4, 4, 2)])
+def test_self_speculative_equals_greedy(draft, verify, ahead):
+    """Chain-mode self-speculation emits exactly the greedy tokens of plain
+    decoding at the verify depth (features page, "Tree speculative decoding",
+    chain mode), and leaves the cache a plain run would leave; with equal
+    depths every draft is accepted."""
+    w = synth.make_weights(SMALL16, 8, random_gains=True)
+    pr = synth.make_prompts(SMALL16.vocab, 1, 5, 13)[0]
+    n_tok = 14
+    plain = oracle.LoopedOracle(SMALL16, w, "f16", 1, 40, 4, exact=True)
+    t0 = plain.prefill(0, pr, verify)["next_token"]
+    ref = _greedy(plain, 0, t0, verify, n_tok)
+    spec = oracle.LoopedOracle(SMALL16, w, "f16", 1, 40, 4, exact=True)
+    assert spec.prefill(0, pr, verify)["next_token"] == t0
+    got, rounds, t = [], [], t0
+    while len(got) < n_tok:
+        r = spec.spec_step(0, t, draft, verify, ahead)
+        got.extend(r["tokens"])
+        rounds.append(len(r["tokens"]))
+        t = r["tokens"][-1]
+    if draft == verify:
+        assert all(n == ahead + 1 for n in rounds)
+    else:
+        assert min(rounds) < ahead + 1          # the rejection path ran
+    # the rounds may overshoot n_tok: decode plainly to the same point
+    extra = len(got) - n_tok
+    if extra:
+        ref += _greedy(plain, 0, ref[-1], verify, extra)
+    assert got == ref
+    # the state a plain run leaves: same length, same h in every layer it ran
+    T = len(pr) + len(got)
+    assert plain.length[0] == T and spec.length[0] == T
+    for layer in range(SMALL16.n_pre + verify):
+        a, b = plain.read_h(layer, 0, T), spec.read_h(layer, 0, T)
+        assert np.allclose(a, b, rtol=0, atol=1e-12 * np.abs(a).max()), layer
+
+
+def test_self_speculative_on_aborted_lane():
+    w = synth.make_weights(SMALL16, 9)
+    o = oracle.LoopedOracle(SMALL16, w, "int4", 1, 20, 4)
+    t = o.prefill(0, [3, 1, 4], 4)["next_token"]
+    assert o.decode_step([0], [4], [t], 1e-6)["status"][0] == oracle.LANE_ABORTED
+    r = o.spec_step(0, t, 1, 4, 3)
+    assert r["tokens"] == [] and o.length[0] == 3
+
+
 def test_cache_bytes_closed_form():
     # per-entry bytes at d_model 1024: fp16 K/V 4096, fp16-h 2048, INT8-h 1026, INT4-h 576
     assert looped.cache_bytes("kv", 1024, "f16", 1, 1, 1, 0) == 4096
