@@ -22,6 +22,11 @@ What it computes (TinyLoop documentation pages):
   for every L >= i + 1.
 * Per-lane loops (features page, "L-aware batching"): every lane of a batch runs
   its own loop count; lanes never interact.
+* Iteration-axis delta mode (features page, "4) Iteration-axis delta-KV"):
+  the unique layers keep fp16 h, the last of them serving as the anchor h0;
+  loop layer n_pre + i keeps the INT8 delta of its h against the previous
+  layer's reconstruction, one fp16 scale per head; a loop layer's h' is
+  fp16 of the FP32 prefix sum h0 + sum of s * q up to it.
 * Safety check (novel-contributions page, "Per-Iteration Safety Check";
   features page, "Per-iteration safety check"): during decode, after every loop
   iteration, the FP32 residual L2 norm is compared with a threshold and the
@@ -37,12 +42,15 @@ elements, divisors 127 and 7, fp32 IEEE divide and round-half-to-even, clamps
 [-127, 127] and [-8, 7], fp16 scales; the safety check fires iff
 not (norm <= threshold), only on loop iterations during decode, and a +inf
 threshold turns it off; an aborted lane emits no token and its length does not
-advance; argmax ties go to the lowest index.
+advance; argmax ties go to the lowest index; delta mode: the anchor h0 is
+the last unique layer's h, and the write side is closed-loop (each delta is
+taken against the previous layer's FP32 prefix sum, which is what the
+page's reconstruction-error table, falling as L grows, implies).
 
 Rounding points (the storage and operand dtypes that define the cache and the
 fp16 model; everything else is float64):
   R1  h rounded to the h dtype (model dtype);
-  R2  the INT8 / INT4 codec (float32 arithmetic, exactly as specified);
+  R2  the INT8 / INT4 / delta codec (float32 arithmetic, exactly as specified);
   R3  dequantised h' = fp16(q * s);
   R4  o, the norm-2 output, the GELU output and the final-norm output rounded
       to the model dtype before they enter a matrix product;
@@ -64,7 +72,7 @@ __all__ = [
     "attend", "entry_bytes", "cache_bytes", "LoopedOracle",
 ]
 
-MODES = ("kv", "f32", "f16", "int8", "int4")
+MODES = ("kv", "f32", "f16", "int8", "int4", "delta8")
 LANE_OK, LANE_ABORTED = 0, 1
 INT4_GROUP = 32
 
@@ -102,17 +110,22 @@ def encode_int(h16: np.ndarray, group: int, qmax: int, qmin: int) -> Tuple[np.nd
     group whose scale is zero (all-zero or underflowed) gets q = 0.
     Returns int8 codes [..., D] and fp16 scales [..., D / group].
     """
-    h16 = np.asarray(h16, dtype=np.float16)
-    D = h16.shape[-1]
+    return _encode_f32(np.asarray(h16, dtype=np.float16).astype(np.float32), group, qmax, qmin)
+
+
+def _encode_f32(x: np.ndarray, group: int, qmax: int, qmin: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The rule of ``encode_int`` on float32 rows."""
+    x = np.asarray(x, dtype=np.float32)
+    D = x.shape[-1]
     assert D % group == 0
-    hf = h16.astype(np.float32).reshape(h16.shape[:-1] + (D // group, group))
+    hf = x.reshape(x.shape[:-1] + (D // group, group))
     am = np.max(np.abs(hf), axis=-1)
     s = (am / np.float32(qmax)).astype(np.float16)
     sf = s.astype(np.float32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint(hf / sf)
     q = np.where(sf == 0, np.float32(0), np.clip(q, qmin, qmax))
-    return q.astype(np.int8).reshape(h16.shape), s
+    return q.astype(np.int8).reshape(x.shape), s
 
 
 def decode_int(q: np.ndarray, s: np.ndarray) -> np.ndarray:
@@ -136,6 +149,25 @@ def int8_encode(h16):
 def int4_encode(h16):
     """INT4-h: one scale per 32 consecutive d_model elements, divisor 7, clamp [-8, 7]."""
     return encode_int(h16, INT4_GROUP, 7, -8)
+
+
+# ---------------------------------------------------------------------------
+# iteration-axis delta codec (features page, "4) Iteration-axis delta-KV")
+# ---------------------------------------------------------------------------
+def delta_encode(d32: np.ndarray, d_head: int) -> Tuple[np.ndarray, np.ndarray]:
+    """INT8 codes of float32 delta rows [..., D] with one fp16 scale per head
+    (the [T, n_heads] scale grid): the INT8 rule (divisor 127, clamp
+    [-127, 127]) in groups of d_head."""
+    return _encode_f32(d32, d_head, 127, -127)
+
+
+def delta_accumulate(r: np.ndarray, q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """One term of the FP32 prefix sum: r + s[head] * q, float32. The product
+    of an fp16 scale and an 8-bit code is exact in float32, so the only
+    rounding is the addition."""
+    D = q.shape[-1]
+    sf = np.repeat(s.astype(np.float32), D // s.shape[-1], axis=-1)
+    return (np.asarray(r, np.float32) + sf * q.astype(np.float32)).astype(np.float32)
 
 
 # ---------------------------------------------------------------------------
@@ -168,15 +200,22 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, n_heads: int, pos0: int)
 # cache byte counts (closed form)
 # ---------------------------------------------------------------------------
 def entry_bytes(mode: str, d_model: int) -> int:
-    """Bytes of one cache entry (one token, one layer-iteration)."""
+    """Bytes of one cache entry (one token, one layer-iteration); the delta mode
+    has two kinds of entry and is counted by ``cache_bytes``."""
     D = d_model
     return {"kv": None, "f32": 4 * D, "f16": 2 * D, "int8": D + 2,
             "int4": D // 2 + 2 * (D // INT4_GROUP)}[mode]
 
 
 def cache_bytes(mode: str, d_model: int, model_dtype: str, n_lanes: int, max_seq: int,
-                l_max: int, n_pre: int) -> int:
-    """Total cache payload for n_pre + L_max layers x lanes x max_seq positions."""
+                l_max: int, n_pre: int, n_heads: int = 0) -> int:
+    """Total cache payload for n_pre + L_max layers x lanes x max_seq positions.
+
+    Delta mode: the n_pre unique layers keep fp16 h (the last one is the
+    anchor h0), every loop layer INT8 codes plus one fp16 scale per head."""
+    if mode == "delta8":
+        per_token = n_pre * 2 * d_model + l_max * (d_model + 2 * n_heads)
+        return n_lanes * max_seq * per_token
     if mode == "kv":
         per = 2 * d_model * (4 if model_dtype == "f32" else 2)
     else:
@@ -201,6 +240,8 @@ class LoopedOracle:
             raise ValueError("an fp32 model stores fp32 h or K/V")
         if shape.dtype == "f16" and mode == "f32":
             raise ValueError("an fp16 model stores fp16, INT8 or INT4 h, or fp16 K/V")
+        if mode == "delta8" and (exact or shape.n_pre < 1):
+            raise ValueError("the delta codec needs a pre layer for its anchor and rounds by definition")
         self.shape = shape
         self.mode = mode
         self.exact = exact
@@ -246,8 +287,10 @@ class LoopedOracle:
             if self.mode == "kv":
                 dt = np.float64 if self.exact else self.dt
                 slot = {"k": np.zeros((S, D), dt), "v": np.zeros((S, D), dt)}
-            elif self.mode in ("f32", "f16"):
+            elif self.mode in ("f32", "f16") or (self.mode == "delta8" and layer < self.n_pre):
                 slot = {"h": np.zeros((S, D), np.float64 if self.exact else self.dt)}
+            elif self.mode == "delta8":
+                slot = {"q": np.zeros((S, D), np.int8), "s": np.zeros((S, self.H), np.float16)}
             else:
                 ng = 1 if self.mode == "int8" else D // INT4_GROUP
                 slot = {"q": np.zeros((S, D), np.int8), "s": np.zeros((S, ng), np.float16)}
@@ -268,17 +311,42 @@ class LoopedOracle:
         elif self.mode == "int4":
             q, s = int4_encode(h.astype(np.float16))
             slot["q"][pos0:pos0 + n], slot["s"][pos0:pos0 + n] = q, s
+        elif self.mode == "delta8":
+            if layer < self.n_pre:
+                slot["h"][pos0:pos0 + n] = h
+            else:
+                # closed loop: the delta is taken against the previous layer as
+                # the reader rebuilds it, so quantisation errors do not pile up
+                r_prev = self.delta_rec(layer - 1, lane, pos0, n)
+                d = h.astype(np.float16).astype(np.float32) - r_prev
+                q, s = delta_encode(d, self.d)
+                slot["q"][pos0:pos0 + n], slot["s"][pos0:pos0 + n] = q, s
         else:
             W = self.weights_for(layer)
             hf = np.asarray(h, dtype=np.float64)
             slot["k"][pos0:pos0 + n] = self._rd(hf @ W["wk"].T)      # R5
             slot["v"][pos0:pos0 + n] = self._rd(hf @ W["wv"].T)
 
+    def delta_rec(self, layer: int, lane: int, pos0: int, n: int) -> np.ndarray:
+        """Delta mode, float32 rows of positions pos0..pos0+n-1: a unique layer's
+        own h; a loop layer's FP32 prefix sum h0 + sum of s * q over the loop
+        layers up to it, h0 being the last unique layer's h."""
+        if layer < self.n_pre:
+            return self._slot(layer, lane)["h"][pos0:pos0 + n].astype(np.float32)
+        r = self._slot(self.n_pre - 1, lane)["h"][pos0:pos0 + n].astype(np.float32)
+        for j in range(self.n_pre, layer + 1):
+            sj = self._slot(j, lane)
+            r = delta_accumulate(r, sj["q"][pos0:pos0 + n], sj["s"][pos0:pos0 + n])
+        return r
+
     def read_h(self, layer: int, lane: int, T: int) -> np.ndarray:
-        """Dequantised h' for positions 0..T-1 as float64 (R3)."""
+        """Dequantised h' for positions 0..T-1 as float64 (R3; delta mode: the
+        prefix sum rounded to fp16)."""
         slot = self._slot(layer, lane)
-        if self.mode in ("f32", "f16"):
+        if self.mode in ("f32", "f16") or (self.mode == "delta8" and layer < self.n_pre):
             return slot["h"][:T].astype(np.float64)
+        if self.mode == "delta8":
+            return self.delta_rec(layer, lane, 0, T).astype(np.float16).astype(np.float64)
         return decode_int(slot["q"][:T], slot["s"][:T]).astype(np.float64)
 
     def read_codes(self, layer: int, lane: int, pos0: int, n: int):

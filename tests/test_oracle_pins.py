@@ -343,6 +343,112 @@ def test_prefill_equals_token_by_token():
     assert np.allclose(ra["logits"][-1], last, rtol=0, atol=1e-12 * np.abs(last).max())
 
 
+# ------------------------------------------------------- delta codec (f2)
+def test_delta_codec_hand_case():
+    """Features page, "4) Iteration-axis delta-KV", worked by hand on D = 4,
+    two heads of 2: anchor h0 = (1, 2, 3, 4), next h = (1.5, 2, 3, 4.25).
+    delta = (0.5, 0, 0, 0.25); head scales fp16(0.5/127) = 1032 * 2^-18 and
+    fp16(0.25/127) = 1032 * 2^-19; codes rint(127.0077) = 127 and 0; the FP32
+    prefix sum is 1 + 127 * 1032 * 2^-18 = 49151/32768 and 4 + 127 * 1032 * 2^-19,
+    both exact in fp32, which round to fp16 1.5 and 4.25."""
+    h0 = np.array([[1, 2, 3, 4]], np.float16)
+    h1 = np.array([[1.5, 2, 3, 4.25]], np.float16)
+    d = h1.astype(np.float32) - h0.astype(np.float32)
+    q, sc = looped.delta_encode(d, 2)
+    assert q.tolist() == [[127, 0, 0, 127]]
+    assert sc.astype(np.float64).tolist() == [[1032 * 2.0 ** -18, 1032 * 2.0 ** -19]]
+    r = looped.delta_accumulate(h0.astype(np.float32), q, sc)
+    assert r.astype(np.float64).tolist() == [[49151 / 32768, 2, 3, 4 + 127 * 1032 * 2.0 ** -19]]
+    assert r.astype(np.float16).tolist() == [[1.5, 2, 3, 4.25]]
+
+
+DELTA16 = synth.ModelShape("delta16", 64, 4, 16, 128, 2, 97, "f16")
+
+
+def _trajectory(n_pos, n_layers, seed):
+    """fp16 h rows per layer that settle geometrically, like the loop's
+    converging trajectory (the relative step shrinks by 0.6 per layer)."""
+    rng = np.random.default_rng(seed)
+    base = rng.standard_normal((n_pos, 64)).astype(np.float32)
+    out, step = [], 1.0
+    for _ in range(n_layers):
+        base = base + np.float32(step) * rng.standard_normal((n_pos, 64)).astype(np.float32)
+        out.append(base.astype(np.float16))
+        step *= 0.6
+    return out
+
+
+def test_delta_closed_loop_error_is_one_step():
+    """Closed loop: every loop layer's FP32 reconstruction is within half of its
+    own head scale of its h (one quantisation, no pile-up of the earlier,
+    much coarser steps), and h' is that reconstruction rounded to fp16."""
+    o = oracle.LoopedOracle(DELTA16, synth.make_weights(DELTA16, 1), "delta8", 1, 8, 10)
+    hs = _trajectory(6, DELTA16.n_pre + 10, 3)
+    for layer, h in enumerate(hs):
+        o.write_h(layer, 0, 0, h)
+    first_step = None
+    for layer in range(DELTA16.n_pre, len(hs)):
+        r = o.delta_rec(layer, 0, 0, 6).astype(np.float64)
+        _, sc = o.read_codes(layer, 0, 0, 6)
+        half = np.repeat(sc.astype(np.float64), 16, axis=-1) / 2
+        err = np.abs(r - hs[layer].astype(np.float64))
+        assert np.all(err <= half * (1 + 2.0 ** -10) + 4 * np.spacing(np.abs(r).astype(np.float32))), layer
+        if first_step is None:
+            first_step = float(np.max(half))
+        assert np.array_equal(o.read_h(layer, 0, 6), r.astype(np.float32).astype(np.float16).astype(np.float64))
+    assert float(np.max(half)) < first_step / 50      # the last steps are far finer than the first
+
+
+def test_delta_open_loop_would_pile_up():
+    """The same trajectory coded open-loop (deltas of the exact h) misses the
+    one-step bound at the last layer: the closed-loop reading is what the
+    bound above pins."""
+    hs = _trajectory(6, DELTA16.n_pre + 10, 3)
+    r = hs[DELTA16.n_pre - 1].astype(np.float32)
+    for layer in range(DELTA16.n_pre, len(hs)):
+        d = hs[layer].astype(np.float32) - hs[layer - 1].astype(np.float32)
+        q, sc = looped.delta_encode(d, 16)
+        r = looped.delta_accumulate(r, q, sc)
+    half = np.repeat(sc.astype(np.float64), 16, axis=-1) / 2
+    assert np.any(np.abs(r.astype(np.float64) - hs[-1].astype(np.float64)) > half * 1.01)
+
+
+def test_delta_identical_layer_codes_zero():
+    """A first loop layer equal to the anchor has a zero delta: zero codes,
+    zero scales, and h' equal to the anchor bit for bit."""
+    o = oracle.LoopedOracle(DELTA16, synth.make_weights(DELTA16, 1), "delta8", 1, 4, 2)
+    h = _trajectory(3, 1, 5)[0]
+    o.write_h(0, 0, 0, h)
+    o.write_h(1, 0, 0, h)
+    o.write_h(2, 0, 0, h)
+    q, sc = o.read_codes(2, 0, 0, 3)
+    assert not q.any() and not sc.astype(np.float32).any()
+    assert np.array_equal(o.read_h(2, 0, 3), h.astype(np.float64))
+
+
+def test_delta_variable_L_reuse_and_resume():
+    """Delta mode keeps the variable-L property (loop layer n_pre + i depends
+    only on earlier layers of the same position) and warm start equals a
+    fresh run, bit for bit."""
+    w = synth.make_weights(DELTA16, 2, random_gains=True)
+    seq = list(synth.make_prompts(DELTA16.vocab, 1, 5, 7)[0]) + [11, 23, 5]
+    caches = {}
+    for L in (2, 5):
+        o = oracle.LoopedOracle(DELTA16, w, "delta8", 1, 16, 5)
+        o.prefill(0, seq[:5], L)
+        for t in seq[5:]:
+            o.decode_step([0], [L], [t])
+        caches[L] = o
+    for layer in range(DELTA16.n_pre + 2):
+        assert np.array_equal(caches[2].read_h(layer, 0, 8), caches[5].read_h(layer, 0, 8))
+    fresh = oracle.LoopedOracle(DELTA16, w, "delta8", 1, 16, 5)
+    rf = fresh.prefill(0, seq[:6], 5)
+    warm = oracle.LoopedOracle(DELTA16, w, "delta8", 1, 16, 5)
+    r2 = warm.forward(0, seq[:6], 2, check_safety=False)
+    r5 = warm.extend_depth(0, r2["x"], 2, 5)
+    assert np.array_equal(r5["logits"], rf["logits"])
+
+
 def _greedy(o, lane, token, loops, n):
     out = []
     while len(out) < n:
@@ -395,6 +501,12 @@ def test_self_speculative_on_aborted_lane():
     assert o.decode_step([0], [4], [t], 1e-6)["status"][0] == oracle.LANE_ABORTED
     r = o.spec_step(0, t, 1, 4, 3)
     assert r["tokens"] == [] and o.length[0] == 3
+
+
+def test_cache_bytes_closed_form_delta():
+    # 407M shape, 2 unique layers + 8 loop layers: 2 * 2048 + 8 * (1024 + 2 * 16) bytes a token
+    assert looped.cache_bytes("delta8", 1024, "f16", 1, 1, 8, 2, 16) == 12544
+    assert looped.cache_bytes("delta8", 1024, "f16", 3, 5, 8, 2, 16) == 15 * 12544
 
 
 def test_cache_bytes_closed_form():
