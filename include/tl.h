@@ -52,13 +52,24 @@ typedef enum {
  * H_INT8:  h as int8 codes with one fp16 absmax scale per token, D + 2 bytes.
  * H_INT4:  h as 4-bit codes with one fp16 absmax scale per 32 consecutive
  *          d_model elements, D/2 + D/16 bytes.
- * (features page, "Store-h KV cache": FP16-h, INT8-h and INT4-h modes.) */
+ * (features page, "Store-h KV cache": FP16-h, INT8-h and INT4-h modes.)
+ * H_DELTA8: the iteration-axis delta codec (features page, "4) Iteration-axis
+ *          delta-KV"; fp16 models with n_pre >= 1). The n_pre unique layers
+ *          keep fp16 h (2*D bytes); the last of them is the anchor h0. Loop
+ *          layer n_pre + i keeps the INT8 delta of its h against the previous
+ *          layer's reconstruction with one fp16 absmax scale per head
+ *          (D + 2*n_heads bytes); its h' is fp16 of the FP32 prefix sum
+ *          h0 + sum over loop layers 0..i of scale * code. The delta is taken
+ *          against that same prefix sum (closed loop), so each layer's h'
+ *          carries one quantisation error. Attention rebuilds a layer's h'
+ *          for all positions into workspace before reconstructing K/V. */
 typedef enum {
   TL_CACHE_KV = 0,
   TL_CACHE_H_F32 = 1,
   TL_CACHE_H_F16 = 2,
   TL_CACHE_H_INT8 = 3,
-  TL_CACHE_H_INT4 = 4
+  TL_CACHE_H_INT4 = 4,
+  TL_CACHE_H_DELTA8 = 5
 } tl_cache_mode;
 
 typedef enum { TL_LANE_OK = 0, TL_LANE_ABORTED = 1 } tl_lane_status;
@@ -257,7 +268,12 @@ tl_status tl_cache_set_length(tl_cache* c, int lane, int length, int layers_vali
  * d_scales (nullable, INT modes): device uint16 (fp16 bits) [n, groups]
  *   (INT8: 1 group, INT4: d_model/32 groups).
  * d_h (nullable): device, model dtype: [n, d_model] the h the attention uses
- *   (dequantised fp16(q*s) for INT modes), or [n, 2*d_model] K|V in KV mode. */
+ *   (dequantised fp16(q*s) for INT modes, fp16 of the prefix sum in delta
+ *   mode), or [n, 2*d_model] K|V in KV mode.
+ * Delta mode, loop layers: d_codes the INT8 deltas [n, d_model], d_scales the
+ *   per-head scales [n, n_heads]. tl_cache_write_h and tl_cache_fill_synthetic
+ *   code a loop layer against the cache's reconstruction of the layer below,
+ *   so layers are written in order. */
 tl_status tl_cache_read(const tl_cache* c, int lane, int layer, int pos0, int n, int8_t* d_codes,
                         uint16_t* d_scales, void* d_h, void* stream);
 

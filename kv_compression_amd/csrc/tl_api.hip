@@ -39,6 +39,7 @@ struct tl_cache {
   const tl_model* m;
   int mode, n_lanes, max_seq, l_max, n_layers;
   CacheView cv;
+  CacheView mat;                   // delta mode: the one-layer fp16 view of Workspace::hmat
   Workspace ws;
   std::vector<int> host_len;       // upper bound of each lane's length
   std::vector<int> layers_valid;   // layers filled for every position < length
@@ -97,7 +98,11 @@ bool config_ok(const tl_config* c, std::string* why) {
 }
 
 bool mode_ok(const tl_config* c, int mode, std::string* why) {
-  if (mode < TL_CACHE_KV || mode > TL_CACHE_H_INT4) { *why = "unknown cache mode"; return false; }
+  if (mode < TL_CACHE_KV || mode > TL_CACHE_H_DELTA8) { *why = "unknown cache mode"; return false; }
+  if (mode == TL_CACHE_H_DELTA8 && (c->dtype != TL_DTYPE_F16 || c->n_pre < 1)) {
+    *why = "the delta codec needs an fp16 model and a unique layer for its anchor";
+    return false;
+  }
   if (c->dtype == TL_DTYPE_F32 && !(mode == TL_CACHE_KV || mode == TL_CACHE_H_F32)) {
     *why = "fp32 models store fp32 h or K/V";
     return false;
@@ -130,8 +135,15 @@ size_t entry_bytes(const tl_config* c, int mode) {
   return 0;
 }
 
+// bytes of one position of one lane over all n_pre + l_max layers
+size_t position_bytes(const tl_config* c, int mode, int l_max) {
+  if (mode == TL_CACHE_H_DELTA8)
+    return (size_t)c->n_pre * 2 * c->d_model + (size_t)l_max * (c->d_model + 2 * c->n_heads);
+  return (size_t)(c->n_pre + l_max) * entry_bytes(c, mode);
+}
+
 struct Layout {
-  size_t off[20];
+  size_t off[22];
   size_t total;
   int R, Bmax, S;
 };
@@ -149,7 +161,8 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
   L.S = (max_seq + min_split - 1) / min_split;
   const size_t head_rows = std::max(L.Bmax, kSpecRows);
   const size_t ppart = (size_t)kMaxChunk * c->n_heads * 8 * (c->d_head + 2);
-  const size_t sizes[20] = {
+  const bool delta = mode == TL_CACHE_H_DELTA8;
+  const size_t sizes[22] = {
       (size_t)n_lanes * 4,                        // len
       (size_t)n_lanes * 4,                        // status
       (size_t)n_lanes * l_max * 4,                // norms
@@ -168,9 +181,11 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
       (size_t)L.R * 4,                            // row_dead
       (size_t)(2 * kSpecRows + 2) * 4,            // spec
       ppart * 4,                                  // ppart
+      delta ? (size_t)L.R * D * 4 : 0,            // hrec
+      delta ? (size_t)n_lanes * max_seq * D * 2 : 0,   // hmat
   };
   size_t o = 0;
-  for (int i = 0; i < 20; ++i) {
+  for (int i = 0; i < 22; ++i) {
     L.off[i] = o;
     o = align256(o + sizes[i]);
   }
@@ -235,7 +250,7 @@ void tl_model_destroy(tl_model* m) { delete m; }
 size_t tl_cache_bytes(const tl_config* cfg, int mode, int n_lanes, int max_seq, int l_max) {
   std::string why;
   if (!config_ok(cfg, &why) || !mode_ok(cfg, mode, &why) || !dims_ok(n_lanes, max_seq, l_max)) return 0;
-  return (size_t)(cfg->n_pre + l_max) * n_lanes * max_seq * entry_bytes(cfg, mode);
+  return (size_t)n_lanes * max_seq * position_bytes(cfg, mode, l_max);
 }
 
 size_t tl_workspace_bytes(const tl_config* cfg, int mode, int n_lanes, int max_seq, int l_max) {
@@ -296,6 +311,16 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   s.spec = (int32_t*)(w + L.off[18]);
   s.ppart = (float*)(w + L.off[19]);
   s.ppart_floats = (int)((size_t)kMaxChunk * cfg->n_heads * 8 * (cfg->d_head + 2));
+  s.hrec = mode == TL_CACHE_H_DELTA8 ? (float*)(w + L.off[20]) : nullptr;
+  s.hmat = mode == TL_CACHE_H_DELTA8 ? (void*)(w + L.off[21]) : nullptr;
+  v.n_pre = cfg->n_pre; v.H = cfg->n_heads; v.dh = cfg->d_head;
+  if (mode == TL_CACHE_H_DELTA8) {
+    v.scales = (uint16_t*)(v.base + (size_t)n_lanes * max_seq *
+                                        ((size_t)cfg->n_pre * 2 * D + (size_t)l_max * D));
+    CacheView& mt = c->mat;
+    mt = v;
+    mt.base = (char*)s.hmat; mt.scales = nullptr; mt.mode = TL_CACHE_H_F16; mt.n_layers = 1;
+  }
   s.R = L.R; s.Bmax = L.Bmax; s.S = L.S;
   c->host_len.assign(n_lanes, 0);
   c->layers_valid.assign(n_lanes, 0);
@@ -396,8 +421,10 @@ tl_status tl_cache_read(const tl_cache* c, int lane, int layer, int pos0, int n,
   if (st) return st;
   if (layer < 0 || layer >= c->n_layers) return fail(TL_E_ARG, "layer out of range");
   if (n <= 0 || pos0 < 0 || pos0 + n > c->max_seq) return fail(TL_E_ARG, "positions out of range");
-  const bool int_mode = c->mode == TL_CACHE_H_INT8 || c->mode == TL_CACHE_H_INT4;
-  if ((d_codes || d_scales) && !int_mode) return fail(TL_E_ARG, "codes and scales exist in INT modes only");
+  const bool int_mode = c->mode == TL_CACHE_H_INT8 || c->mode == TL_CACHE_H_INT4 ||
+                        (c->mode == TL_CACHE_H_DELTA8 && layer >= c->m->mv.n_pre);
+  if ((d_codes || d_scales) && !int_mode)
+    return fail(TL_E_ARG, "codes and scales exist in INT modes only (delta mode: loop layers)");
   TL_HIP(launch_cache_read(c->m->mv, c->cv, lane, layer, pos0, n, d_codes, d_scales, d_h,
                            (hipStream_t)stream));
   return TL_OK;
@@ -443,11 +470,16 @@ tl_status run_chunk(tl_cache* c, int lane, int pos0, int n, int layer_begin, int
   // embeddings, or the caller's residuals when resuming mid-loop
   TL_HIP(launch_prefill_setup(mv, ws, lane, n, d_x_in ? nullptr : d_tokens, pos0, s));
   if (d_x_in) TL_HIP(launch_copy_f32(d_x_in, ws.x, (size_t)n * D, s));
+  const bool delta = c->mode == TL_CACHE_H_DELTA8;
+  // delta mode, resuming mid-loop: the rows' reconstruction of the layer below
+  if (delta && layer_begin > 0)
+    TL_HIP(launch_delta_rec(c->cv, layer_begin - 1, lane, pos0, n, ws.hrec, s));
   for (int layer = layer_begin; layer < layer_end; ++layer) {
     const LayerW& W = layer_w(c, layer);
     AppendArgs a{};
     a.src = HS_NORM; a.n = n; a.layer = layer; a.x = ws.x; a.gain = W.norm1;
     a.row_lane = ws.row_lane; a.row_pos = ws.row_pos; a.status = ws.status; a.h_out = ws.h;
+    a.rec = ws.hrec;
     TL_HIP(launch_norm_append(mv, c->cv, a, s));
     const void* kv;
     if (c->mode == TL_CACHE_KV) {
@@ -460,7 +492,13 @@ tl_status run_chunk(tl_cache* c, int lane, int pos0, int n, int layer_begin, int
       GemmArgs g = gemm_args(W.w_qkv, D, ws.h, D, n, D, D, EPI_STORE_F32, ws.q, D);
       g.scale = qscale; g.row_lane = ws.row_lane; g.status = ws.status; g.row_dead = ws.row_dead;
       TL_HIP(launch_gemm(mv, g, s));
-      TL_HIP(launch_recon_store(mv, c->cv, layer, lane, T, W.w_qkv, ws.kvbuf, ws.status, s));
+      if (delta) {
+        // h' of this layer for positions 0 .. T-1, then the fp16-h reconstruction
+        TL_HIP(launch_delta_mat(c->cv, c->mat, layer, ws.row_lane, ws.row_pos, ws.status, 1, T, T, s));
+        TL_HIP(launch_recon_store(mv, c->mat, 0, lane, T, W.w_qkv, ws.kvbuf, ws.status, s));
+      } else {
+        TL_HIP(launch_recon_store(mv, c->cv, layer, lane, T, W.w_qkv, ws.kvbuf, ws.status, s));
+      }
       kv = ws.kvbuf;
     }
     if (c->prof_on) {
@@ -625,7 +663,7 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     // layer (the one after loop iteration layer - 1 - n_pre) and the append
     // of h to the cache
     auto row_work = [&](GemmArgs& g) {
-      g.norm_gain = W.norm1; g.row_tasks = 1; g.check_iter = -1;
+      g.norm_gain = W.norm1; g.row_tasks = 1; g.check_iter = -1; g.rec = ws.hrec;
       g.cache = c->cv; g.layer = layer; g.row_pos = ws.row_pos;
       g.row_lane = ws.row_lane; g.status = ws.status; g.row_dead = ws.row_dead;
       if (layer > mv.n_pre) {
@@ -660,9 +698,15 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
       g.scale = qscale;
       row_work(g);
       TL_HIP(launch_gemm(mv, g, s));
+      if (c->mode == TL_CACHE_H_DELTA8) {
+        // h' of this layer for every active row's positions, then the fp16-h kernel
+        TL_HIP(launch_delta_mat(c->cv, c->mat, layer, ws.row_lane, ws.row_pos, ws.status, rows, t_ub, 0, s));
+        ra.cache = c->mat;
+        ra.layer = 0;
+      }
       if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
       TL_HIP(launch_recon_attn(mv, ra, s));
-      split_len = recon_split_len(mv, c->mode);
+      split_len = recon_split_len(mv, ra.cache.mode);
     }
     if (c->prof_on) {
       TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));

@@ -114,15 +114,112 @@ __device__ __forceinline__ half4 int8_dequant4(uint32_t w, half_t s) {
   return r;
 }
 
+// EPT codes of one delta row (8- or 4-byte vector loads where EPT allows)
+template <int EPT>
+struct DeltaRow {
+  int8_t q[EPT];
+};
+template <int EPT>
+__device__ __forceinline__ DeltaRow<EPT> delta_load(const int8_t* p) {
+  DeltaRow<EPT> r;
+  if constexpr (EPT == 8) {
+    typedef int8_t v8 __attribute__((ext_vector_type(8)));
+    const v8 v = *(const v8*)p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.q[i] = v[i];
+  } else if constexpr (EPT == 4) {
+    typedef int8_t v4 __attribute__((ext_vector_type(4)));
+    const v4 v = *(const v4*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.q[i] = v[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) r.q[i] = p[i];
+  }
+  return r;
+}
+// Delta mode: elements e0 .. e0+EPT-1 of the FP32 reconstruction of `layer`
+// at (lane, pos): a unique layer's own h, or the prefix sum of the anchor
+// (layer n_pre - 1) and scale * code of loop layers n_pre .. layer, added in
+// that order (each product is exact in fp32; the addition rounds).
+// EPT divides the head width, so one scale covers a thread's elements.
+template <int EPT>
+__device__ __forceinline__ void delta_prefix(const CacheView& c, int layer, int lane, int pos,
+                                             int e0, float (&r)[EPT]) {
+  const half_t* a = c.delta_anchor(layer < c.n_pre ? layer : c.n_pre - 1, lane, pos) + e0;
+  if constexpr (EPT == 8) {
+    const half8 v = *(const half8*)a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (float)v[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) r[i] = (float)a[i];
+  }
+  const int head = e0 / c.dh;
+  int j = c.n_pre;
+  // four layers' codes and scales in flight at a time
+  for (; j + 3 <= layer; j += 4) {
+    DeltaRow<EPT> q[4];
+    half_t sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      q[u] = delta_load<EPT>(c.delta_codes(j + u, lane, pos) + e0);
+      sc[u] = h_from_bits(c.delta_scales(j + u, lane, pos)[head]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) r[i] = r[i] + (float)sc[u] * (float)q[u].q[i];
+  }
+  for (; j <= layer; ++j) {
+    const DeltaRow<EPT> q = delta_load<EPT>(c.delta_codes(j, lane, pos) + e0);
+    const float sf = (float)h_from_bits(c.delta_scales(j, lane, pos)[head]);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) r[i] = r[i] + sf * (float)q.q[i];
+  }
+}
+
 // Store elements e0 .. e0+EPT-1 of h (already rounded to the model dtype) of
 // one cache entry (layer, lane, pos) in the cache's h codec. The threads of a
 // row hold consecutive runs of EPT elements, so an INT4 group is 32 / EPT
 // consecutive lanes and an 8-code INT4 word 8 / EPT of them; rowmax(v) returns
 // the maximum of v over all threads of the row (the INT8 per-token scale) and
-// must be called by all of them.
+// must be called by all of them. Delta mode: rec (the thread's EPT elements
+// of the row's FP32 reconstruction of the previous layer) is updated to this
+// layer's; a head of dh elements is dh / EPT consecutive lanes of one wave.
 template <typename T, int EPT, typename RowMax>
 __device__ __forceinline__ void cache_store_h(const CacheView& c, int layer, int lane, int pos,
-                                              int e0, const float (&h)[EPT], RowMax&& rowmax) {
+                                              int e0, const float (&h)[EPT], RowMax&& rowmax,
+                                              float* rec = nullptr) {
+  if (c.mode == TL_CACHE_H_DELTA8) {
+    if (layer < c.n_pre) {
+      half_t* dst = c.delta_anchor(layer, lane, pos) + e0;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) dst[i] = (half_t)h[i];
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) rec[i] = h[i];
+      return;
+    }
+    float d[EPT], am = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      d[i] = h[i] - rec[i];
+      am = fmaxf(am, fabsf(d[i]));
+    }
+    const int tph = c.dh / EPT;   // threads of one head
+    for (int o = 1; o < tph; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    const half_t s = codec_scale(am, 127.f);
+    const float sf = (float)s;
+    int8_t* qp = c.delta_codes(layer, lane, pos) + e0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int q = codec_code(d[i], sf, -127.f, 127.f);
+      qp[i] = (int8_t)q;
+      rec[i] = rec[i] + sf * (float)q;
+    }
+    if (e0 % c.dh == 0) c.delta_scales(layer, lane, pos)[e0 / c.dh] = h_bits(s);
+    return;
+  }
   const int kb = e0 / kKBlock, w = e0 % kKBlock;
   char* row = c.code_row(layer, lane, kb, pos);
   if (c.mode == TL_CACHE_H_F32 || c.mode == TL_CACHE_H_F16) {

@@ -150,7 +150,8 @@ __device__ void row_tasks_ept(const ModelView& m, const GemmArgs& g, int m0, int
     for (int i = 0; i < EPT; ++i) h[i] = holds ? to_f(from_f<T>(pre.x[i] * rinv[rr] * to_f(pre.gn[i]))) : 0.f;
     auto rowmax = [&](float v) { return block_max(v, rmax); };
     if (holds) {
-      cache_store_h<T, EPT>(g.cache, g.layer, lane, g.row_pos[row], e0, h, rowmax);
+      cache_store_h<T, EPT>(g.cache, g.layer, lane, g.row_pos[row], e0, h, rowmax,
+                            g.rec ? g.rec + (size_t)row * D + e0 : nullptr);
     } else if (g.cache.mode == TL_CACHE_H_INT8) {
       rowmax(0.f);   // threads past the row still join the INT8 scale reduction
     }

@@ -43,11 +43,27 @@ constexpr __host__ __device__ inline int block_row_bytes(int mode) {
 //           INT8 scales[layer][lane][pos]                  (fp16 bits)
 //           INT4 scales[layer][lane][kb][pos][2]           (fp16 bits, groups 2kb, 2kb+1)
 // KV mode:  kv[layer][lane][pos][2D]                       K | V, model dtype
+// Delta mode (plain rows, read only by the delta kernels):
+//           anchors[layer < n_pre][lane][pos][D]              fp16 h
+//           codes[layer - n_pre][lane][pos][D]                int8 deltas
+//           scales[layer - n_pre][lane][pos][H]               fp16 bits
 struct CacheView {
   char* base;          // entries (codes, or K|V rows)
   uint16_t* scales;    // INT modes
   int mode, dtype;
   int D, n_lanes, max_seq, n_layers;
+  int n_pre, H, dh;    // delta mode addressing and head groups
+
+  __host__ __device__ half_t* delta_anchor(int layer, int lane, int pos) const {
+    return (half_t*)base + (lane_block(layer, lane) * max_seq + pos) * D;
+  }
+  __host__ __device__ int8_t* delta_codes(int layer, int lane, int pos) const {
+    return (int8_t*)(base + (size_t)n_pre * n_lanes * max_seq * D * 2) +
+           (((size_t)(layer - n_pre) * n_lanes + lane) * max_seq + pos) * D;
+  }
+  __host__ __device__ uint16_t* delta_scales(int layer, int lane, int pos) const {
+    return scales + (((size_t)(layer - n_pre) * n_lanes + lane) * max_seq + pos) * H;
+  }
 
   __host__ __device__ size_t lane_block(int layer, int lane) const {
     return (size_t)layer * n_lanes + lane;
@@ -90,6 +106,8 @@ struct Workspace {
   float* logits;       // [max(Bmax, kSpecRows), V]
   float* part;         // [Bmax, H, S, d + 2]
   void* kvbuf;         // [max_seq, 2D] f32 (prefill K/V rebuilt from h)
+  float* hrec;         // [R, D]   delta mode: each row's FP32 reconstruction of the last layer written
+  void* hmat;          // delta mode: one layer's h' of every lane, fp16 tiled (a one-layer H_F16 cache)
   float* ppart;        // [kMaxChunk * H * 8 * (d + 2)] prefill key-split partials
   int ppart_floats;
   int32_t* spec;       // speculative round: [0, kSpecRows) input token then drafts,
@@ -146,6 +164,9 @@ struct AppendArgs {
   int fixed_lane, pos0;
   const int32_t* status;     // nullable
   void* h_out;               // nullable
+  // delta mode: rows [n, D] holding each row's reconstruction of layer - 1,
+  // updated to this layer's; null: rebuilt from the cache (layers in order)
+  float* rec = nullptr;
   // HS_NORM, decode: the residual entering this layer is the one after loop
   // iteration check_iter (-1: none); its FP32 norm goes to norms[lane, iter]
   // and, if check and !(norm <= thr), the lane aborts before this layer
@@ -215,6 +236,7 @@ struct GemmArgs {
   // check of loop iteration check_iter (>= 0) on the entering residual, then
   // (h modes) the append of h to the cache at (layer, row_lane, row_pos)
   int row_tasks;
+  float* rec;                // delta mode: the rows' FP32 reconstructions (Workspace::hrec)
   int check_iter;
   float* norms;              // [lanes, l_max]
   int32_t* status_w;
@@ -282,6 +304,18 @@ hipError_t launch_prefill_finish(const ModelView& m, const Workspace& ws, int la
 // lane), -1 after; spec[2 kSpecRows] = n; len[lane] = pos0 + n.
 hipError_t launch_spec_accept(const ModelView& m, const Workspace& ws, int lane, int pos0, int k,
                               const float* logits, int32_t* tokens_out, hipStream_t s);
+
+// Delta mode: h' of `layer` for the positions of each of the n_rows rows'
+// lanes (0 .. row_pos[r], or 0 .. fixed_T - 1 when fixed_T > 0) into layer 0
+// of the fp16 tiled view `mat`; t_ub bounds the positions for the grid.
+hipError_t launch_delta_mat(const CacheView& c, const CacheView& mat, int layer,
+                            const int32_t* row_lane, const int32_t* row_pos,
+                            const int32_t* status, int n_rows, int t_ub, int fixed_T,
+                            hipStream_t s);
+// Delta mode: rec[i] = FP32 reconstruction of `layer` at position pos0 + i of
+// `lane`, for i < n (the state a chunk resuming at layer + 1 continues from).
+hipError_t launch_delta_rec(const CacheView& c, int layer, int lane, int pos0, int n, float* rec,
+                            hipStream_t s);
 
 // Fill lane state: len, status for lanes [l0, l0+n) and norms to NaN.
 hipError_t launch_lane_reset(const Workspace& ws, int l0, int n, int l_max, int length,

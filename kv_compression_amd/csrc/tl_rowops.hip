@@ -103,7 +103,51 @@ __global__ __launch_bounds__(kRowThreads) void norm_append_kernel(ModelView m, C
     for (int i = 0; i < EPT; ++i) ho[e0 + i] = from_f<T>(h[i]);
   }
   if (c.mode == TL_CACHE_KV) return;
-  cache_store_h<T, EPT>(c, a.layer, lane, pos, e0, h, [&](float v) { return block_max(v, red); });
+  float rl[EPT];
+  float* rec = rl;
+  if (c.mode == TL_CACHE_H_DELTA8) {
+    if (a.rec) rec = a.rec + (size_t)r * D + e0;
+    else if (a.layer >= c.n_pre) delta_prefix<EPT>(c, a.layer - 1, lane, pos, e0, rl);
+  }
+  cache_store_h<T, EPT>(c, a.layer, lane, pos, e0, h, [&](float v) { return block_max(v, red); }, rec);
+}
+
+// Delta mode: h' = fp16(FP32 prefix sum) of `layer` into layer 0 of the fp16
+// tiled view `mat`. Block (x, r): positions x * ppb .. of row r's lane; a
+// position's D elements are D / EPT consecutive threads (one contiguous read
+// of each code row, 16-byte stores).
+template <int EPT>
+__global__ __launch_bounds__(256) void delta_mat_kernel(CacheView c, CacheView mat, int layer,
+                                                        const int32_t* row_lane,
+                                                        const int32_t* row_pos,
+                                                        const int32_t* status, int fixed_T,
+                                                        int ppb) {
+  const int r = blockIdx.y;
+  const int lane = row_lane[r];
+  if (status && status[lane] == TL_LANE_ABORTED) return;
+  const int T = fixed_T > 0 ? fixed_T : row_pos[r] + 1;
+  const int tpp = c.D / EPT;
+  const int pos = blockIdx.x * ppb + (int)threadIdx.x / tpp;
+  if (pos >= T || (int)threadIdx.x >= ppb * tpp) return;
+  const int e0 = ((int)threadIdx.x % tpp) * EPT;
+  float acc[EPT];
+  delta_prefix<EPT>(c, layer, lane, pos, e0, acc);
+  half_t* dst = (half_t*)mat.code_row(0, lane, e0 / kKBlock, pos) + e0 % kKBlock;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) dst[i] = (half_t)acc[i];
+}
+
+template <int EPT>
+__global__ __launch_bounds__(256) void delta_rec_kernel(CacheView c, int layer, int lane, int pos0,
+                                                        int n, float* rec) {
+  const int tpp = c.D / EPT, ppb = 256 / tpp;
+  const int i = blockIdx.x * ppb + (int)threadIdx.x / tpp;
+  if (i >= n || (int)threadIdx.x >= ppb * tpp) return;
+  const int e0 = ((int)threadIdx.x % tpp) * EPT;
+  float acc[EPT];
+  delta_prefix<EPT>(c, layer, lane, pos0 + i, e0, acc);
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) rec[(size_t)i * c.D + e0 + k] = acc[k];
 }
 
 template <typename T, int EPT, bool CHECK>
@@ -267,6 +311,17 @@ template <typename T>
 __global__ void cache_read_kernel(ModelView m, CacheView c, int lane, int layer, int pos0,
                                   int8_t* codes, uint16_t* scales, void* hout) {
   const int r = blockIdx.x, pos = pos0 + r, D = m.D;
+  if (c.mode == TL_CACHE_H_DELTA8) {
+    for (int e = threadIdx.x; e < D; e += blockDim.x) {
+      float acc[1];
+      delta_prefix<1>(c, layer, lane, pos, e, acc);
+      if (hout) ((T*)hout)[(size_t)r * D + e] = from_f<T>(acc[0]);
+      if (layer < c.n_pre) continue;
+      if (codes) codes[(size_t)r * D + e] = c.delta_codes(layer, lane, pos)[e];
+      if (scales && e % c.dh == 0) scales[(size_t)r * c.H + e / c.dh] = c.delta_scales(layer, lane, pos)[e / c.dh];
+    }
+    return;
+  }
   if (c.mode == TL_CACHE_KV) {
     if (!hout) return;
     const T* src = (const T*)c.kv_row(layer, lane, pos);
@@ -386,6 +441,40 @@ hipError_t launch_spec_accept(const ModelView& m, const Workspace& ws, int lane,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   spec_accept_kernel<<<1, 64, 0, s>>>(ws, lane, pos0, k, tokens_out);
+  return hipGetLastError();
+}
+
+// elements per thread of the delta kernels: 8 (16-byte fp16 stores) when a
+// position's threads fit a block and 8 divides the head width
+static int delta_ept(const CacheView& c) {
+  return (c.D / 8 <= 256 && c.dh % 8 == 0) ? 8 : (c.D / 4 <= 256 && c.dh % 4 == 0) ? 4 : 0;
+}
+
+hipError_t launch_delta_mat(const CacheView& c, const CacheView& mat, int layer,
+                            const int32_t* row_lane, const int32_t* row_pos,
+                            const int32_t* status, int n_rows, int t_ub, int fixed_T,
+                            hipStream_t s) {
+  const int ept = delta_ept(c);
+  if (!ept || n_rows < 1 || t_ub < 1 || layer < 0 || layer >= c.n_layers) return hipErrorInvalidValue;
+  const int ppb = 256 / (c.D / ept);
+  const dim3 grid((t_ub + ppb - 1) / ppb, n_rows);
+  if (ept == 8)
+    delta_mat_kernel<8><<<grid, 256, 0, s>>>(c, mat, layer, row_lane, row_pos, status, fixed_T, ppb);
+  else
+    delta_mat_kernel<4><<<grid, 256, 0, s>>>(c, mat, layer, row_lane, row_pos, status, fixed_T, ppb);
+  return hipGetLastError();
+}
+
+hipError_t launch_delta_rec(const CacheView& c, int layer, int lane, int pos0, int n, float* rec,
+                            hipStream_t s) {
+  const int ept = delta_ept(c);
+  if (!ept || n < 1 || layer < c.n_pre - 1 || layer >= c.n_layers) return hipErrorInvalidValue;
+  const int ppb = 256 / (c.D / ept);
+  const int grid = (n + ppb - 1) / ppb;
+  if (ept == 8)
+    delta_rec_kernel<8><<<grid, 256, 0, s>>>(c, layer, lane, pos0, n, rec);
+  else
+    delta_rec_kernel<4><<<grid, 256, 0, s>>>(c, layer, lane, pos0, n, rec);
   return hipGetLastError();
 }
 

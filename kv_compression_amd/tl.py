@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtl.so")
 
 TL_OK, TL_E_ARG, TL_E_UNSUPPORTED, TL_E_CAPACITY, TL_E_CACHE_GAP, TL_E_HIP = range(6)
-MODES = {"kv": 0, "f32": 1, "f16": 2, "int8": 3, "int4": 4}
+MODES = {"kv": 0, "f32": 1, "f16": 2, "int8": 3, "int4": 4, "delta8": 5}
 DTYPES = {"f32": 0, "f16": 1}
 LANE_OK, LANE_ABORTED = 0, 1
 MAX_BATCH, MAX_CHUNK = 256, 512

@@ -36,11 +36,12 @@ def test_cache_bytes_match_closed_form(name):
     from kv_compression_amd import tl
     sh = synth.SHAPES[name]
     cfg = tl.make_config(sh)
-    modes = ("f32", "kv") if sh.dtype == "f32" else ("f16", "int8", "int4", "kv")
+    modes = ("f32", "kv") if sh.dtype == "f32" else ("f16", "int8", "int4", "kv", "delta8")
     for mode in modes:
         for lanes, seq, lmax in ((1, 1, 1), (4, 4224, 8), (3, 77, 32)):
-            want = looped.cache_bytes(mode, sh.d_model, sh.dtype, lanes, seq, lmax, sh.n_pre)
+            want = looped.cache_bytes(mode, sh.d_model, sh.dtype, lanes, seq, lmax, sh.n_pre,
+                                      sh.n_heads)
             assert tl.tl_cache_bytes(cfg, mode, lanes, seq, lmax) == want
     # modes a model dtype does not support have no layout
-    bad = "int4" if sh.dtype == "f32" else "f32"
-    assert tl.tl_cache_bytes(cfg, bad, 1, 16, 1) == 0
+    for bad in (("int4", "delta8") if sh.dtype == "f32" else ("f32",)):
+        assert tl.tl_cache_bytes(cfg, bad, 1, 16, 1) == 0
