@@ -190,8 +190,11 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile):
         cache.tl_profile_start()
         run(K)
         kern_ms, launches = cache.tl_profile_stop()
-        # bytes per (token, layer) entry, from the library's own cache size
+        # bytes per (token, layer) entry, from the library's own cache size;
+        # the delta mode's attention kernel streams the fp16 h' it was handed
         eb = cache.cache_bytes / ((shape.n_pre + wl.l_max) * wl.lanes * max_seq)
+        if mode == "delta8":
+            eb = 2 * shape.d_model
         t_values = [context + 1 + s for s in range(K)]
         flops, hbytes, n_launch = recon_flops_bytes(shape, eb, lanes, loops, t_values)
         assert n_launch == launches, (n_launch, launches)
@@ -294,7 +297,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--mode", default="int4", choices=["int4", "int8", "f16", "kv"])
+    ap.add_argument("--mode", default="int4", choices=["int4", "int8", "f16", "kv", "delta8"])
     ap.add_argument("--workload", default="407m-int4h-ctx4096-b4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile-pass", action="store_true")

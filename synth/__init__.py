@@ -62,7 +62,7 @@ class ModelShape:
 class Workload:
     name: str
     shape: ModelShape
-    modes: tuple        # cache modes the workload is run in ("int4", "int8", "f16", "f32", "kv")
+    modes: tuple        # cache modes the workload is run in ("int4", "int8", "f16", "f32", "kv", "delta8")
     lanes: int
     loops: tuple        # per-lane loop counts (cycled over lanes)
     l_max: int
@@ -100,7 +100,7 @@ WORKLOADS: Dict[str, Workload] = {
                                   1024, False, 0, 128, _INF),
     # the headline: 4 lanes x 4096-token prompts, 128 greedy steps, INT4-h
     "407m-int4h-ctx4096-b4": Workload("407m-int4h-ctx4096-b4", SHAPES["407m"],
-                                      ("int4", "int8", "f16", "kv"), 4, (8,), 8,
+                                      ("int4", "int8", "f16", "kv", "delta8"), 4, (8,), 8,
                                       4096, False, 0, 128, _INF),
     # 48 lanes at loops [4, 16, 32] on one 34-layer cache, 2048-token prompts, 64 steps
     "2b-int4h-laware-b48": Workload("2b-int4h-laware-b48", SHAPES["2b"], ("int4",), 48,
