@@ -125,10 +125,12 @@ def cpu_baseline(shape, w, mode, context, loops, budget_s=12.0, max_steps=8):
                       "(%.1f s)" % (steps, context, mode, L, dt)}
 
 
-def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile):
+def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, order="explicit"):
     """Prefill the workload's lanes in `mode`, time K decode steps after W
     warm-up steps (inputs resident in HBM), then, if `profile`, time the
     attention kernel alone over another K steps with HIP events on its stream.
+    `order`: the decode attention's evaluation order ("explicit" rebuilds K/V
+    on MFMA; "absorbed" attends over h' with W_k^T q and applies W_v after).
     Returns (tok/s, wall s, roofline, extra, prefill s, cache bytes)."""
     lanes = list(range(wl.lanes))
     loops = wl.lane_loops()
@@ -145,6 +147,8 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile):
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - tp0
     log("prefill %.2f s" % prefill_s)
+    if order != "explicit":
+        cache.tl_cache_set_attention(order)
     n_layers = shape.n_pre + max(loops)
 
     ta = torch.empty(wl.lanes, dtype=torch.int32, device="cuda")
@@ -199,8 +203,17 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile):
         flops, hbytes, n_launch = recon_flops_bytes(shape, eb, lanes, loops, t_values)
         assert n_launch == launches, (n_launch, launches)
         avg_ms = kern_ms / launches
-        traffic = load_traffic(wl.name, mode)
-        if mode == "kv":
+        traffic = load_traffic(wl.name, mode) if order == "explicit" else None
+        if order == "absorbed":
+            # HBM-bound: the h entries, plus per row W_k^T q in and the
+            # weighted sums r out (H x D fp32 each)
+            rows_bytes = sum(len([L for L in loops if shape.n_pre + L > layer])
+                             for _ in t_values for layer in range(n_layers)) * 2 * shape.n_heads * shape.d_model * 4
+            abytes = hbytes + rows_bytes
+            achieved = abytes / (kern_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+        elif mode == "kv":
             achieved = hbytes / (kern_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
@@ -208,14 +221,14 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile):
             achieved = flops / (kern_ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": traffic}
-        extra = {"kernel": "recon_attn" if mode != "kv" else "kv_attn",
+        extra = {"kernel": ("absorbed_attn" if order == "absorbed" else "recon_attn") if mode != "kv" else "kv_attn",
                  "kernel_avg_us": round(avg_ms * 1e3, 2), "kernel_launches": launches,
                  "kernel_share_of_step": round(kern_ms / gpu_ms, 3),
                  "flops_per_launch": flops / launches,
                  "h_bytes_per_launch": hbytes / launches,
                  "h_stream_GBs": round(hbytes / (kern_ms * 1e-3) / 1e9, 1)}
         log("%s kernel: %d launches, avg %.1f us, %s" % (mode, launches, avg_ms * 1e3, roof))
-    if profile:
+    if profile and order == "explicit":
         # the prefill's causal attention kernel over one lane's prompt, timed
         # alone: algorithmic work sum over positions of (keys seen) * 4 * D
         # flops per layer on fp32 MFMA
@@ -332,6 +345,16 @@ def main():
     value, wall, roof, extra, prefill_s, kv_bytes = measure_mode(
         torch, tl, model, wl, shape, args.mode, prompts, K, W, not args.no_profile_pass)
 
+    # the absorbed evaluation order of the same decode (attention over h'
+    # with W_k^T q, W_v applied to the weighted sums)
+    absorbed = None
+    if not args.headline_only and args.mode in ("int4", "int8", "f16", "delta8"):
+        va, wa, ra, xa, _, _ = measure_mode(torch, tl, model, wl, shape, args.mode, prompts, K,
+                                            W, True, order="absorbed")
+        absorbed = {"decode_tok_s": round(va, 2), "ms_per_step": round(wa * 1e3 / K, 4),
+                    "attention_kernel": xa.get("kernel"), "kernel_avg_us": xa.get("kernel_avg_us"),
+                    "roofline": ra}
+
     # warm start mid-loop on one lane of the workload: prefill at L/2 keeping
     # the residuals, deepen to L from them, against a fresh prefill at L
     resume = spec = None
@@ -411,6 +434,7 @@ def main():
         "cpu_baseline": cpu,
         "extra": extra,
         "modes": modes,
+        "absorbed_order": absorbed,
         "warm_start": resume,
         "speculative": spec,
     }

@@ -233,6 +233,24 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
 tl_status tl_spec_step(tl_cache* c, int lane, int draft_loops, int verify_loops, int draft_ahead,
                        const int32_t* d_token_in, int32_t* d_tokens_out, int* n_out, void* stream);
 
+/* Evaluation order of the decode attention over a store-h cache.
+ * EXPLICIT (default): K = W_k h' and V = W_v h' are rebuilt on MFMA for every
+ * position, then attended (features page, "Store-h KV cache").
+ * ABSORBED: the same attention with the products reassociated (the
+ * novel-contributions page relates store-h to MLA): head h scores position j
+ * as (W_k,h^T q_h) . h'_j and outputs W_v,h (sum_j p_j h'_j), so all heads
+ * attend over the shared rows h' and no K or V is formed; 4*H*D instead of
+ * 4*D^2 flops per position. Rounding differs from EXPLICIT (the sums are
+ * taken in another order), within the same tolerance of the exact result.
+ * Prefill and speculative verification keep the explicit order. */
+typedef enum { TL_ATTN_EXPLICIT = 0, TL_ATTN_ABSORBED = 1 } tl_attn_order;
+
+/* Choose the decode attention's evaluation order for later tl_decode_step
+ * calls on `c`. Errors: TL_E_ARG (unknown order), TL_E_UNSUPPORTED (ABSORBED
+ * covers fp16 models with d_model 1024 and 16 heads of 64, and the h cache
+ * modes; stored-K/V caches have no h to absorb into). */
+tl_status tl_cache_set_attention(tl_cache* c, int order);
+
 /* Residual norms of `lane`'s last decode step, one per loop iteration
  * (NaN for iterations that did not run). h_out: host float [l_max].
  * Synchronises `stream`. */

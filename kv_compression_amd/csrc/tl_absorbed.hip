@@ -1,0 +1,408 @@
+// Absorbed evaluation order of store-h decode attention (novel-contributions
+// page, "Novel Mechanism: Store-h KV Cache", which relates store-h to MLA).
+//
+// With K = W_k h' and V = W_v h', head h's score is q_h . (W_k,h h'_j) =
+// (W_k,h^T q_h) . h'_j and its output is W_v,h (sum_j p_j h'_j). So every head
+// attends over the same D-wide rows h'_j (multi-query attention with head
+// width D) with the query qt_h = W_k,h^T q_h, and W_v,h is applied once to the
+// weighted sum r_h. Per position that is 4 H D flops instead of the 4 D^2 of
+// rebuilding K and V.
+//
+// Three kernels per layer:
+//   absorb_q_kernel        qt[row][h][c] = sum_j q[row][h d + j] W_k[h d + j][c]  (fp32)
+//   absorbed_attn_kernel   per (row, key split): the scores and the weighted sum
+//                          of h' on MFMA, written as (max, sum, r[D]) per head
+//   absorbed_merge_kernel  per (row, head, column quarter): merge the splits, r / l
+//   absorbed_o_kernel      o = W_v,h r per row and head (fp32 sums, model dtype out)
+#include <algorithm>
+
+#include "tl_device.h"
+
+namespace tl {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kAbsTP = 16;    // positions per tile
+constexpr int kAbsPad = 8;    // halfs of padding per LDS row (keeps 16-byte alignment)
+
+// qt = W_k^T q per head. Grid (D / 64, H), 64 threads: thread c of column
+// block cb holds W_k rows h d .. h d + d - 1 of column cb * 64 + c in
+// registers (all loads in flight together) and sums them against each row's
+// q, staged 64 rows at a time in LDS. The sum runs over j in order.
+template <int DH>
+__global__ __launch_bounds__(64) void absorb_q_kernel(int D, int n_rows, const float* q,
+                                                      const half_t* wk, float* qt) {
+  __shared__ float qs[64][DH];
+  const int c = blockIdx.x * 64 + threadIdx.x, h = blockIdx.y, H = gridDim.y;
+  float wr[DH];
+#pragma unroll
+  for (int j = 0; j < DH; ++j) wr[j] = (float)wk[((size_t)h * DH + j) * D + c];
+  for (int r0 = 0; r0 < n_rows; r0 += 64) {
+    const int nr = min(64, n_rows - r0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < nr * DH; e += 64)
+      qs[e / DH][e % DH] = q[(size_t)(r0 + e / DH) * D + h * DH + e % DH];
+    __syncthreads();
+    for (int u = 0; u < nr; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < DH; ++j) acc = fmaf(qs[u][j], wr[j], acc);
+      qt[((size_t)(r0 + u) * H + h) * D + c] = acc;
+    }
+  }
+}
+
+// The raw cache bytes of the 64-element block kb of one position, and their
+// dequantisation into an LDS row (fp16 h' in natural element order; zeros
+// for a position past the tile's end).
+template <int MODE> struct BlockRaw;
+template <> struct BlockRaw<TL_CACHE_H_F16> { u32x4 v[8]; };
+template <> struct BlockRaw<TL_CACHE_H_INT8> { u32x4 v[4]; uint16_t s; };
+template <> struct BlockRaw<TL_CACHE_H_INT4> { u32x4 v[2]; uint32_t s; };
+
+template <int MODE>
+__device__ __forceinline__ BlockRaw<MODE> load_block(const CacheView& c, int layer, int lane, int kb,
+                                                     int pos) {
+  BlockRaw<MODE> b;
+  const u32x4* row = (const u32x4*)c.code_row(layer, lane, kb, pos);
+  constexpr int NV = sizeof(b.v) / sizeof(u32x4);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) b.v[i] = row[i];
+  if constexpr (MODE == TL_CACHE_H_INT4) b.s = *(const uint32_t*)c.int4_scale(layer, lane, kb, pos);
+  if constexpr (MODE == TL_CACHE_H_INT8) b.s = *c.int8_scale(layer, lane, pos);
+  return b;
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_block(const BlockRaw<MODE>& b, bool valid, half_t* dst) {
+  if (!valid) {
+    half8 z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (half_t)0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(half8*)(dst + 8 * i) = z;
+    return;
+  }
+  if constexpr (MODE == TL_CACHE_H_F16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(u32x4*)(dst + 8 * i) = b.v[i];
+  } else if constexpr (MODE == TL_CACHE_H_INT4) {
+    // word g holds elements 16 (g % 4) + 8 (g / 4) .. +7; elements 32.. use the second scale
+    const half_t s0 = h_from_bits((uint16_t)(b.s & 0xFFFFu)), s1 = h_from_bits((uint16_t)(b.s >> 16));
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int base = 16 * (g & 3) + 8 * (g >> 2);
+      *(half8*)(dst + base) = int4_dequant8(b.v[g >> 2][g & 3], (g & 3) >= 2 ? s1 : s0);
+    }
+  } else {  // INT8: group g of 8 bytes holds elements 16 (g % 4) + 8 (g / 4) .. +7
+    const half_t s = h_from_bits(b.s);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int g = 2 * v + k, base = 16 * (g & 3) + 8 * (g >> 2);
+        const half4 lo = int8_dequant4(b.v[v][2 * k], s), hi = int8_dequant4(b.v[v][2 * k + 1], s);
+        const half8 e = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        *(half8*)(dst + base) = e;
+      }
+  }
+}
+
+struct AbsArgs {
+  CacheView cache;
+  int layer;
+  const int32_t* row_lane;
+  const int32_t* row_pos;
+  const int32_t* status;
+  const float* qt;       // [rows, H, D]
+  float* part;           // [rows, S, H, D + 2]
+  int S, split_len;
+};
+
+// One workgroup per (row, key split), 4 waves; wave w owns d_model columns
+// 256w .. 256w + 255 (D = 1024) of both products. Per tile of 16 positions:
+//   S^T[pos][head] = h'[pos][:] . qt[head][:]   (16x16x16 f16 MFMA, A = h' rows
+//     from LDS, B = qt held in registers as fp16 high and low halves, so the
+//     product keeps fp32 accuracy); the four waves' partial sums over their
+//     columns are added in LDS in wave order;
+//   online softmax per head (lane l holds head l % 16 at positions 4(l/16)+i);
+//   R[head][d] += P[head][pos] h'[pos][d]: the score accumulators are already
+//     the A operand (row = head, k = position), split into fp16 high and low
+//     halves; B = h' from LDS.
+template <int MODE, int D>
+__global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
+  constexpr int H = 16, TP = kAbsTP, LDR = D + kAbsPad, WC = D / 4, KS = WC / 16, NB = WC / 16;
+  static_assert(D == 1024, "one column quarter of 256 per wave");
+  __shared__ __attribute__((aligned(16))) half_t hs[TP * LDR];
+  __shared__ float sp[4][256];
+  const int row = blockIdx.x / a.S, split = blockIdx.x % a.S;
+  const int lane = a.row_lane[row];
+  if (a.status[lane] == TL_LANE_ABORTED || a.row_pos[row] < 0) return;
+  const int T = a.row_pos[row] + 1;
+  const int p_lo = split * a.split_len, p_hi = min(T, p_lo + a.split_len);
+  if (p_lo >= p_hi) return;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, lq = l & 15, lg = l >> 4;
+  const int c0 = w * WC;
+  // qt as B operand: k-step s holds columns c0 + 16 s + 4 lg + i of head lq
+  half4 qh[KS], ql[KS];
+  {
+    const float* qp = a.qt + ((size_t)row * H + lq) * D + c0 + 4 * lg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float4v v = *(const float4v*)(qp + 16 * s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qh[s][i] = (half_t)v[i];
+        ql[s][i] = (half_t)(v[i] - (float)qh[s][i]);
+      }
+    }
+  }
+  float4v R[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) R[n] = float4v{0.f, 0.f, 0.f, 0.f};
+  float mx = -__builtin_inff(), lsum = 0.f;   // head lq
+  const int spos = t >> 4, skb = t & 15;      // staging: position spos of the tile, block skb
+  half_t* sdst = hs + spos * LDR + skb * 64;
+  // the thread's blocks of the next PF tiles are loaded while the current
+  // one is multiplied (positions past p_hi are clamped in and staged as zeros)
+  constexpr int PF = MODE == TL_CACHE_H_INT4 ? 4 : MODE == TL_CACHE_H_INT8 ? 2 : 1;
+  BlockRaw<MODE> ring[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+    ring[u] = load_block<MODE>(a.cache, a.layer, lane, skb, min(p_lo + u * TP + spos, p_hi - 1));
+  for (int pr = p_lo; pr < p_hi; pr += PF * TP) {
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    const int p0 = pr + u * TP;
+    if (p0 >= p_hi) break;
+    const BlockRaw<MODE> cur = ring[u];
+    if (p0 + PF * TP < p_hi)
+      ring[u] = load_block<MODE>(a.cache, a.layer, lane, skb, min(p0 + PF * TP + spos, p_hi - 1));
+    __syncthreads();   // the previous tile is no longer read
+    store_block<MODE>(cur, p0 + spos < p_hi, sdst);
+    __syncthreads();
+    // partial scores over this wave's columns, in four independent chains
+    // (k-steps s = 4 m + u go to chain u), added in chain order
+    float4v sa[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sa[u] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const half4 av = *(const half4*)(hs + lq * LDR + c0 + 16 * s + 4 * lg);
+      sa[s & 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, qh[s], sa[s & 3], 0, 0, 0);
+      sa[s & 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ql[s], sa[s & 3], 0, 0, 0);
+    }
+    const float4v st = ((sa[0] + sa[1]) + sa[2]) + sa[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sp[w][4 * l + i] = st[i];
+    __syncthreads();
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = ((sp[0][4 * l + i] + sp[1][4 * l + i]) + sp[2][4 * l + i]) + sp[3][4 * l + i];
+      if (p0 + 4 * lg + i >= p_hi) sc[i] = -__builtin_inff();
+    }
+    // online softmax of head lq over the tile's 16 positions
+    float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float mn = fmaxf(mx, cm);
+    const float corr = mx == -__builtin_inff() ? 0.f : exp2f((mx - mn) * kLog2e);
+    float pv[4], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = sc[i] == -__builtin_inff() ? 0.f : exp2f((sc[i] - mn) * kLog2e);
+      ps += pv[i];
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lsum = lsum * corr + ps;
+    mx = mn;
+    // R rows are heads 4 lg + i: their correction factors sit in lanes 4 lg + i
+    float ci[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ci[i] = __shfl(corr, 4 * lg + i, 64);
+    half4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ph[i] = (half_t)pv[i];
+      pl[i] = (half_t)(pv[i] - (float)ph[i]);
+    }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int col = c0 + 16 * n + lq;
+      half4 bv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bv[i] = hs[(4 * lg + i) * LDR + col];
+      float4v r = R[n];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] *= ci[i];
+      r = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, bv, r, 0, 0, 0);
+      R[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, bv, r, 0, 0, 0);
+    }
+  }
+  }
+  // partial of (row, split): per head [max, sum, r[0..D)]
+  float* pp = a.part + ((size_t)row * a.S + split) * H * (D + 2);
+  if (w == 0 && lg == 0) {
+    pp[(size_t)lq * (D + 2)] = mx;
+    pp[(size_t)lq * (D + 2) + 1] = lsum;
+  }
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pp[(size_t)(4 * lg + i) * (D + 2) + 2 + c0 + 16 * n + lq] = R[n][i];
+}
+
+// Merge of the key splits, one workgroup per (row, head, quarter of the
+// columns): every workgroup forms the split weights exp(m_s - M) and the
+// total L = sum_s l_s w_s in split order, then r[c] = (sum_s w_s r_s[c]) / L
+// for its 256 columns, the splits added in order (their loads issued sixteen
+// at a time). r goes to out [rows][H][D] (fp32).
+__global__ __launch_bounds__(256) void absorbed_merge_kernel(int D, int H, const int32_t* row_lane,
+                                                             const int32_t* row_pos,
+                                                             const int32_t* status,
+                                                             const float* part, int S,
+                                                             int split_len, float* out) {
+  __shared__ float ms[1024];
+  __shared__ float wgt[1024];
+  __shared__ float lsh;
+  const int q4 = blockIdx.x & 3, rh = blockIdx.x >> 2;
+  const int r = rh / H, h = rh % H;
+  if (status[row_lane[r]] == TL_LANE_ABORTED || row_pos[r] < 0) return;
+  const int T = row_pos[r] + 1;
+  const int ns = (T + split_len - 1) / split_len;
+  const size_t sstride = (size_t)H * (D + 2);
+  const float* p = part + (size_t)r * S * sstride + (size_t)h * (D + 2);
+  const int t = threadIdx.x;
+  for (int s = t; s < ns; s += 256) {
+    ms[s] = p[s * sstride];
+    wgt[s] = p[s * sstride + 1];
+  }
+  __syncthreads();
+  if (t == 0) {
+    float M = -__builtin_inff();
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ms[s]);
+    float L = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float w = exp2f((ms[s] - M) * kLog2e);
+      L = fmaf(wgt[s], w, L);
+      ms[s] = w;
+    }
+    lsh = L;
+  }
+  __syncthreads();
+  const int c = q4 * (D / 4) + t;
+  if (t >= D / 4) return;
+  const float* pc = p + 2 + c;
+  float acc = 0.f;
+  int s = 0;
+  for (; s + 16 <= ns; s += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = pc[(size_t)(s + u) * sstride];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc = fmaf(v[u], ms[s + u], acc);
+  }
+  for (; s < ns; ++s) acc = fmaf(pc[(size_t)s * sstride], ms[s], acc);
+  out[((size_t)r * H + h) * D + c] = __fdiv_rn(acc, lsh);
+}
+
+// o[row][h d + j] = W_v[h d + j][:] . r[row][h][:] in fp32, rounded to the
+// model dtype. One workgroup per (head, 4 outputs); wave w takes output
+// j0 + w for every row, lane l columns 16 l .. 16 l + 15 (D = 1024), the lanes
+// added in a fixed butterfly order.
+__global__ __launch_bounds__(256) void absorbed_o_kernel(int D, int H, int dh, int n_rows,
+                                                         const int32_t* row_lane,
+                                                         const int32_t* row_pos,
+                                                         const int32_t* status, const float* rbuf,
+                                                         const half_t* wv, half_t* out) {
+  const int h = blockIdx.x / (dh / 4), j = (blockIdx.x % (dh / 4)) * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  float wr[16];
+  {
+    const half_t* src = wv + ((size_t)h * dh + j) * D + 16 * l;
+    const half8 a0 = *(const half8*)src, a1 = *(const half8*)(src + 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wr[i] = (float)a0[i];
+      wr[8 + i] = (float)a1[i];
+    }
+  }
+  for (int r = 0; r < n_rows; ++r) {
+    if (status[row_lane[r]] == TL_LANE_ABORTED || row_pos[r] < 0) continue;
+    const float* rr = rbuf + ((size_t)r * H + h) * D + 16 * l;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      const float4v v = *(const float4v*)(rr + i);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc = fmaf(wr[i + k], v[k], acc);
+    }
+    acc = wave_sum(acc);
+    if (l == 0) out[(size_t)r * D + h * dh + j] = (half_t)acc;
+  }
+}
+
+}  // namespace
+
+bool absorbed_supported(const ModelView& m, int view_mode) {
+  return m.dtype == TL_DTYPE_F16 && m.D == 1024 && m.H == 16 && m.dh == 64 &&
+         (view_mode == TL_CACHE_H_INT4 || view_mode == TL_CACHE_H_INT8 ||
+          view_mode == TL_CACHE_H_F16);
+}
+
+int absorbed_splits(int n_rows, int t_ub, int pair_cap, int* split_len) {
+  // about 512 workgroups, at least 64 positions a split, the partials within
+  // their buffer
+  int S = (512 + n_rows - 1) / n_rows;
+  S = std::min(S, std::max(1, (t_ub + 63) / 64));
+  S = std::min(S, std::max(1, pair_cap / n_rows));
+  int len = (t_ub + S - 1) / S;
+  len = (len + kAbsTP - 1) / kAbsTP * kAbsTP;
+  *split_len = len;
+  return (t_ub + len - 1) / len;
+}
+
+hipError_t launch_absorb_q(const ModelView& m, int n_rows, const float* q, const void* w_qkv,
+                           float* qt, hipStream_t s) {
+  if (m.D % 64 || n_rows < 1 || m.dh != 64) return hipErrorInvalidValue;
+  const half_t* wk = (const half_t*)w_qkv + (size_t)m.D * m.D;
+  absorb_q_kernel<64><<<dim3(m.D / 64, m.H), 64, 0, s>>>(m.D, n_rows, q, wk, qt);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorbed_attn(const ModelView& m, const CacheView& c, int layer, int n_rows,
+                                const int32_t* row_lane, const int32_t* row_pos,
+                                const int32_t* status, const float* qt, float* part, int S,
+                                int split_len, hipStream_t s) {
+  if (!absorbed_supported(m, c.mode) || n_rows < 1 || S < 1) return hipErrorInvalidValue;
+  AbsArgs a{};
+  a.cache = c; a.layer = layer; a.row_lane = row_lane; a.row_pos = row_pos; a.status = status;
+  a.qt = qt; a.part = part; a.S = S; a.split_len = split_len;
+  const int grid = n_rows * S;
+  if (c.mode == TL_CACHE_H_INT4)
+    absorbed_attn_kernel<TL_CACHE_H_INT4, 1024><<<grid, 256, 0, s>>>(a);
+  else if (c.mode == TL_CACHE_H_INT8)
+    absorbed_attn_kernel<TL_CACHE_H_INT8, 1024><<<grid, 256, 0, s>>>(a);
+  else
+    absorbed_attn_kernel<TL_CACHE_H_F16, 1024><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorbed_out(const ModelView& m, int n_rows, const int32_t* row_lane,
+                               const int32_t* row_pos, const int32_t* status, const float* part,
+                               int S, int split_len, const void* w_qkv, float* rbuf, void* o,
+                               hipStream_t s) {
+  if (m.D != 1024 || m.dh % 4 || S > 1024 || n_rows < 1) return hipErrorInvalidValue;
+  absorbed_merge_kernel<<<n_rows * m.H * 4, 256, 0, s>>>(m.D, m.H, row_lane, row_pos, status, part,
+                                                         S, split_len, rbuf);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const half_t* wv = (const half_t*)w_qkv + (size_t)2 * m.D * m.D;
+  absorbed_o_kernel<<<m.H * (m.dh / 4), 256, 0, s>>>(m.D, m.H, m.dh, n_rows, row_lane, row_pos,
+                                                     status, rbuf, wv, (half_t*)o);
+  return hipGetLastError();
+}
+
+}  // namespace tl

@@ -40,6 +40,7 @@ struct tl_cache {
   int mode, n_lanes, max_seq, l_max, n_layers;
   CacheView cv;
   CacheView mat;                   // delta mode: the one-layer fp16 view of Workspace::hmat
+  int order = TL_ATTN_EXPLICIT;    // decode attention's evaluation order
   Workspace ws;
   std::vector<int> host_len;       // upper bound of each lane's length
   std::vector<int> layers_valid;   // layers filled for every position < length
@@ -143,9 +144,9 @@ size_t position_bytes(const tl_config* c, int mode, int l_max) {
 }
 
 struct Layout {
-  size_t off[22];
+  size_t off[24];
   size_t total;
-  int R, Bmax, S;
+  int R, Bmax, S, apair_cap;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -162,7 +163,11 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
   const size_t head_rows = std::max(L.Bmax, kSpecRows);
   const size_t ppart = (size_t)kMaxChunk * c->n_heads * 8 * (c->d_head + 2);
   const bool delta = mode == TL_CACHE_H_DELTA8;
-  const size_t sizes[22] = {
+  // the absorbed order's buffers, for the shapes and modes it covers
+  const bool absorbed = c->dtype == TL_DTYPE_F16 && c->d_model == 1024 && c->n_heads == 16 &&
+                        c->d_head == 64 && mode != TL_CACHE_KV;
+  L.apair_cap = absorbed ? std::min(1024, L.Bmax * 64) : 0;
+  const size_t sizes[24] = {
       (size_t)n_lanes * 4,                        // len
       (size_t)n_lanes * 4,                        // status
       (size_t)n_lanes * l_max * 4,                // norms
@@ -183,9 +188,11 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
       ppart * 4,                                  // ppart
       delta ? (size_t)L.R * D * 4 : 0,            // hrec
       delta ? (size_t)n_lanes * max_seq * D * 2 : 0,   // hmat
+      absorbed ? (size_t)L.Bmax * c->n_heads * D * 4 : 0,                    // qt
+      (size_t)L.apair_cap * c->n_heads * (D + 2) * 4,                       // apart
   };
   size_t o = 0;
-  for (int i = 0; i < 22; ++i) {
+  for (int i = 0; i < 24; ++i) {
     L.off[i] = o;
     o = align256(o + sizes[i]);
   }
@@ -313,6 +320,9 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   s.ppart_floats = (int)((size_t)kMaxChunk * cfg->n_heads * 8 * (cfg->d_head + 2));
   s.hrec = mode == TL_CACHE_H_DELTA8 ? (float*)(w + L.off[20]) : nullptr;
   s.hmat = mode == TL_CACHE_H_DELTA8 ? (void*)(w + L.off[21]) : nullptr;
+  s.qt = L.apair_cap ? (float*)(w + L.off[22]) : nullptr;
+  s.apart = L.apair_cap ? (float*)(w + L.off[23]) : nullptr;
+  s.apair_cap = L.apair_cap;
   v.n_pre = cfg->n_pre; v.H = cfg->n_heads; v.dh = cfg->d_head;
   if (mode == TL_CACHE_H_DELTA8) {
     v.scales = (uint16_t*)(v.base + (size_t)n_lanes * max_seq *
@@ -704,16 +714,36 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
         ra.cache = c->mat;
         ra.layer = 0;
       }
-      if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
-      TL_HIP(launch_recon_attn(mv, ra, s));
-      split_len = recon_split_len(mv, ra.cache.mode);
+      if (c->order == TL_ATTN_ABSORBED) {
+        // absorbed order: qt = W_k^T q, attention over h' itself, o = W_v r
+        TL_HIP(launch_absorb_q(mv, rows, ws.q, W.w_qkv, ws.qt, s));
+        int sl = 0;
+        const int S = absorbed_splits(rows, t_ub, ws.apair_cap, &sl);
+        if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
+        TL_HIP(launch_absorbed_attn(mv, ra.cache, ra.layer, rows, ws.row_lane, ws.row_pos, ws.status,
+                                    ws.qt, ws.apart, S, sl, s));
+        if (c->prof_on) {
+          TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
+          c->prof_used += 2;
+        }
+        // (the merged r reuses the qt rows, which the attention kernel has consumed)
+        TL_HIP(launch_absorbed_out(mv, rows, ws.row_lane, ws.row_pos, ws.status, ws.apart, S, sl,
+                                   W.w_qkv, ws.qt, ws.o, s));
+        split_len = 0;
+      } else {
+        if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
+        TL_HIP(launch_recon_attn(mv, ra, s));
+        split_len = recon_split_len(mv, ra.cache.mode);
+      }
     }
-    if (c->prof_on) {
-      TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
-      c->prof_used += 2;
+    if (split_len) {
+      if (c->prof_on) {
+        TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
+        c->prof_used += 2;
+      }
+      TL_HIP(launch_attn_merge(mv, rows, ws.row_lane, ws.row_pos, ws.status, ws.part, ws.S, split_len,
+                               ws.o, s));
     }
-    TL_HIP(launch_attn_merge(mv, rows, ws.row_lane, ws.row_pos, ws.status, ws.part, ws.S, split_len,
-                             ws.o, s));
     GemmArgs go = gemm_args(W.w_o, D, ws.o, D, rows, D, D, EPI_ADD_F32, ws.x, D);
     go.row_lane = ws.row_lane; go.status = ws.status; go.row_dead = ws.row_dead;
     TL_HIP(launch_gemm(mv, go, s));
@@ -798,6 +828,18 @@ tl_status tl_spec_step(tl_cache* c, int lane, int draft_loops, int verify_loops,
     c->host_len[lane] = pos0 + got;
   }
   *n_out = got;
+  return TL_OK;
+}
+
+tl_status tl_cache_set_attention(tl_cache* c, int order) {
+  if (!c) return fail(TL_E_ARG, "null cache");
+  if (order != TL_ATTN_EXPLICIT && order != TL_ATTN_ABSORBED) return fail(TL_E_ARG, "unknown order %d", order);
+  if (order == TL_ATTN_ABSORBED) {
+    const int view = c->mode == TL_CACHE_H_DELTA8 ? TL_CACHE_H_F16 : c->mode;
+    if (!c->ws.apair_cap || !absorbed_supported(c->m->mv, view))
+      return fail(TL_E_UNSUPPORTED, "absorbed order covers fp16 models with d_model 1024, 16 heads of 64, h caches");
+  }
+  c->order = order;
   return TL_OK;
 }
 

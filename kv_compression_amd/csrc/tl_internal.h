@@ -108,6 +108,9 @@ struct Workspace {
   void* kvbuf;         // [max_seq, 2D] f32 (prefill K/V rebuilt from h)
   float* hrec;         // [R, D]   delta mode: each row's FP32 reconstruction of the last layer written
   void* hmat;          // delta mode: one layer's h' of every lane, fp16 tiled (a one-layer H_F16 cache)
+  float* qt;           // [Bmax, H, D] absorbed order: W_k,h^T q per row and head
+  float* apart;        // [apair_cap, H, D + 2] absorbed order: per (row, split) partials
+  int apair_cap;
   float* ppart;        // [kMaxChunk * H * 8 * (d + 2)] prefill key-split partials
   int ppart_floats;
   int32_t* spec;       // speculative round: [0, kSpecRows) input token then drafts,
@@ -316,6 +319,27 @@ hipError_t launch_delta_mat(const CacheView& c, const CacheView& mat, int layer,
 // `lane`, for i < n (the state a chunk resuming at layer + 1 continues from).
 hipError_t launch_delta_rec(const CacheView& c, int layer, int lane, int pos0, int n, float* rec,
                             hipStream_t s);
+
+// Absorbed evaluation order (decode). Covered: fp16 models with D 1024,
+// 16 heads of 64, the h view in INT4, INT8 or fp16.
+bool absorbed_supported(const ModelView& m, int view_mode);
+// key splits and their length (a multiple of 16) for n_rows rows of up to
+// t_ub positions, at most pair_cap (row, split) partials
+int absorbed_splits(int n_rows, int t_ub, int pair_cap, int* split_len);
+// qt[row][h][:] = W_k,h^T q[row][h d .. h d + d) in fp32
+hipError_t launch_absorb_q(const ModelView& m, int n_rows, const float* q, const void* w_qkv,
+                           float* qt, hipStream_t s);
+// per (row, split): per head (max, sum, r[D]) into part [rows][S][H][D + 2]
+hipError_t launch_absorbed_attn(const ModelView& m, const CacheView& c, int layer, int n_rows,
+                                const int32_t* row_lane, const int32_t* row_pos,
+                                const int32_t* status, const float* qt, float* part, int S,
+                                int split_len, hipStream_t s);
+// merge the splits into rbuf [rows][H][D] (r / l, fp32), then
+// o[row][h d + j] = W_v,h r (model dtype)
+hipError_t launch_absorbed_out(const ModelView& m, int n_rows, const int32_t* row_lane,
+                               const int32_t* row_pos, const int32_t* status, const float* part,
+                               int S, int split_len, const void* w_qkv, float* rbuf, void* o,
+                               hipStream_t s);
 
 // Fill lane state: len, status for lanes [l0, l0+n) and norms to NaN.
 hipError_t launch_lane_reset(const Workspace& ws, int l0, int n, int l_max, int length,

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libtl.so")
 TL_OK, TL_E_ARG, TL_E_UNSUPPORTED, TL_E_CAPACITY, TL_E_CACHE_GAP, TL_E_HIP = range(6)
 MODES = {"kv": 0, "f32": 1, "f16": 2, "int8": 3, "int4": 4, "delta8": 5}
 DTYPES = {"f32": 0, "f16": 1}
+ATTN_ORDERS = {"explicit": 0, "absorbed": 1}
 LANE_OK, LANE_ABORTED = 0, 1
 MAX_BATCH, MAX_CHUNK = 256, 512
 
@@ -55,7 +56,7 @@ EXPORTS = ("tl_version", "tl_last_error", "tl_model_create", "tl_model_destroy",
            "tl_prefill_chunk", "tl_decode_step", "tl_residual_norms", "tl_lane_residual",
            "tl_cache_write_h", "tl_cache_fill_synthetic", "tl_cache_set_length",
            "tl_cache_read", "tl_cache_reset_lane", "tl_profile_start", "tl_profile_stop",
-           "tl_prefill_chunk_x", "tl_extend_depth", "tl_spec_step")
+           "tl_prefill_chunk_x", "tl_extend_depth", "tl_spec_step", "tl_cache_set_attention")
 
 
 def load(path: str = LIB_PATH):
@@ -82,6 +83,7 @@ def load(path: str = LIB_PATH):
         "tl_extend_depth": (I, [P, I, I, I, I, I, P, P, P, P]),
         "tl_decode_step": (I, [P, I, P, P, P, F, P, P, P, P]),
         "tl_spec_step": (I, [P, I, I, I, I, P, P, ctypes.POINTER(I), P]),
+        "tl_cache_set_attention": (I, [P, I]),
         "tl_residual_norms": (I, [P, I, P, P]),
         "tl_lane_residual": (I, [P, I, P, P]),
         "tl_cache_write_h": (I, [P, I, I, I, I, P, P]),
@@ -231,6 +233,10 @@ class Cache:
         _check(_lib.tl_spec_step(self.handle, lane, draft_loops, verify_loops, draft_ahead,
                                  _ptr(d_token_in), _ptr(d_tokens_out), ctypes.byref(n), _stream(stream)))
         return n.value
+
+    def tl_cache_set_attention(self, order: str):
+        """order: "explicit" (rebuild K/V) or "absorbed" (W_k^T q against h')."""
+        _check(_lib.tl_cache_set_attention(self.handle, ATTN_ORDERS[order]))
 
     def tl_residual_norms(self, lane, stream=None) -> np.ndarray:
         out = np.empty(self.l_max, np.float32)
