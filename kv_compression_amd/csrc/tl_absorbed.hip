@@ -22,8 +22,7 @@ namespace tl {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kAbsTP = 16;    // positions per tile
-constexpr int kAbsPad = 8;    // halfs of padding per LDS row (keeps 16-byte alignment)
+constexpr int kAbsTP = 32;    // positions per tile of the attention kernel
 
 // qt = W_k^T q per head. Grid (D / 64, H), 64 threads: thread c of column
 // block cb holds W_k rows h d .. h d + d - 1 of column cb * 64 + c in
@@ -120,21 +119,27 @@ struct AbsArgs {
 };
 
 // One workgroup per (row, key split), 4 waves; wave w owns d_model columns
-// 256w .. 256w + 255 (D = 1024) of both products. Per tile of 16 positions:
-//   S^T[pos][head] = h'[pos][:] . qt[head][:]   (16x16x16 f16 MFMA, A = h' rows
-//     from LDS, B = qt held in registers as fp16 high and low halves, so the
-//     product keeps fp32 accuracy); the four waves' partial sums over their
-//     columns are added in LDS in wave order;
-//   online softmax per head (lane l holds head l % 16 at positions 4(l/16)+i);
-//   R[head][d] += P[head][pos] h'[pos][d]: the score accumulators are already
-//     the A operand (row = head, k = position), split into fp16 high and low
-//     halves; B = h' from LDS.
+// 256w .. 256w + 255 (D = 1024) of both products. Per tile of 32 positions:
+//   S^T[pos][head] = h'[pos][:] . qt[head][:] on v_mfma_f32_16x16x32_f16, in
+//     two blocks of 16 positions: row m of block b is position
+//     8 (m / 4) + 4 b + m % 4, so that lane l's accumulators hold positions
+//     8 (l / 16) + j (j = 4 b + i) of head l % 16. A = h' rows from LDS; B =
+//     qt held in registers as fp16 high and low halves (fp32 accuracy). The
+//     four waves' partial sums over their columns are added in LDS in wave
+//     order;
+//   online softmax per head;
+//   R[head][d] += P[head][pos] h'[pos][d]: the lane's eight weights are exactly
+//     the A operand (row = head, k = 8 (l / 16) + j); B = h' from LDS.
+// LDS row of position p starts at p * LDR + 8 ((p / 8) % 4) halves: the
+// shift keeps the weighted sum's strided B reads (rows 8 (l / 16) + j) on
+// distinct banks and every row 16-byte aligned.
 template <int MODE, int D>
 __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
-  constexpr int H = 16, TP = kAbsTP, LDR = D + kAbsPad, WC = D / 4, KS = WC / 16, NB = WC / 16;
+  constexpr int H = 16, TP = 32, LDR = D + 32, WC = D / 4, KS = WC / 32, NB = WC / 16;
   static_assert(D == 1024, "one column quarter of 256 per wave");
   __shared__ __attribute__((aligned(16))) half_t hs[TP * LDR];
-  __shared__ float sp[4][256];
+  __shared__ float sp[4][512];
+  auto row_of = [](int p) { return p * LDR + 8 * ((p >> 3) & 3); };
   const int row = blockIdx.x / a.S, split = blockIdx.x % a.S;
   const int lane = a.row_lane[row];
   if (a.status[lane] == TL_LANE_ABORTED || a.row_pos[row] < 0) return;
@@ -143,17 +148,19 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
   if (p_lo >= p_hi) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lq = l & 15, lg = l >> 4;
   const int c0 = w * WC;
-  // qt as B operand: k-step s holds columns c0 + 16 s + 4 lg + i of head lq
-  half4 qh[KS], ql[KS];
+  // qt as B operand: k-step s holds columns c0 + 32 s + 8 lg + j of head lq
+  half8 qh[KS], ql[KS];
   {
-    const float* qp = a.qt + ((size_t)row * H + lq) * D + c0 + 4 * lg;
+    const float* qp = a.qt + ((size_t)row * H + lq) * D + c0 + 8 * lg;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const float4v v = *(const float4v*)(qp + 16 * s);
+      const float4v v0 = *(const float4v*)(qp + 32 * s), v1 = *(const float4v*)(qp + 32 * s + 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qh[s][i] = (half_t)v[i];
-        ql[s][i] = (half_t)(v[i] - (float)qh[s][i]);
+        qh[s][i] = (half_t)v0[i];
+        ql[s][i] = (half_t)(v0[i] - (float)qh[s][i]);
+        qh[s][4 + i] = (half_t)v1[i];
+        ql[s][4 + i] = (half_t)(v1[i] - (float)qh[s][4 + i]);
       }
     }
   }
@@ -161,58 +168,83 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
 #pragma unroll
   for (int n = 0; n < NB; ++n) R[n] = float4v{0.f, 0.f, 0.f, 0.f};
   float mx = -__builtin_inff(), lsum = 0.f;   // head lq
-  const int spos = t >> 4, skb = t & 15;      // staging: position spos of the tile, block skb
-  half_t* sdst = hs + spos * LDR + skb * 64;
+  // staging: thread t dequantises block t % 16 of positions t / 16 and t / 16 + 16
+  const int spos = t >> 4, skb = t & 15;
+  half_t* sdst0 = hs + row_of(spos) + skb * 64;
+  half_t* sdst1 = hs + row_of(spos + 16) + skb * 64;
   // the thread's blocks of the next PF tiles are loaded while the current
   // one is multiplied (positions past p_hi are clamped in and staged as zeros)
-  constexpr int PF = MODE == TL_CACHE_H_INT4 ? 4 : MODE == TL_CACHE_H_INT8 ? 2 : 1;
-  BlockRaw<MODE> ring[PF];
+  constexpr int PF = MODE == TL_CACHE_H_INT4 ? 2 : 1;
+  BlockRaw<MODE> ring[PF][2];
 #pragma unroll
   for (int u = 0; u < PF; ++u)
-    ring[u] = load_block<MODE>(a.cache, a.layer, lane, skb, min(p_lo + u * TP + spos, p_hi - 1));
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      ring[u][h2] = load_block<MODE>(a.cache, a.layer, lane, skb, min(p_lo + u * TP + 16 * h2 + spos, p_hi - 1));
   for (int pr = p_lo; pr < p_hi; pr += PF * TP) {
 #pragma unroll
   for (int u = 0; u < PF; ++u) {
     const int p0 = pr + u * TP;
     if (p0 >= p_hi) break;
-    const BlockRaw<MODE> cur = ring[u];
-    if (p0 + PF * TP < p_hi)
-      ring[u] = load_block<MODE>(a.cache, a.layer, lane, skb, min(p0 + PF * TP + spos, p_hi - 1));
+    const BlockRaw<MODE> cur0 = ring[u][0], cur1 = ring[u][1];
+    if (p0 + PF * TP < p_hi) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        ring[u][h2] = load_block<MODE>(a.cache, a.layer, lane, skb, min(p0 + PF * TP + 16 * h2 + spos, p_hi - 1));
+    }
     __syncthreads();   // the previous tile is no longer read
-    store_block<MODE>(cur, p0 + spos < p_hi, sdst);
+    store_block<MODE>(cur0, p0 + spos < p_hi, sdst0);
+    store_block<MODE>(cur1, p0 + 16 + spos < p_hi, sdst1);
     __syncthreads();
-    // partial scores over this wave's columns, in four independent chains
-    // (k-steps s = 4 m + u go to chain u), added in chain order
-    float4v sa[4];
+    // partial scores over this wave's columns: block b in two chains
+    // (even and odd k-steps), added chain 0 then chain 1
+    float4v sa[2][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sa[u] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const half4 av = *(const half4*)(hs + lq * LDR + c0 + 16 * s + 4 * lg);
-      sa[s & 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, qh[s], sa[s & 3], 0, 0, 0);
-      sa[s & 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ql[s], sa[s & 3], 0, 0, 0);
+    for (int b = 0; b < 2; ++b) {
+      sa[b][0] = float4v{0.f, 0.f, 0.f, 0.f};
+      sa[b][1] = float4v{0.f, 0.f, 0.f, 0.f};
     }
-    const float4v st = ((sa[0] + sa[1]) + sa[2]) + sa[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sp[w][4 * l + i] = st[i];
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int prow = 8 * (lq >> 2) + 4 * b + (lq & 3);
+        const half8 av = *(const half8*)(hs + row_of(prow) + c0 + 32 * s + 8 * lg);
+        sa[b][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qh[s], sa[b][s & 1], 0, 0, 0);
+        sa[b][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ql[s], sa[b][s & 1], 0, 0, 0);
+      }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float4v st = sa[b][0] + sa[b][1];
+      *(float4v*)&sp[w][256 * b + 4 * l] = st;
+    }
     __syncthreads();
-    float sc[4];
+    // lane l: positions 8 lg + j of head lq (j = 4 b + i)
+    float sc[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = ((sp[0][4 * l + i] + sp[1][4 * l + i]) + sp[2][4 * l + i]) + sp[3][4 * l + i];
-      if (p0 + 4 * lg + i >= p_hi) sc[i] = -__builtin_inff();
+    for (int b = 0; b < 2; ++b) {
+      const float4v s0 = *(const float4v*)&sp[0][256 * b + 4 * l], s1 = *(const float4v*)&sp[1][256 * b + 4 * l];
+      const float4v s2 = *(const float4v*)&sp[2][256 * b + 4 * l], s3 = *(const float4v*)&sp[3][256 * b + 4 * l];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = ((s0[i] + s1[i]) + s2[i]) + s3[i];
+        if (p0 + 8 * lg + 4 * b + i >= p_hi) v = -__builtin_inff();
+        sc[4 * b + i] = v;
+      }
     }
-    // online softmax of head lq over the tile's 16 positions
-    float cm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    // online softmax of head lq over the tile's 32 positions
+    float cm = sc[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
     cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
     cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
     const float mn = fmaxf(mx, cm);
     const float corr = mx == -__builtin_inff() ? 0.f : exp2f((mx - mn) * kLog2e);
-    float pv[4], ps = 0.f;
+    float pv[8], ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = sc[i] == -__builtin_inff() ? 0.f : exp2f((sc[i] - mn) * kLog2e);
-      ps += pv[i];
+    for (int j = 0; j < 8; ++j) {
+      pv[j] = sc[j] == -__builtin_inff() ? 0.f : exp2f((sc[j] - mn) * kLog2e);
+      ps += pv[j];
     }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
@@ -222,23 +254,22 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
     float ci[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ci[i] = __shfl(corr, 4 * lg + i, 64);
-    half4 ph, pl;
+    half8 ph;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ph[i] = (half_t)pv[i];
-      pl[i] = (half_t)(pv[i] - (float)ph[i]);
-    }
+    for (int j = 0; j < 8; ++j) ph[j] = (half_t)pv[j];
+    int brow[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) brow[j] = row_of(8 * lg + j);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int col = c0 + 16 * n + lq;
-      half4 bv;
+      half8 bv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bv[i] = hs[(4 * lg + i) * LDR + col];
+      for (int j = 0; j < 8; ++j) bv[j] = hs[brow[j] + col];
       float4v r = R[n];
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] *= ci[i];
-      r = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, bv, r, 0, 0, 0);
-      R[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, bv, r, 0, 0, 0);
+      R[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bv, r, 0, 0, 0);
     }
   }
   }
