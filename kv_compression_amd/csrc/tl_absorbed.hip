@@ -27,7 +27,9 @@ constexpr int kAbsTP = 32;    // positions per tile of the attention kernel
 // qt = W_k^T q per head. Grid (D / 64, H), 64 threads: thread c of column
 // block cb holds W_k rows h d .. h d + d - 1 of column cb * 64 + c in
 // registers (all loads in flight together) and sums them against each row's
-// q, staged 64 rows at a time in LDS. The sum runs over j in order.
+// q, staged 64 rows at a time in LDS. The sum runs over j in order. The
+// result is written in the attention kernel's operand order (D = 1024, 16
+// heads): per row 4 waves x 8 k-steps x 64 lanes x (8 high, 8 low) halves.
 template <int DH>
 __global__ __launch_bounds__(64) void absorb_q_kernel(int D, int n_rows, const float* q,
                                                       const half_t* wk, float* qt) {
@@ -46,7 +48,14 @@ __global__ __launch_bounds__(64) void absorb_q_kernel(int D, int n_rows, const f
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < DH; ++j) acc = fmaf(qs[u][j], wr[j], acc);
-      qt[((size_t)(r0 + u) * H + h) * D + c] = acc;
+      // stored as the attention kernel's B fragments: column c of head h is
+      // element e = c % 8 of lane 16 ((c / 8) % 4) + h in k-step (c % 256) / 32 of
+      // wave c / 256, as an fp16 high half and the fp16 rest
+      const half_t hi = (half_t)acc, lo = (half_t)(acc - (float)hi);
+      const int wv = c >> 8, ks = (c & 255) >> 5, ln = 16 * ((c >> 3) & 3) + h, e = c & 7;
+      half_t* f = (half_t*)qt + ((((size_t)(r0 + u) * 4 + wv) * 8 + ks) * 64 + ln) * 16;
+      f[e] = hi;
+      f[8 + e] = lo;
     }
   }
 }
@@ -130,16 +139,19 @@ struct AbsArgs {
 //   online softmax per head;
 //   R[head][d] += P[head][pos] h'[pos][d]: the lane's eight weights are exactly
 //     the A operand (row = head, k = 8 (l / 16) + j); B = h' from LDS.
-// LDS row of position p starts at p * LDR + 8 ((p / 8) % 4) halves: the
-// shift keeps the weighted sum's strided B reads (rows 8 (l / 16) + j) on
-// distinct banks and every row 16-byte aligned.
+// LDS row of position p starts at p * LDR + 8 ((p / 8) % 4) halves and its
+// 64-element blocks are 72 halves apart: the row shift keeps the weighted
+// sum's strided B reads (rows 8 (l / 16) + j) on distinct banks, the block
+// padding the staging writes (one block per lane), and every 8-element run
+// stays 16-byte aligned.
 template <int MODE, int D>
 __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
-  constexpr int H = 16, TP = 32, LDR = D + 32, WC = D / 4, KS = WC / 32, NB = WC / 16;
+  constexpr int H = 16, TP = 32, BS = 72, LDR = D / 64 * BS + 32, WC = D / 4, KS = WC / 32, NB = WC / 16;
   static_assert(D == 1024, "one column quarter of 256 per wave");
   __shared__ __attribute__((aligned(16))) half_t hs[TP * LDR];
   __shared__ float sp[4][512];
   auto row_of = [](int p) { return p * LDR + 8 * ((p >> 3) & 3); };
+  auto col_of = [](int k) { return (k >> 6) * BS + (k & 63); };
   const int row = blockIdx.x / a.S, split = blockIdx.x % a.S;
   const int lane = a.row_lane[row];
   if (a.status[lane] == TL_LANE_ABORTED || a.row_pos[row] < 0) return;
@@ -148,20 +160,15 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
   if (p_lo >= p_hi) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lq = l & 15, lg = l >> 4;
   const int c0 = w * WC;
-  // qt as B operand: k-step s holds columns c0 + 32 s + 8 lg + j of head lq
+  // qt as B operand: k-step s holds columns c0 + 32 s + 8 lg + j of head lq,
+  // stored in this order by absorb_q_kernel (one contiguous 32 bytes per lane)
   half8 qh[KS], ql[KS];
   {
-    const float* qp = a.qt + ((size_t)row * H + lq) * D + c0 + 8 * lg;
+    const half8* qp = (const half8*)a.qt + (((size_t)row * 4 + w) * KS * 64 + l) * 2;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const float4v v0 = *(const float4v*)(qp + 32 * s), v1 = *(const float4v*)(qp + 32 * s + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qh[s][i] = (half_t)v0[i];
-        ql[s][i] = (half_t)(v0[i] - (float)qh[s][i]);
-        qh[s][4 + i] = (half_t)v1[i];
-        ql[s][4 + i] = (half_t)(v1[i] - (float)qh[s][4 + i]);
-      }
+      qh[s] = qp[s * 128];
+      ql[s] = qp[s * 128 + 1];
     }
   }
   float4v R[NB];
@@ -170,8 +177,8 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
   float mx = -__builtin_inff(), lsum = 0.f;   // head lq
   // staging: thread t dequantises block t % 16 of positions t / 16 and t / 16 + 16
   const int spos = t >> 4, skb = t & 15;
-  half_t* sdst0 = hs + row_of(spos) + skb * 64;
-  half_t* sdst1 = hs + row_of(spos + 16) + skb * 64;
+  half_t* sdst0 = hs + row_of(spos) + skb * BS;
+  half_t* sdst1 = hs + row_of(spos + 16) + skb * BS;
   // the thread's blocks of the next PF tiles are loaded while the current
   // one is multiplied (positions past p_hi are clamped in and staged as zeros)
   constexpr int PF = MODE == TL_CACHE_H_INT4 ? 2 : 1;
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int prow = 8 * (lq >> 2) + 4 * b + (lq & 3);
-        const half8 av = *(const half8*)(hs + row_of(prow) + c0 + 32 * s + 8 * lg);
+        const half8 av = *(const half8*)(hs + row_of(prow) + col_of(c0 + 32 * s + 8 * lg));
         sa[b][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qh[s], sa[b][s & 1], 0, 0, 0);
         sa[b][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ql[s], sa[b][s & 1], 0, 0, 0);
       }
@@ -262,7 +269,7 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
     for (int j = 0; j < 8; ++j) brow[j] = row_of(8 * lg + j);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const int col = c0 + 16 * n + lq;
+      const int col = col_of(c0 + 16 * n + lq);
       half8 bv;
 #pragma unroll
       for (int j = 0; j < 8; ++j) bv[j] = hs[brow[j] + col];
