@@ -311,6 +311,8 @@ def main():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--mode", default="int4", choices=["int4", "int8", "f16", "kv", "delta8"])
+    ap.add_argument("--order", default="explicit", choices=["explicit", "absorbed"],
+                    help="decode attention order of the headline measurement (absorbed: for profiling that path)")
     ap.add_argument("--workload", default="407m-int4h-ctx4096-b4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile-pass", action="store_true")
@@ -343,12 +345,13 @@ def main():
     prompts = synth.make_prompts(shape.vocab, wl.lanes, context, wl.seed_prompt)
 
     value, wall, roof, extra, prefill_s, kv_bytes = measure_mode(
-        torch, tl, model, wl, shape, args.mode, prompts, K, W, not args.no_profile_pass)
+        torch, tl, model, wl, shape, args.mode, prompts, K, W, not args.no_profile_pass,
+        order=args.order)
 
     # the absorbed evaluation order of the same decode (attention over h'
     # with W_k^T q, W_v applied to the weighted sums)
     absorbed = None
-    if not args.headline_only and args.mode in ("int4", "int8", "f16", "delta8"):
+    if not args.headline_only and args.order == "explicit" and args.mode in ("int4", "int8", "f16", "delta8"):
         va, wa, ra, xa, _, _ = measure_mode(torch, tl, model, wl, shape, args.mode, prompts, K,
                                             W, True, order="absorbed")
         absorbed = {"decode_tok_s": round(va, 2), "ms_per_step": round(wa * 1e3 / K, 4),
@@ -427,6 +430,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": wl.name, "model_shape": shape.name, "cache_mode": args.mode,
+                   "attention_order": args.order,
                    "lanes": wl.lanes, "loops": loops[0] if len(set(loops)) == 1 else loops,
                    "context": context, "decode_steps": K,
                    "kv_bytes": kv_bytes, "prefill_s": round(prefill_s, 3)},
