@@ -481,6 +481,8 @@ tl_status run_chunk(tl_cache* c, int lane, int pos0, int n, int layer_begin, int
   TL_HIP(launch_prefill_setup(mv, ws, lane, n, d_x_in ? nullptr : d_tokens, pos0, s));
   if (d_x_in) TL_HIP(launch_copy_f32(d_x_in, ws.x, (size_t)n * D, s));
   const bool delta = c->mode == TL_CACHE_H_DELTA8;
+  // chunks of 64 tokens or more run their products on the LDS-tiled kernel
+  const int tiled = n >= 64 ? 1 : 0;
   // delta mode, resuming mid-loop: the rows' reconstruction of the layer below
   if (delta && layer_begin > 0)
     TL_HIP(launch_delta_rec(c->cv, layer_begin - 1, lane, pos0, n, ws.hrec, s));
@@ -501,6 +503,7 @@ tl_status run_chunk(tl_cache* c, int lane, int pos0, int n, int layer_begin, int
     } else {
       GemmArgs g = gemm_args(W.w_qkv, D, ws.h, D, n, D, D, EPI_STORE_F32, ws.q, D);
       g.scale = qscale; g.row_lane = ws.row_lane; g.status = ws.status; g.row_dead = ws.row_dead;
+      g.tiled = tiled;
       TL_HIP(launch_gemm(mv, g, s));
       if (delta) {
         // h' of this layer for positions 0 .. T-1, then the fp16-h reconstruction
@@ -527,14 +530,14 @@ tl_status run_chunk(tl_cache* c, int lane, int pos0, int n, int layer_begin, int
       c->prof_used += 2;
     }
     GemmArgs go = gemm_args(W.w_o, D, ws.o, D, n, D, D, EPI_ADD_F32, ws.x, D);
-    go.row_lane = ws.row_lane; go.status = ws.status; go.row_dead = ws.row_dead;
+    go.row_lane = ws.row_lane; go.status = ws.status; go.row_dead = ws.row_dead; go.tiled = tiled;
     TL_HIP(launch_gemm(mv, go, s));
     TL_HIP(launch_rmsnorm(mv, n, ws.x, W.norm2, ws.u, ws.row_lane, ws.status, s));
     GemmArgs gu = gemm_args(W.w_up, D, ws.u, D, n, mv.F, D, EPI_GELU_T, ws.a, mv.F);
-    gu.row_lane = ws.row_lane; gu.status = ws.status; gu.row_dead = ws.row_dead;
+    gu.row_lane = ws.row_lane; gu.status = ws.status; gu.row_dead = ws.row_dead; gu.tiled = tiled;
     TL_HIP(launch_gemm(mv, gu, s));
     GemmArgs gd = gemm_args(W.w_down, mv.F, ws.a, mv.F, n, D, mv.F, EPI_ADD_F32, ws.x, D);
-    gd.row_lane = ws.row_lane; gd.status = ws.status; gd.row_dead = ws.row_dead;
+    gd.row_lane = ws.row_lane; gd.status = ws.status; gd.row_dead = ws.row_dead; gd.tiled = tiled;
     TL_HIP(launch_gemm(mv, gd, s));
   }
   if (d_x_out) TL_HIP(launch_copy_f32(ws.x, d_x_out, (size_t)n * D, s));

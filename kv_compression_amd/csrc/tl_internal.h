@@ -229,6 +229,7 @@ struct GemmArgs {
   int fixed_lane, pos0;
   int f_offset;              // EPI_QKV: global feature index = f + f_offset
   int fb;                    // output features per workgroup: 16, 8 or 4 (set by launch_gemm)
+  int tiled;                 // a prefill chunk's product: LDS-tiled MFMA kernel where it applies
   // nullable: 1 when the row's lane has stopped (read instead of status by
   // the products of at most 16 rows; the attention input's safety check sets it)
   int32_t* row_dead;
