@@ -144,7 +144,7 @@ size_t position_bytes(const tl_config* c, int mode, int l_max) {
 }
 
 struct Layout {
-  size_t off[24];
+  size_t off[26];
   size_t total;
   int R, Bmax, S, apair_cap;
 };
@@ -167,7 +167,7 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
   const bool absorbed = c->dtype == TL_DTYPE_F16 && c->d_model == 1024 && c->n_heads == 16 &&
                         c->d_head == 64 && mode != TL_CACHE_KV;
   L.apair_cap = absorbed ? std::min(1024, L.Bmax * 64) : 0;
-  const size_t sizes[24] = {
+  const size_t sizes[26] = {
       (size_t)n_lanes * 4,                        // len
       (size_t)n_lanes * 4,                        // status
       (size_t)n_lanes * l_max * 4,                // norms
@@ -190,9 +190,11 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
       delta ? (size_t)n_lanes * max_seq * D * 2 : 0,   // hmat
       absorbed ? (size_t)L.Bmax * c->n_heads * D * 4 : 0,                    // qt
       (size_t)L.apair_cap * c->n_heads * (D + 2) * 4,                       // apart
+      (size_t)L.Bmax * kArgChunks * 4,            // amax_v
+      (size_t)L.Bmax * kArgChunks * 4,            // amax_i
   };
   size_t o = 0;
-  for (int i = 0; i < 24; ++i) {
+  for (int i = 0; i < 26; ++i) {
     L.off[i] = o;
     o = align256(o + sizes[i]);
   }
@@ -323,6 +325,8 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   s.qt = L.apair_cap ? (float*)(w + L.off[22]) : nullptr;
   s.apart = L.apair_cap ? (float*)(w + L.off[23]) : nullptr;
   s.apair_cap = L.apair_cap;
+  s.amax_v = (float*)(w + L.off[24]);
+  s.amax_i = (int32_t*)(w + L.off[25]);
   v.n_pre = cfg->n_pre; v.H = cfg->n_heads; v.dh = cfg->d_head;
   if (mode == TL_CACHE_H_DELTA8) {
     v.scales = (uint16_t*)(v.base + (size_t)n_lanes * max_seq *

@@ -17,6 +17,7 @@ constexpr int kInt4Group = 32;        // INT4-h scale group along d_model
 constexpr int kKvSplit = 32;          // positions per split in the stored-K/V attention
 constexpr int kSpecMax = 15;          // drafted tokens per speculative round
 constexpr int kSpecRows = 16;         // verification rows of a round (kSpecMax + 1)
+constexpr int kArgChunks = 32;        // chunks of the decode argmax over the vocabulary
 
 typedef _Float16 half_t;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -108,6 +109,8 @@ struct Workspace {
   void* kvbuf;         // [max_seq, 2D] f32 (prefill K/V rebuilt from h)
   float* hrec;         // [R, D]   delta mode: each row's FP32 reconstruction of the last layer written
   void* hmat;          // delta mode: one layer's h' of every lane, fp16 tiled (a one-layer H_F16 cache)
+  float* amax_v;       // [Bmax, kArgChunks] decode argmax: each chunk's best logit
+  int32_t* amax_i;     // [Bmax, kArgChunks] and its index
   float* qt;           // [Bmax, H, D] absorbed order: W_k,h^T q per row and head
   float* apart;        // [apair_cap, H, D + 2] absorbed order: per (row, split) partials
   int apair_cap;
@@ -292,7 +295,8 @@ hipError_t launch_prefill_attn(const ModelView& m, int n, int pos0, const float*
                                const int32_t* status, float* part, int part_floats,
                                const int32_t* row_lane, const int32_t* row_pos, hipStream_t s);
 
-// Per decode row: argmax of logits (lowest index on ties) -> tokens_out[slot],
+// Per decode row: argmax of logits (lowest index on ties; chunk partials,
+// then their merge) -> tokens_out[slot],
 // lane_status[slot]; len[lane] += 1 unless aborted; xres[lane] = x[row].
 hipError_t launch_finish(const ModelView& m, const Workspace& ws, int n, const float* logits,
                          int ld_logits, int logits_by_slot, int32_t* tokens_out,

@@ -226,6 +226,39 @@ __device__ int block_argmax(const float* lg, int V) {
   return ib == 0x7fffffff ? 0 : ib;
 }
 
+// Argmax of the logits in 32 chunks per row, one workgroup per (row, chunk):
+// the chunk's (value, index) under the lowest-index-on-ties order. The
+// merge of the chunks in finish_kernel gives the same token as one scan.
+__global__ __launch_bounds__(kRowThreads) void argmax_part_kernel(ModelView m, Workspace ws,
+                                                                  const float* logits, int ld,
+                                                                  int by_slot) {
+  __shared__ float sv[kRowThreads / 64];
+  __shared__ int si[kRowThreads / 64];
+  const int r = blockIdx.x / kArgChunks, c = blockIdx.x % kArgChunks;
+  const int slot = ws.row_slot[r];
+  const float* lg = logits + (size_t)(by_slot ? slot : r) * ld;
+  const int ch = (m.V + kArgChunks - 1) / kArgChunks;
+  const int lo = c * ch, hi = min(m.V, lo + ch);
+  float best = -__builtin_inff();
+  int bi = 0x7fffffff;
+  for (int j = lo + threadIdx.x; j < hi; j += blockDim.x) argmax_merge(best, bi, lg[j], j);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(best, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    argmax_merge(best, bi, v2, i2);
+  }
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = sv[0];
+    int ib = si[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_merge(b, ib, sv[w], si[w]);
+    ws.amax_v[r * kArgChunks + c] = b;
+    ws.amax_i[r * kArgChunks + c] = ib;
+  }
+}
+
 __global__ __launch_bounds__(kRowThreads) void finish_kernel(ModelView m, Workspace ws,
                                                              const float* logits, int ld,
                                                              int by_slot, int32_t* tokens_out,
@@ -244,8 +277,12 @@ __global__ __launch_bounds__(kRowThreads) void finish_kernel(ModelView m, Worksp
         ws.xres[(size_t)lane * m.D + i] = ws.x[(size_t)r * m.D + i];
     return;
   }
-  const float* lg = logits + (size_t)(by_slot ? slot : r) * ld;
-  const int tok = block_argmax(lg, m.V);
+  // the chunks' (value, index) pairs, merged in chunk order
+  float b = ws.amax_v[r * kArgChunks];
+  int ib = ws.amax_i[r * kArgChunks];
+  for (int c = 1; c < kArgChunks; ++c) argmax_merge(b, ib, ws.amax_v[r * kArgChunks + c], ws.amax_i[r * kArgChunks + c]);
+  const int tok = ib == 0x7fffffff ? 0 : ib;
+  (void)logits; (void)ld; (void)by_slot;
   for (int i = threadIdx.x; i < m.D; i += blockDim.x)
     ws.xres[(size_t)lane * m.D + i] = ws.x[(size_t)r * m.D + i];
   if (threadIdx.x == 0) {
@@ -423,6 +460,9 @@ hipError_t launch_rmsnorm(const ModelView& m, int n, const float* x, const void*
 hipError_t launch_finish(const ModelView& m, const Workspace& ws, int n, const float* logits,
                          int ld_logits, int logits_by_slot, int32_t* tokens_out,
                          int32_t* lane_status, float* user_logits, hipStream_t s) {
+  argmax_part_kernel<<<n * kArgChunks, kRowThreads, 0, s>>>(m, ws, logits, ld_logits, logits_by_slot);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   finish_kernel<<<n, kRowThreads, 0, s>>>(m, ws, logits, ld_logits, logits_by_slot, tokens_out,
                                           lane_status, user_logits);
   return hipGetLastError();
