@@ -138,7 +138,6 @@ def test_absorbed_refused_where_not_covered():
         c.tl_cache_set_attention("absorbed")
     assert e.value.status == tl.TL_E_UNSUPPORTED
     c.tl_cache_set_attention("explicit")
-    with pytest.raises(tl.TLError) as e:
-        tl.load().tl_cache_set_attention
-        tl._check(tl._lib.tl_cache_set_attention(c.handle, 7))
+    with pytest.raises(tl.TLError) as e:           # an order that does not exist
+        tl._check(tl.load().tl_cache_set_attention(c.handle, 7))
     assert e.value.status == tl.TL_E_ARG
