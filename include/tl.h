@@ -247,8 +247,8 @@ typedef enum { TL_ATTN_EXPLICIT = 0, TL_ATTN_ABSORBED = 1 } tl_attn_order;
 
 /* Choose the decode attention's evaluation order for later tl_decode_step
  * calls on `c`. Errors: TL_E_ARG (unknown order), TL_E_UNSUPPORTED (ABSORBED
- * covers fp16 models with d_model 1024 and 16 heads of 64, and the h cache
- * modes; stored-K/V caches have no h to absorb into). */
+ * covers fp16 models with 16 heads of 64 at d_model 1024 or of 128 at 2048,
+ * and the h cache modes; stored-K/V caches have no h to absorb into). */
 tl_status tl_cache_set_attention(tl_cache* c, int order);
 
 /* Residual norms of `lane`'s last decode step, one per loop iteration

@@ -28,8 +28,8 @@ constexpr int kAbsTP = 32;    // positions per tile of the attention kernel
 // block cb holds W_k rows h d .. h d + d - 1 of column cb * 64 + c in
 // registers (all loads in flight together) and sums them against each row's
 // q, staged 64 rows at a time in LDS. The sum runs over j in order. The
-// result is written in the attention kernel's operand order (D = 1024, 16
-// heads): per row 4 waves x 8 k-steps x 64 lanes x (8 high, 8 low) halves.
+// result is written in the attention kernel's operand order (16 heads): per
+// row 4 waves x D / 128 k-steps x 64 lanes x (8 high, 8 low) halves.
 template <int DH>
 __global__ __launch_bounds__(64) void absorb_q_kernel(int D, int n_rows, const float* q,
                                                       const half_t* wk, float* qt) {
@@ -52,8 +52,9 @@ __global__ __launch_bounds__(64) void absorb_q_kernel(int D, int n_rows, const f
       // element e = c % 8 of lane 16 ((c / 8) % 4) + h in k-step (c % 256) / 32 of
       // wave c / 256, as an fp16 high half and the fp16 rest
       const half_t hi = (half_t)acc, lo = (half_t)(acc - (float)hi);
-      const int wv = c >> 8, ks = (c & 255) >> 5, ln = 16 * ((c >> 3) & 3) + h, e = c & 7;
-      half_t* f = (half_t*)qt + ((((size_t)(r0 + u) * 4 + wv) * 8 + ks) * 64 + ln) * 16;
+      const int wc = D / 4, nks = wc / 32;
+      const int wv = c / wc, ks = (c % wc) >> 5, ln = 16 * ((c >> 3) & 3) + h, e = c & 7;
+      half_t* f = (half_t*)qt + ((((size_t)(r0 + u) * 4 + wv) * nks + ks) * 64 + ln) * 16;
       f[e] = hi;
       f[8 + e] = lo;
     }
@@ -128,7 +129,7 @@ struct AbsArgs {
 };
 
 // One workgroup per (row, key split), 4 waves; wave w owns d_model columns
-// 256w .. 256w + 255 (D = 1024) of both products. Per tile of 32 positions:
+// w D / 4 .. (w + 1) D / 4 - 1 (D = 1024 or 2048) of both products. Per tile of 32 positions:
 //   S^T[pos][head] = h'[pos][:] . qt[head][:] on v_mfma_f32_16x16x32_f16, in
 //     two blocks of 16 positions: row m of block b is position
 //     8 (m / 4) + 4 b + m % 4, so that lane l's accumulators hold positions
@@ -147,7 +148,7 @@ struct AbsArgs {
 template <int MODE, int D>
 __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
   constexpr int H = 16, TP = 32, BS = 72, LDR = D / 64 * BS + 32, WC = D / 4, KS = WC / 32, NB = WC / 16;
-  static_assert(D == 1024, "one column quarter of 256 per wave");
+  static_assert(D == 1024 || D == 2048, "a quarter of d_model per wave");
   __shared__ __attribute__((aligned(16))) half_t hs[TP * LDR];
   __shared__ float sp[4][512];
   auto row_of = [](int p) { return p * LDR + 8 * ((p >> 3) & 3); };
@@ -175,33 +176,56 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
 #pragma unroll
   for (int n = 0; n < NB; ++n) R[n] = float4v{0.f, 0.f, 0.f, 0.f};
   float mx = -__builtin_inff(), lsum = 0.f;   // head lq
-  // staging: thread t dequantises block t % 16 of positions t / 16 and t / 16 + 16
+  // staging: thread t dequantises blocks t % 16 + 16 b (b < D / 1024) of
+  // positions t / 16 and t / 16 + 16; staged block s is position
+  // spos + 16 (s % 2), block skb + 16 (s / 2)
+  constexpr int NS = 2 * (D / 1024);
   const int spos = t >> 4, skb = t & 15;
-  half_t* sdst0 = hs + row_of(spos) + skb * BS;
-  half_t* sdst1 = hs + row_of(spos + 16) + skb * BS;
+  half_t* sdst[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) sdst[q] = hs + row_of(spos + 16 * (q & 1)) + (skb + 16 * (q >> 1)) * BS;
   // the thread's blocks of the next PF tiles are loaded while the current
   // one is multiplied (positions past p_hi are clamped in and staged as zeros)
-  constexpr int PF = MODE == TL_CACHE_H_INT4 ? 2 : 1;
-  BlockRaw<MODE> ring[PF][2];
+  // (at D = 2048 the INT8 and fp16 blocks are loaded right before they are
+  // staged: the operands of both products leave no registers for a ring)
+  constexpr bool DIRECT = D == 2048 && MODE != TL_CACHE_H_INT4;
+  constexpr int PF = MODE == TL_CACHE_H_INT4 && D == 1024 ? 2 : 1;
+  BlockRaw<MODE> ring[DIRECT ? 1 : PF][DIRECT ? 1 : NS];
+  if constexpr (!DIRECT) {
 #pragma unroll
-  for (int u = 0; u < PF; ++u)
+    for (int u = 0; u < PF; ++u)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-      ring[u][h2] = load_block<MODE>(a.cache, a.layer, lane, skb, min(p_lo + u * TP + 16 * h2 + spos, p_hi - 1));
+      for (int q = 0; q < NS; ++q)
+        ring[u][q] = load_block<MODE>(a.cache, a.layer, lane, skb + 16 * (q >> 1),
+                                      min(p_lo + u * TP + 16 * (q & 1) + spos, p_hi - 1));
+  }
   for (int pr = p_lo; pr < p_hi; pr += PF * TP) {
 #pragma unroll
   for (int u = 0; u < PF; ++u) {
     const int p0 = pr + u * TP;
     if (p0 >= p_hi) break;
-    const BlockRaw<MODE> cur0 = ring[u][0], cur1 = ring[u][1];
-    if (p0 + PF * TP < p_hi) {
+    if constexpr (DIRECT) {
+      __syncthreads();   // the previous tile is no longer read
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-        ring[u][h2] = load_block<MODE>(a.cache, a.layer, lane, skb, min(p0 + PF * TP + 16 * h2 + spos, p_hi - 1));
+      for (int q = 0; q < NS; ++q) {
+        const BlockRaw<MODE> b1 = load_block<MODE>(a.cache, a.layer, lane, skb + 16 * (q >> 1),
+                                                   min(p0 + 16 * (q & 1) + spos, p_hi - 1));
+        store_block<MODE>(b1, p0 + 16 * (q & 1) + spos < p_hi, sdst[q]);
+      }
+    } else {
+      BlockRaw<MODE> cur[NS];
+#pragma unroll
+      for (int q = 0; q < NS; ++q) cur[q] = ring[u][q];
+      if (p0 + PF * TP < p_hi) {
+#pragma unroll
+        for (int q = 0; q < NS; ++q)
+          ring[u][q] = load_block<MODE>(a.cache, a.layer, lane, skb + 16 * (q >> 1),
+                                        min(p0 + PF * TP + 16 * (q & 1) + spos, p_hi - 1));
+      }
+      __syncthreads();   // the previous tile is no longer read
+#pragma unroll
+      for (int q = 0; q < NS; ++q) store_block<MODE>(cur[q], p0 + 16 * (q & 1) + spos < p_hi, sdst[q]);
     }
-    __syncthreads();   // the previous tile is no longer read
-    store_block<MODE>(cur0, p0 + spos < p_hi, sdst0);
-    store_block<MODE>(cur1, p0 + 16 + spos < p_hi, sdst1);
     __syncthreads();
     // partial scores over this wave's columns: block b in two chains
     // (even and odd k-steps), added chain 0 then chain 1
@@ -292,8 +316,7 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
     for (int i = 0; i < 4; ++i) pp[(size_t)(4 * lg + i) * (D + 2) + 2 + c0 + 16 * n + lq] = R[n][i];
 }
 
-// Merge of the key splits, one workgroup per (row, head, quarter of the
-// columns): every workgroup forms the split weights exp(m_s - M) and the
+// Merge of the key splits, one workgroup per (row, head, 256 columns): every workgroup forms the split weights exp(m_s - M) and the
 // total L = sum_s l_s w_s in split order, then r[c] = (sum_s w_s r_s[c]) / L
 // for its 256 columns, the splits added in order (their loads issued sixteen
 // at a time). r goes to out [rows][H][D] (fp32).
@@ -305,7 +328,7 @@ __global__ __launch_bounds__(256) void absorbed_merge_kernel(int D, int H, const
   __shared__ float ms[1024];
   __shared__ float wgt[1024];
   __shared__ float lsh;
-  const int q4 = blockIdx.x & 3, rh = blockIdx.x >> 2;
+  const int parts = D / 256, q4 = blockIdx.x % parts, rh = blockIdx.x / parts;
   const int r = rh / H, h = rh % H;
   if (status[row_lane[r]] == TL_LANE_ABORTED || row_pos[r] < 0) return;
   const int T = row_pos[r] + 1;
@@ -330,8 +353,7 @@ __global__ __launch_bounds__(256) void absorbed_merge_kernel(int D, int H, const
     lsh = L;
   }
   __syncthreads();
-  const int c = q4 * (D / 4) + t;
-  if (t >= D / 4) return;
+  const int c = q4 * 256 + t;
   const float* pc = p + 2 + c;
   float acc = 0.f;
   int s = 0;
@@ -348,31 +370,33 @@ __global__ __launch_bounds__(256) void absorbed_merge_kernel(int D, int H, const
 
 // o[row][h d + j] = W_v[h d + j][:] . r[row][h][:] in fp32, rounded to the
 // model dtype. One workgroup per (head, 4 outputs); wave w takes output
-// j0 + w for every row, lane l columns 16 l .. 16 l + 15 (D = 1024), the lanes
-// added in a fixed butterfly order.
-__global__ __launch_bounds__(256) void absorbed_o_kernel(int D, int H, int dh, int n_rows,
+// j0 + w for every row, lane l columns CPL l .. CPL l + CPL - 1 (CPL = D / 64),
+// the lanes added in a fixed butterfly order.
+template <int D>
+__global__ __launch_bounds__(256) void absorbed_o_kernel(int H, int dh, int n_rows,
                                                          const int32_t* row_lane,
                                                          const int32_t* row_pos,
                                                          const int32_t* status, const float* rbuf,
                                                          const half_t* wv, half_t* out) {
+  constexpr int CPL = D / 64;
   const int h = blockIdx.x / (dh / 4), j = (blockIdx.x % (dh / 4)) * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
-  float wr[16];
+  float wr[CPL];
   {
-    const half_t* src = wv + ((size_t)h * dh + j) * D + 16 * l;
-    const half8 a0 = *(const half8*)src, a1 = *(const half8*)(src + 8);
+    const half_t* src = wv + ((size_t)h * dh + j) * D + CPL * l;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      wr[i] = (float)a0[i];
-      wr[8 + i] = (float)a1[i];
+    for (int k = 0; k < CPL; k += 8) {
+      const half8 a0 = *(const half8*)(src + k);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wr[k + i] = (float)a0[i];
     }
   }
   for (int r = 0; r < n_rows; ++r) {
     if (status[row_lane[r]] == TL_LANE_ABORTED || row_pos[r] < 0) continue;
-    const float* rr = rbuf + ((size_t)r * H + h) * D + 16 * l;
+    const float* rr = rbuf + ((size_t)r * H + h) * D + CPL * l;
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; i += 4) {
+    for (int i = 0; i < CPL; i += 4) {
       const float4v v = *(const float4v*)(rr + i);
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc = fmaf(wr[i + k], v[k], acc);
@@ -385,9 +409,10 @@ __global__ __launch_bounds__(256) void absorbed_o_kernel(int D, int H, int dh, i
 }  // namespace
 
 bool absorbed_supported(const ModelView& m, int view_mode) {
-  return m.dtype == TL_DTYPE_F16 && m.D == 1024 && m.H == 16 && m.dh == 64 &&
-         (view_mode == TL_CACHE_H_INT4 || view_mode == TL_CACHE_H_INT8 ||
-          view_mode == TL_CACHE_H_F16);
+  const bool shape = m.dtype == TL_DTYPE_F16 && m.H == 16 &&
+                     ((m.D == 1024 && m.dh == 64) || (m.D == 2048 && m.dh == 128));
+  return shape && (view_mode == TL_CACHE_H_INT4 || view_mode == TL_CACHE_H_INT8 ||
+                   view_mode == TL_CACHE_H_F16);
 }
 
 int absorbed_splits(int n_rows, int t_ub, int pair_cap, int* split_len) {
@@ -404,9 +429,12 @@ int absorbed_splits(int n_rows, int t_ub, int pair_cap, int* split_len) {
 
 hipError_t launch_absorb_q(const ModelView& m, int n_rows, const float* q, const void* w_qkv,
                            float* qt, hipStream_t s) {
-  if (m.D % 64 || n_rows < 1 || m.dh != 64) return hipErrorInvalidValue;
+  if (m.D % 128 || n_rows < 1) return hipErrorInvalidValue;
   const half_t* wk = (const half_t*)w_qkv + (size_t)m.D * m.D;
-  absorb_q_kernel<64><<<dim3(m.D / 64, m.H), 64, 0, s>>>(m.D, n_rows, q, wk, qt);
+  const dim3 grid(m.D / 64, m.H);
+  if (m.dh == 64) absorb_q_kernel<64><<<grid, 64, 0, s>>>(m.D, n_rows, q, wk, qt);
+  else if (m.dh == 128) absorb_q_kernel<128><<<grid, 64, 0, s>>>(m.D, n_rows, q, wk, qt);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -419,12 +447,15 @@ hipError_t launch_absorbed_attn(const ModelView& m, const CacheView& c, int laye
   a.cache = c; a.layer = layer; a.row_lane = row_lane; a.row_pos = row_pos; a.status = status;
   a.qt = qt; a.part = part; a.S = S; a.split_len = split_len;
   const int grid = n_rows * S;
-  if (c.mode == TL_CACHE_H_INT4)
-    absorbed_attn_kernel<TL_CACHE_H_INT4, 1024><<<grid, 256, 0, s>>>(a);
-  else if (c.mode == TL_CACHE_H_INT8)
-    absorbed_attn_kernel<TL_CACHE_H_INT8, 1024><<<grid, 256, 0, s>>>(a);
-  else
-    absorbed_attn_kernel<TL_CACHE_H_F16, 1024><<<grid, 256, 0, s>>>(a);
+#define TL_ABS(D_)                                                                              \
+  do {                                                                                          \
+    if (c.mode == TL_CACHE_H_INT4) absorbed_attn_kernel<TL_CACHE_H_INT4, D_><<<grid, 256, 0, s>>>(a); \
+    else if (c.mode == TL_CACHE_H_INT8) absorbed_attn_kernel<TL_CACHE_H_INT8, D_><<<grid, 256, 0, s>>>(a); \
+    else absorbed_attn_kernel<TL_CACHE_H_F16, D_><<<grid, 256, 0, s>>>(a);                     \
+  } while (0)
+  if (m.D == 1024) TL_ABS(1024);
+  else TL_ABS(2048);
+#undef TL_ABS
   return hipGetLastError();
 }
 
@@ -432,14 +463,17 @@ hipError_t launch_absorbed_out(const ModelView& m, int n_rows, const int32_t* ro
                                const int32_t* row_pos, const int32_t* status, const float* part,
                                int S, int split_len, const void* w_qkv, float* rbuf, void* o,
                                hipStream_t s) {
-  if (m.D != 1024 || m.dh % 4 || S > 1024 || n_rows < 1) return hipErrorInvalidValue;
-  absorbed_merge_kernel<<<n_rows * m.H * 4, 256, 0, s>>>(m.D, m.H, row_lane, row_pos, status, part,
-                                                         S, split_len, rbuf);
+  if ((m.D != 1024 && m.D != 2048) || m.dh % 4 || S > 1024 || n_rows < 1) return hipErrorInvalidValue;
+  absorbed_merge_kernel<<<n_rows * m.H * (m.D / 256), 256, 0, s>>>(m.D, m.H, row_lane, row_pos, status,
+                                                                  part, S, split_len, rbuf);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const half_t* wv = (const half_t*)w_qkv + (size_t)2 * m.D * m.D;
-  absorbed_o_kernel<<<m.H * (m.dh / 4), 256, 0, s>>>(m.D, m.H, m.dh, n_rows, row_lane, row_pos,
-                                                     status, rbuf, wv, (half_t*)o);
+  const int grid = m.H * (m.dh / 4);
+  if (m.D == 1024)
+    absorbed_o_kernel<1024><<<grid, 256, 0, s>>>(m.H, m.dh, n_rows, row_lane, row_pos, status, rbuf, wv, (half_t*)o);
+  else
+    absorbed_o_kernel<2048><<<grid, 256, 0, s>>>(m.H, m.dh, n_rows, row_lane, row_pos, status, rbuf, wv, (half_t*)o);
   return hipGetLastError();
 }
 

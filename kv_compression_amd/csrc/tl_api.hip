@@ -164,8 +164,8 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
   const size_t ppart = (size_t)kMaxChunk * c->n_heads * 8 * (c->d_head + 2);
   const bool delta = mode == TL_CACHE_H_DELTA8;
   // the absorbed order's buffers, for the shapes and modes it covers
-  const bool absorbed = c->dtype == TL_DTYPE_F16 && c->d_model == 1024 && c->n_heads == 16 &&
-                        c->d_head == 64 && mode != TL_CACHE_KV;
+  const bool absorbed = c->dtype == TL_DTYPE_F16 && c->n_heads == 16 && mode != TL_CACHE_KV &&
+                        ((c->d_model == 1024 && c->d_head == 64) || (c->d_model == 2048 && c->d_head == 128));
   L.apair_cap = absorbed ? std::min(1024, L.Bmax * 64) : 0;
   const size_t sizes[26] = {
       (size_t)n_lanes * 4,                        // len
@@ -844,7 +844,7 @@ tl_status tl_cache_set_attention(tl_cache* c, int order) {
   if (order == TL_ATTN_ABSORBED) {
     const int view = c->mode == TL_CACHE_H_DELTA8 ? TL_CACHE_H_F16 : c->mode;
     if (!c->ws.apair_cap || !absorbed_supported(c->m->mv, view))
-      return fail(TL_E_UNSUPPORTED, "absorbed order covers fp16 models with d_model 1024, 16 heads of 64, h caches");
+      return fail(TL_E_UNSUPPORTED, "absorbed order covers fp16 models with 16 heads of 64 (d_model 1024) or 128 (2048), h caches");
   }
   c->order = order;
   return TL_OK;
