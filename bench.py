@@ -305,6 +305,54 @@ def measure_spec(torch, tl, rc, shape, context, L, t0, draft=2, ahead=4, rounds=
     return out
 
 
+def measure_laware(torch, tl, steps=8, warmup=1):
+    """The 2B L-aware batch (48 lanes, loops [4, 16, 32] on one 34-layer INT4-h
+    cache, 2048 synthetic prior positions in every layer a lane uses) decoded
+    in both attention orders: tokens/s of the batch and the attention kernel's
+    average launch time."""
+    import synth
+    wl = synth.workload("2b-int4h-laware-b48")
+    sh, ctx = wl.shape, wl.context
+    loops = wl.lane_loops()
+    log("L-aware 2B batch: weights")
+    model = tl.Model(sh, tl.upload_weights(sh, synth.make_weights(sh, wl.seed_weights)))
+    cache = tl.Cache(model, "int4", wl.lanes, ctx + steps + warmup + 2, wl.l_max)
+    for k in range(wl.lanes):
+        for layer in range(sh.n_pre + loops[k]):
+            cache.tl_cache_fill_synthetic(k, layer, 0, ctx, wl.seed_prior)
+    lanes = list(range(wl.lanes))
+    tin = torch.tensor(synth.make_prompts(sh.vocab, wl.lanes, 1, wl.seed_prompt)[:, 0].astype(np.int32),
+                       device="cuda")
+    tout = torch.empty_like(tin)
+    st = torch.empty_like(tin)
+    out = {"workload": wl.name, "lanes": wl.lanes, "loops": sorted(set(loops)), "context": ctx}
+    for order in ("explicit", "absorbed"):
+        cache.tl_cache_set_attention(order)
+        for k in range(wl.lanes):
+            cache.tl_cache_set_length(k, ctx, sh.n_pre + loops[k])
+        a, b = tin.clone(), tout
+        for _ in range(warmup):
+            cache.tl_decode_step(lanes, loops, a, wl.threshold, b, None, st)
+            a, b = b, a
+        torch.cuda.synchronize()
+        cache.tl_profile_start()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            cache.tl_decode_step(lanes, loops, a, wl.threshold, b, None, st)
+            a, b = b, a
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms, launches = cache.tl_profile_stop()
+        assert np.all(st.cpu().numpy() == 0)
+        out[order] = {"decode_tok_s": round(wl.lanes * steps / wall, 1),
+                      "ms_per_step": round(wall * 1e3 / steps, 3),
+                      "attention_kernel_avg_us": round(kern_ms * 1e3 / launches, 2)}
+        log("L-aware 2B %s: %.1f tok/s, %.2f ms/step" % (order, wl.lanes * steps / wall, wall * 1e3 / steps))
+    del cache, model
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +436,10 @@ def main():
         spec = measure_spec(torch, tl, rc, shape, context, L, int(nxt.cpu()[0]))
         del rc
 
+    laware = None
+    if not args.headline_only:
+        laware = measure_laware(torch, tl)
+
     # the other cache modes of the workload (fewer steps), each with its own
     # attention kernel roofline
     modes = {}
@@ -439,6 +491,7 @@ def main():
         "extra": extra,
         "modes": modes,
         "absorbed_order": absorbed,
+        "laware_2b": laware,
         "warm_start": resume,
         "speculative": spec,
     }
