@@ -347,6 +347,15 @@ def measure_laware(torch, tl, steps=8, warmup=1):
         out[order] = {"decode_tok_s": round(wl.lanes * steps / wall, 1),
                       "ms_per_step": round(wall * 1e3 / steps, 3),
                       "attention_kernel_avg_us": round(kern_ms * 1e3 / launches, 2)}
+        if order == "explicit":
+            # reconstruction + attention flops of the timed steps against the
+            # fp16 MFMA peak
+            t_values = [ctx + warmup + 1 + s for s in range(steps)]
+            flops, _, n_launch = recon_flops_bytes(sh, 0, lanes, loops, t_values)
+            assert n_launch == launches, (n_launch, launches)
+            tf = flops / (kern_ms * 1e-3) / 1e12
+            out[order]["roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP16_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(tf / PEAK_FP16_TFLOPS, 4)}
         log("L-aware 2B %s: %.1f tok/s, %.2f ms/step" % (order, wl.lanes * steps / wall, wall * 1e3 / steps))
     del cache, model
     torch.cuda.synchronize()
