@@ -205,14 +205,7 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, orde
         avg_ms = kern_ms / launches
         traffic = load_traffic(wl.name, mode) if order == "explicit" else None
         if order == "absorbed":
-            # HBM-bound: the h entries, plus per row W_k^T q in and the
-            # weighted sums r out (H x D fp32 each)
-            rows_bytes = sum(len([L for L in loops if shape.n_pre + L > layer])
-                             for _ in t_values for layer in range(n_layers)) * 2 * shape.n_heads * shape.d_model * 4
-            abytes = hbytes + rows_bytes
-            achieved = abytes / (kern_ms * 1e-3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+            roof = dict(absorbed_roofline(shape, loops, t_values, kern_ms, eb), traffic=traffic)
         elif mode == "kv":
             achieved = hbytes / (kern_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -305,18 +298,31 @@ def measure_spec(torch, tl, rc, shape, context, L, t0, draft=2, ahead=4, rounds=
     return out
 
 
-def measure_laware(torch, tl, steps=8, warmup=1):
-    """The 2B L-aware batch (48 lanes, loops [4, 16, 32] on one 34-layer INT4-h
-    cache, 2048 synthetic prior positions in every layer a lane uses) decoded
-    in both attention orders: tokens/s of the batch and the attention kernel's
-    average launch time."""
+def absorbed_roofline(shape, loops, t_values, kern_ms, entry_bytes):
+    """HBM roofline of the absorbed attention kernel over decode steps: the h
+    entries streamed plus, per row, W_k^T q in and the weighted sums r out
+    (H x D fp32 each)."""
+    _, hbytes, _ = recon_flops_bytes(shape, entry_bytes, None, loops, t_values)
+    n_layers = shape.n_pre + max(loops)
+    rows = sum(len([L for L in loops if shape.n_pre + L > layer]) for _ in t_values for layer in range(n_layers))
+    abytes = hbytes + rows * 2 * shape.n_heads * shape.d_model * 4
+    gbs = abytes / (kern_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def decode_both_orders(torch, tl, wl, loops, steps, warmup, label):
+    """A 2B INT4-h batch over wl.context synthetic prior positions in every
+    layer a lane uses, decoded in both attention orders: tokens/s, the
+    attention kernel's average launch time and its roofline (MFMA for the
+    explicit reconstruction, HBM for the absorbed order)."""
     import synth
-    wl = synth.workload("2b-int4h-laware-b48")
-    sh, ctx = wl.shape, wl.context
-    loops = wl.lane_loops()
-    log("L-aware 2B batch: weights")
+    sh, ctx, l_max = wl.shape, wl.context, max(loops)
+    log("%s: weights, %d lanes x %d positions" % (label, wl.lanes, ctx))
     model = tl.Model(sh, tl.upload_weights(sh, synth.make_weights(sh, wl.seed_weights)))
-    cache = tl.Cache(model, "int4", wl.lanes, ctx + steps + warmup + 2, wl.l_max)
+    max_seq = ctx + steps + warmup + 2
+    cache = tl.Cache(model, "int4", wl.lanes, max_seq, l_max)
+    eb = cache.cache_bytes / ((sh.n_pre + l_max) * wl.lanes * max_seq)
     for k in range(wl.lanes):
         for layer in range(sh.n_pre + loops[k]):
             cache.tl_cache_fill_synthetic(k, layer, 0, ctx, wl.seed_prior)
@@ -325,7 +331,9 @@ def measure_laware(torch, tl, steps=8, warmup=1):
                        device="cuda")
     tout = torch.empty_like(tin)
     st = torch.empty_like(tin)
-    out = {"workload": wl.name, "lanes": wl.lanes, "loops": sorted(set(loops)), "context": ctx}
+    out = {"workload": wl.name, "lanes": wl.lanes, "loops": sorted(set(loops)), "context": ctx,
+           "kv_bytes": cache.cache_bytes}
+    t_values = [ctx + warmup + 1 + s for s in range(steps)]
     for order in ("explicit", "absorbed"):
         cache.tl_cache_set_attention(order)
         for k in range(wl.lanes):
@@ -344,22 +352,41 @@ def measure_laware(torch, tl, steps=8, warmup=1):
         wall = time.perf_counter() - t0
         kern_ms, launches = cache.tl_profile_stop()
         assert np.all(st.cpu().numpy() == 0)
+        flops, _, n_launch = recon_flops_bytes(sh, eb, lanes, loops, t_values)
+        assert n_launch == launches, (n_launch, launches)
         out[order] = {"decode_tok_s": round(wl.lanes * steps / wall, 1),
                       "ms_per_step": round(wall * 1e3 / steps, 3),
                       "attention_kernel_avg_us": round(kern_ms * 1e3 / launches, 2)}
         if order == "explicit":
             # reconstruction + attention flops of the timed steps against the
             # fp16 MFMA peak
-            t_values = [ctx + warmup + 1 + s for s in range(steps)]
-            flops, _, n_launch = recon_flops_bytes(sh, 0, lanes, loops, t_values)
-            assert n_launch == launches, (n_launch, launches)
             tf = flops / (kern_ms * 1e-3) / 1e12
             out[order]["roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP16_TFLOPS,
                                       "unit": "TFLOP/s", "frac": round(tf / PEAK_FP16_TFLOPS, 4)}
-        log("L-aware 2B %s: %.1f tok/s, %.2f ms/step" % (order, wl.lanes * steps / wall, wall * 1e3 / steps))
+        else:
+            out[order]["roofline"] = absorbed_roofline(sh, loops, t_values, kern_ms, eb)
+        log("%s %s: %.1f tok/s, %.2f ms/step, %s" % (label, order, wl.lanes * steps / wall, wall * 1e3 / steps,
+                                                    out[order]["roofline"]))
     del cache, model
     torch.cuda.synchronize()
     return out
+
+
+def measure_laware(torch, tl, steps=8, warmup=1):
+    """The 2B L-aware batch: 48 lanes with loops [4, 16, 32] on one 34-layer
+    cache, 2048 positions."""
+    import synth
+    wl = synth.workload("2b-int4h-laware-b48")
+    return decode_both_orders(torch, tl, wl, wl.lane_loops(), steps, warmup, "L-aware 2B")
+
+
+def measure_long(torch, tl, steps=4, warmup=1):
+    """The 2B long-context batch: 8 lanes at L = 8 over 32768 positions in all
+    10 layers."""
+    import synth
+    wl = synth.workload("2b-int4h-ctx32k-b8")
+    L = max(wl.lane_loops())
+    return decode_both_orders(torch, tl, wl, [L] * wl.lanes, steps, warmup, "long-context 2B")
 
 
 def main():
@@ -445,9 +472,10 @@ def main():
         spec = measure_spec(torch, tl, rc, shape, context, L, int(nxt.cpu()[0]))
         del rc
 
-    laware = None
+    laware = long2b = None
     if not args.headline_only:
         laware = measure_laware(torch, tl)
+        long2b = measure_long(torch, tl)
 
     # the other cache modes of the workload (fewer steps), each with its own
     # attention kernel roofline
@@ -501,6 +529,7 @@ def main():
         "modes": modes,
         "absorbed_order": absorbed,
         "laware_2b": laware,
+        "long_context_2b": long2b,
         "warm_start": resume,
         "speculative": spec,
     }
