@@ -320,24 +320,42 @@ def decode_both_orders(torch, tl, wl, loops, steps, warmup, label):
     sh, ctx, l_max = wl.shape, wl.context, max(loops)
     log("%s: weights, %d lanes x %d positions" % (label, wl.lanes, ctx))
     model = tl.Model(sh, tl.upload_weights(sh, synth.make_weights(sh, wl.seed_weights)))
-    max_seq = ctx + steps + warmup + 2
+    max_seq = ctx + wl.chunk + steps + warmup + 2
     cache = tl.Cache(model, "int4", wl.lanes, max_seq, l_max)
     eb = cache.cache_bytes / ((sh.n_pre + l_max) * wl.lanes * max_seq)
     for k in range(wl.lanes):
         for layer in range(sh.n_pre + loops[k]):
             cache.tl_cache_fill_synthetic(k, layer, 0, ctx, wl.seed_prior)
+        cache.tl_cache_set_length(k, ctx, sh.n_pre + loops[k])
     lanes = list(range(wl.lanes))
-    tin = torch.tensor(synth.make_prompts(sh.vocab, wl.lanes, 1, wl.seed_prompt)[:, 0].astype(np.int32),
-                       device="cuda")
-    tout = torch.empty_like(tin)
-    st = torch.empty_like(tin)
     out = {"workload": wl.name, "lanes": wl.lanes, "loops": sorted(set(loops)), "context": ctx,
            "kv_bytes": cache.cache_bytes}
-    t_values = [ctx + warmup + 1 + s for s in range(steps)]
+    if wl.chunk:
+        # one prefill chunk per lane after the prior context, lane by lane
+        chunks = synth.make_prompts(sh.vocab, wl.lanes, wl.chunk, wl.seed_prompt)
+        first = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in lanes:
+            nxt, _ = cache.prefill(k, chunks[k], loops[k], chunk=wl.chunk)
+            first.append(nxt)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        out["prefill_chunk"] = {"tokens_per_lane": wl.chunk, "s": round(wall, 4),
+                                "tok_s": round(wl.lanes * wl.chunk / wall, 1)}
+        log("%s: %d-token chunk on %d lanes after %d positions in %.3f s" % (label, wl.chunk, wl.lanes, ctx, wall))
+        tin = torch.cat(first).to(torch.int32)
+    else:
+        tin = torch.tensor(synth.make_prompts(sh.vocab, wl.lanes, 1, wl.seed_prompt)[:, 0].astype(np.int32),
+                           device="cuda")
+    tout = torch.empty_like(tin)
+    st = torch.empty_like(tin)
+    start = ctx + wl.chunk
+    t_values = [start + warmup + 1 + s for s in range(steps)]
     for order in ("explicit", "absorbed"):
         cache.tl_cache_set_attention(order)
         for k in range(wl.lanes):
-            cache.tl_cache_set_length(k, ctx, sh.n_pre + loops[k])
+            cache.tl_cache_set_length(k, start, sh.n_pre + loops[k])
         a, b = tin.clone(), tout
         for _ in range(warmup):
             cache.tl_decode_step(lanes, loops, a, wl.threshold, b, None, st)
@@ -372,7 +390,7 @@ def decode_both_orders(torch, tl, wl, loops, steps, warmup, label):
     return out
 
 
-def measure_laware(torch, tl, steps=8, warmup=1):
+def measure_laware(torch, tl, steps=64, warmup=1):
     """The 2B L-aware batch: 48 lanes with loops [4, 16, 32] on one 34-layer
     cache, 2048 positions."""
     import synth
@@ -380,9 +398,9 @@ def measure_laware(torch, tl, steps=8, warmup=1):
     return decode_both_orders(torch, tl, wl, wl.lane_loops(), steps, warmup, "L-aware 2B")
 
 
-def measure_long(torch, tl, steps=4, warmup=1):
+def measure_long(torch, tl, steps=32, warmup=1):
     """The 2B long-context batch: 8 lanes at L = 8 over 32768 positions in all
-    10 layers."""
+    10 layers, one 512-token prefill chunk per lane, then the decode steps."""
     import synth
     wl = synth.workload("2b-int4h-ctx32k-b8")
     L = max(wl.lane_loops())
@@ -402,6 +420,8 @@ def main():
     ap.add_argument("--no-profile-pass", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="measure only --mode (skip the workload's other cache modes)")
+    ap.add_argument("--leg", choices=["laware_2b", "long_context_2b"],
+                    help="run only this 2B measurement and print its JSON object (for profiling it)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="end with a 64 MiB device copy (calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
     args = ap.parse_args()
@@ -418,6 +438,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     tl.load()
+    if args.leg:
+        fn = measure_laware if args.leg == "laware_2b" else measure_long
+        print(json.dumps({args.leg: fn(torch, tl)}), flush=True)
+        return
     wl = synth.workload(args.workload)
     shape = wl.shape
     loops = wl.lane_loops()
