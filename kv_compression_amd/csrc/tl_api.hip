@@ -144,7 +144,7 @@ size_t position_bytes(const tl_config* c, int mode, int l_max) {
 }
 
 struct Layout {
-  size_t off[26];
+  size_t off[27];
   size_t total;
   int R, Bmax, S, apair_cap;
 };
@@ -167,7 +167,7 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
   const bool absorbed = c->dtype == TL_DTYPE_F16 && c->n_heads == 16 && mode != TL_CACHE_KV &&
                         ((c->d_model == 1024 && c->d_head == 64) || (c->d_model == 2048 && c->d_head == 128));
   L.apair_cap = absorbed ? std::min(1024, L.Bmax * 64) : 0;
-  const size_t sizes[26] = {
+  const size_t sizes[27] = {
       (size_t)n_lanes * 4,                        // len
       (size_t)n_lanes * 4,                        // status
       (size_t)n_lanes * l_max * 4,                // norms
@@ -192,9 +192,10 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
       (size_t)L.apair_cap * c->n_heads * (D + 2) * 4,                       // apart
       (size_t)L.Bmax * kArgChunks * 4,            // amax_v
       (size_t)L.Bmax * kArgChunks * 4,            // amax_i
+      (size_t)L.Bmax * (2 * D / 128) * 4,         // tilecnt
   };
   size_t o = 0;
-  for (int i = 0; i < 26; ++i) {
+  for (int i = 0; i < 27; ++i) {
     L.off[i] = o;
     o = align256(o + sizes[i]);
   }
@@ -327,6 +328,7 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   s.apair_cap = L.apair_cap;
   s.amax_v = (float*)(w + L.off[24]);
   s.amax_i = (int32_t*)(w + L.off[25]);
+  s.tilecnt = (int32_t*)(w + L.off[26]);
   v.n_pre = cfg->n_pre; v.H = cfg->n_heads; v.dh = cfg->d_head;
   if (mode == TL_CACHE_H_DELTA8) {
     v.scales = (uint16_t*)(v.base + (size_t)n_lanes * max_seq *
@@ -342,6 +344,7 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   c->ext_from.assign(n_lanes, 0);
   c->ext_to.assign(n_lanes, 0);
   hipError_t e = launch_lane_reset(s, 0, n_lanes, l_max, 0, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_fill_i32(s.tilecnt, L.Bmax * (int)(2 * D / 128), 0, (hipStream_t)stream);
   if (e != hipSuccess) {
     delete c;
     return fail(TL_E_HIP, "lane reset: %s", hipGetErrorString(e));
@@ -738,9 +741,19 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
                                    W.w_qkv, ws.qt, ws.o, s));
         split_len = 0;
       } else {
+        // INT4 / INT8 h: the attention kernel merges its own tiles into o
+        const bool fused = combined_splits(mv, ra.cache.mode);
+        if (fused) {
+          ra.o = ws.o;
+          ra.tilecnt = ws.tilecnt;
+        }
         if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
         TL_HIP(launch_recon_attn(mv, ra, s));
-        split_len = recon_split_len(mv, ra.cache.mode);
+        split_len = fused ? 0 : recon_split_len(mv, ra.cache.mode);
+        if (fused && c->prof_on) {
+          TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
+          c->prof_used += 2;
+        }
       }
     }
     if (split_len) {

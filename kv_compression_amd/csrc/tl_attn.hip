@@ -120,63 +120,22 @@ __global__ __launch_bounds__(NT) void kv_attn_kernel(ModelView m, ReconArgs a, i
   for (int e = 0; e < EPT; ++e) dst[2 + (e0 % DH) + e] = O[e];
 }
 
-// One block of 256 threads per (row, head). Thread (dim, group g) sums the
-// splits s = g, g + G, ... for its dimension with weights exp(m_s - M), M the
-// largest split maximum, and the G group sums are added in order g = 0, 1,
-// ... . The summation order depends only on T. Each thread loads its (m, l,
-// o[dim]) of 32 / G splits at a time, the first batch together with the
-// maxima, so a merge of up to 32 splits is one memory round trip.
+// One block of 256 threads per (row, head): merge_splits over the row's
+// ceil(T / split_len) splits.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void merge_kernel(int D, int H, const int32_t* row_lane,
                                                     const int32_t* row_pos, const int32_t* status,
                                                     const float* part, int S, int split_len,
                                                     void* out) {
-  constexpr int G = 256 / DH, U = 32 / G;
+  __shared__ float osum[256];
+  __shared__ float lsum[256 / DH];
   __shared__ float red[4];
-  __shared__ float osum[G][DH];
-  __shared__ float lsum[G];
   const int r = blockIdx.x / H, head = blockIdx.x % H;
   if (status[row_lane[r]] == TL_LANE_ABORTED) return;
   const int Tn = row_pos[r] + 1;
   const int ns = (Tn + split_len - 1) / split_len;   // >= 1, <= S
-  const float* p = part + ((size_t)r * H + head) * S * (DH + 2);
-  const int t = threadIdx.x, dim = t % DH, g = t / DH;
-  float mv[U], lv[U], ov[U];
-  auto load = [&](int c) {   // splits c + g + G u (the last split stands in past ns)
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float* ps = p + (size_t)min(c + g + G * u, ns - 1) * (DH + 2);
-      mv[u] = ps[0];
-      lv[u] = ps[1];
-      ov[u] = ps[2 + dim];
-    }
-  };
-  load(0);
-  float M = -__builtin_inff();
-  for (int s = t; s < ns; s += 256) M = fmaxf(M, p[(size_t)s * (DH + 2)]);
-  M = block_max(M, red);
-  float acc = 0.f, lacc = 0.f;
-  for (int c = 0; c < ns; c += G * U) {
-    if (c) load(c);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (c + g + G * u < ns) {
-        const float w = exp2f((mv[u] - M) * kLog2e);
-        acc = fmaf(ov[u], w, acc);
-        lacc = fmaf(lv[u], w, lacc);
-      }
-  }
-  osum[g][dim] = acc;
-  if (dim == 0) lsum[g] = lacc;
-  __syncthreads();
-  if (g != 0) return;
-  float o = 0.f, L = 0.f;
-#pragma unroll
-  for (int k = 0; k < G; ++k) {
-    o += osum[k][dim];
-    L += lsum[k];
-  }
-  ((T*)out)[(size_t)r * D + head * DH + dim] = from_f<T>(__fdiv_rn(o, L));
+  merge_splits<T, DH>(part + ((size_t)r * H + head) * S * (DH + 2), ns,
+                      (T*)out + (size_t)r * D + head * DH, osum, lsum, red);
 }
 
 // Causal attention of a prefill chunk on fp32 MFMA (v_mfma_f32_16x16x4_f32).

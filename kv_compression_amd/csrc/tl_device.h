@@ -53,6 +53,65 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return s;
 }
 
+// Merge of one (row, head)'s ns >= 1 key-split partials p[s] = (max m_s, sum
+// l_s, unnormalised o_s[DH]) by a block of 256 threads: o = sum_s w_s o_s /
+// sum_s w_s l_s with w_s = exp(m_s - M), M the largest m_s. Thread (dim,
+// group g) sums the splits s = g, g + G, ... for its dimension and the G group
+// sums are added in order g = 0, 1, ..., so the result depends only on ns and
+// the partials. Each thread loads its (m, l, o[dim]) of 32 / G splits at a
+// time, the first batch together with the maxima. Scratch: osum [256],
+// lsum [G], red [4] in LDS. Every thread of the block must call it. COHERENT:
+// read the partials with device-coherent loads (written in the same launch by
+// workgroups on other XCDs with device-coherent stores).
+template <typename T, int DH, bool COHERENT = false>
+__device__ __forceinline__ void merge_splits(const float* p, int ns, T* out, float* osum,
+                                             float* lsum, float* red) {
+  constexpr int G = 256 / DH, U = 32 / G;
+  constexpr float kL2e = 1.4426950408889634f;
+  const int t = threadIdx.x, dim = t % DH, g = t / DH;
+  auto ld = [](const float* a) -> float {
+    if constexpr (COHERENT) return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *a;
+  };
+  float mv[U], lv[U], ov[U];
+  auto load = [&](int c) {   // splits c + g + G u (the last split stands in past ns)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float* ps = p + (size_t)min(c + g + G * u, ns - 1) * (DH + 2);
+      mv[u] = ld(ps);
+      lv[u] = ld(ps + 1);
+      ov[u] = ld(ps + 2 + dim);
+    }
+  };
+  load(0);
+  float M = -__builtin_inff();
+  for (int s = t; s < ns; s += 256) M = fmaxf(M, ld(p + (size_t)s * (DH + 2)));
+  M = block_max(M, red);
+  float acc = 0.f, lacc = 0.f;
+  for (int c = 0; c < ns; c += G * U) {
+    if (c) load(c);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c + g + G * u < ns) {
+        const float w = exp2f((mv[u] - M) * kL2e);
+        acc = fmaf(ov[u], w, acc);
+        lacc = fmaf(lv[u], w, lacc);
+      }
+  }
+  osum[g * DH + dim] = acc;
+  if (dim == 0) lsum[g] = lacc;
+  __syncthreads();
+  if (g == 0) {
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      o += osum[k * DH + dim];
+      L += lsum[k];
+    }
+    out[dim] = from_f<T>(__fdiv_rn(o, L));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // h codec: symmetric absmax, fp16 scale (IEEE fp32 divide, round half to even)
 // ---------------------------------------------------------------------------

@@ -116,6 +116,7 @@ struct Workspace {
   int apair_cap;
   float* ppart;        // [kMaxChunk * H * 8 * (d + 2)] prefill key-split partials
   int ppart_floats;
+  int32_t* tilecnt;    // [Bmax, 2 D / 128] decode attention: tiles done per (row, head group)
   int32_t* spec;       // speculative round: [0, kSpecRows) input token then drafts,
                        // [kSpecRows, 2 kSpecRows) verified tokens, [2 kSpecRows] count,
                        // [2 kSpecRows + 1] draft lane status
@@ -266,9 +267,16 @@ struct ReconArgs {
   const float* q;            // [rows, D] f32 (scaled)
   float* part;
   int S;                     // splits capacity per (row, head)
+  // non-null (combined_splits configurations only): the last workgroup of
+  // each (row, head group) merges the tiles into o, and no split merge follows
+  void* o;
+  int32_t* tilecnt;          // [rows, 2 D / 128] zero before the first launch
 };
 hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& a, hipStream_t s);
 int recon_split_len(const ModelView& m, int mode);
+// fp16 INT4 / INT8 h: one partial per (row, head, 256-position tile), and
+// the attention kernel can merge them itself (ReconArgs::tilecnt)
+bool combined_splits(const ModelView& m, int mode);
 
 // Prefill: rebuild K|V (fp32 accumulators, kept in fp32) for positions 0..T-1
 // into kvbuf [T, 2D].
@@ -349,6 +357,8 @@ hipError_t launch_absorbed_out(const ModelView& m, int n_rows, const int32_t* ro
 // Fill lane state: len, status for lanes [l0, l0+n) and norms to NaN.
 hipError_t launch_lane_reset(const Workspace& ws, int l0, int n, int l_max, int length,
                              hipStream_t s);
+// p[0 .. n) = v (a kernel, so that it may sit in a captured graph)
+hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);
 
 // Cache read-back (test hook).
 hipError_t launch_cache_read(const ModelView& m, const CacheView& c, int lane, int layer, int pos0,

@@ -105,6 +105,8 @@ struct KArgs {
   const float* q;
   float* part;
   int S;
+  void* o;                   // with tilecnt: merged output [rows, D]
+  int32_t* tilecnt;          // [rows, n_hg] tiles done, zero between launches
   // prefill store
   int lane, T;
   void* kvbuf;
@@ -906,8 +908,45 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) vo
         O = fmaf(c[2 + dim], e, O);
       }
       float* dst = part_of(hg * (BF / (2 * DH)) + g, ptile);
-      if (dim == 0) { dst[0] = M; dst[1] = L; }
-      dst[2 + dim] = O;
+      if (a.tilecnt) {
+        // device-coherent stores: the merging workgroup may sit on another XCD
+        if (dim == 0) {
+          __hip_atomic_store(dst, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(dst + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __hip_atomic_store(dst + 2 + dim, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        if (dim == 0) { dst[0] = M; dst[1] = L; }
+        dst[2 + dim] = O;
+      }
+    }
+    if (a.tilecnt) {
+      // The workgroup that completes a (row, head group) merges the row's
+      // tiles for those heads, exactly as the split merge would. The partials
+      // go out with device-coherent stores, which have completed (vmcnt 0)
+      // before the workgroup counts itself; the last one reads them with
+      // device-coherent loads. No cache is written back or invalidated, so
+      // the W rows and h codes other workgroups share in L2 stay there. It
+      // also zeroes the count for the next launch.
+      __shared__ int last_tile;
+      const int n_t = (Tn + BJ - 1) / BJ;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        int* cnt = a.tilecnt + r * a.n_hg + hg;
+        const int done = atomicAdd(cnt, 1) + 1;
+        last_tile = done == n_t;
+        if (done == n_t) atomicExch(cnt, 0);
+      }
+      __syncthreads();
+      if (!last_tile) return;
+      static_assert(NWV * HPW_T * (DH + 2) >= 256 + 256 / DH + 4, "merge scratch within comb_lds");
+#pragma unroll
+      for (int g = 0; g < HPW; ++g) {
+        const int head = hg * (BF / (2 * DH)) + g;
+        merge_splits<half_t, DH, true>(part_of(head, 0), n_t, (half_t*)a.o + (size_t)r * D + head * DH,
+                                       comb, comb + 256, comb + 256 + 256 / DH);
+      }
     }
   } else if constexpr (!kCross) {
     if (!wave_live) return;
@@ -1000,6 +1039,7 @@ static int recon_bj(const ModelView& m) {
 }
 
 hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t s) {
+  if (r.tilecnt && (!r.o || !combined_splits(m, r.cache.mode))) return hipErrorInvalidValue;
   const int BF = recon_bf(m, r.cache.mode);
   const int BJ = recon_bj(m);
   KArgs k{};
@@ -1017,6 +1057,8 @@ hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t
   k.q = r.q;
   k.part = r.part;
   k.S = r.S;
+  k.o = r.o;
+  k.tilecnt = r.tilecnt;
   // head groups per XCD: as many as keep their W rows within 2 MB of the
   // XCD's 4 MB L2 (the rest streams h), with the sets dividing the 8 XCDs
   const size_t hg_bytes = (size_t)BF * m.D * (m.dtype == TL_DTYPE_F32 ? 4 : 2);

@@ -343,6 +343,10 @@ __global__ void lane_reset_kernel(Workspace ws, int l0, int n, int l_max, int le
     ws.norms[(size_t)l0 * l_max + j] = __builtin_nanf("");
 }
 
+__global__ void fill_i32_kernel(int32_t* p, int n, int v) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+}
+
 // One block per (row); threads over d_model.
 template <typename T>
 __global__ void cache_read_kernel(ModelView m, CacheView c, int lane, int layer, int pos0,
@@ -522,6 +526,13 @@ hipError_t launch_lane_reset(const Workspace& ws, int l0, int n, int l_max, int 
                              hipStream_t s) {
   const int blocks = (n * l_max + 255) / 256 + 1;
   lane_reset_kernel<<<blocks < 1024 ? blocks : 1024, 256, 0, s>>>(ws, l0, n, l_max, length);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (n + 255) / 256;
+  fill_i32_kernel<<<blocks < 1024 ? blocks : 1024, 256, 0, s>>>(p, n, v);
   return hipGetLastError();
 }
 
