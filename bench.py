@@ -224,7 +224,10 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, orde
     if profile and order == "explicit":
         # the prefill's causal attention kernel over one lane's prompt, timed
         # alone: algorithmic work sum over positions of (keys seen) * 4 * D
-        # flops per layer on fp32 MFMA
+        # flops per layer. fp16 models run it on fp16 MFMA with the fp32
+        # operands split into (hi, lo) halves: three MFMA products per
+        # algorithmic one (two with stored fp16 K/V), priced against the fp16
+        # peak; the fp32 model on fp32 MFMA
         cache.tl_cache_reset_lane(0)
         torch.cuda.synchronize()
         cache.tl_profile_start()
@@ -233,12 +236,16 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, orde
         n_layers0 = shape.n_pre + loops[0]
         pa_flops = n_layers0 * 4.0 * shape.d_model * context * (context + 1) / 2.0
         pa_tf = pa_flops / (pa_ms * 1e-3) / 1e12
+        fp16 = shape.dtype == "f16"
+        pa_peak = PEAK_FP16_TFLOPS if fp16 else PEAK_FP32_MFMA_TFLOPS
+        pa_products = (2 if mode == "kv" else 3) if fp16 else 1
         extra["prefill"] = {
             "tok_s": round(wl.lanes * context / prefill_s, 1),
             "attention_kernel_avg_us": round(pa_ms * 1e3 / pa_launches, 2),
             "attention_launches": pa_launches,
-            "roofline": {"bound": "mfma", "achieved": round(pa_tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(pa_tf / PEAK_FP32_MFMA_TFLOPS, 4)}}
+            "roofline": {"bound": "mfma", "achieved": round(pa_tf, 2), "peak": pa_peak,
+                         "unit": "TFLOP/s", "frac": round(pa_tf / pa_peak, 4),
+                         "mfma_products_per_product": pa_products}}
         log("%s prefill attention: %d launches, avg %.1f us, %.1f TFLOP/s" %
             (mode, pa_launches, pa_ms * 1e3 / pa_launches, pa_tf))
     kv_bytes = cache.cache_bytes

@@ -7,6 +7,7 @@
 //  * prefill_attn: causal attention of a prefill chunk over K|V rows (chunked
 //    prefill; features page, closing list of supported techniques).
 #include <algorithm>
+#include <type_traits>
 
 #include "tl_device.h"
 
@@ -15,6 +16,9 @@ namespace tl {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// keys per LDS tile of the fp16-MFMA prefill attention (key splits are
+// multiples of it)
+constexpr int kPrefillKeyTile16 = 64;
 
 // All-reduce (sum) over aligned groups of N lanes (N = 8 or 16) with row-level
 // data-parallel moves: partners l ^ 1, l ^ 2 (quad permutations), l ^ 7
@@ -282,6 +286,271 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(ModelView m, int n, i
       out[(size_t)qi * D + head * DH + 16 * d + 4 * lg + i] = from_f<T>(__fdiv_rn(ot[d][i], lsum));
 }
 
+
+// Merge of the prefill's key splits, one thread per output element (query
+// row r, column head * DH + dim): o = sum_s w_s o_s / sum_s w_s l_s with
+// w_s = exp(m_s - M) over the row's ceil(T / split_len) splits in split
+// order, loaded 8 splits at a time. A prefill chunk has up to 512 query rows
+// and few splits per row, so one thread per element keeps the launch wide.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void merge_rows_kernel(int n_rows, int D, int H, const int32_t* row_lane,
+                                                         const int32_t* row_pos, const int32_t* status,
+                                                         const float* part, int S, int split_len,
+                                                         void* out) {
+  constexpr int U = 8;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_rows * D) return;
+  const int r = i / D, col = i % D, head = col / DH, dim = col % DH;
+  if (status[row_lane[r]] == TL_LANE_ABORTED) return;
+  const int ns = (row_pos[r] + split_len) / split_len;   // ceil((pos + 1) / split_len) >= 1
+  const float* p = part + ((size_t)r * H + head) * S * (DH + 2);
+  float M = -__builtin_inff();
+  for (int c = 0; c < ns; c += U) {
+    float mv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mv[u] = p[(size_t)min(c + u, ns - 1) * (DH + 2)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mv[u]);
+  }
+  float o = 0.f, L = 0.f;
+  for (int c = 0; c < ns; c += U) {
+    float mv[U], lv[U], ov[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float* ps = p + (size_t)min(c + u, ns - 1) * (DH + 2);
+      mv[u] = ps[0];
+      lv[u] = ps[1];
+      ov[u] = ps[2 + dim];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c + u < ns) {
+        const float w = exp2f((mv[u] - M) * kLog2e);
+        o = fmaf(ov[u], w, o);
+        L = fmaf(lv[u], w, L);
+      }
+  }
+  ((T*)out)[(size_t)r * D + col] = from_f<T>(__fdiv_rn(o, L));
+}
+
+// x = hi + lo with hi = fp16(x) and lo = fp16(x - hi) (the difference is exact
+// in fp32): the pair holds about 22 significant bits of x.
+__device__ __forceinline__ void split_half(float x, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)(x - (float)hi);
+}
+
+// Causal attention of a prefill chunk on fp16 MFMA (v_mfma_f32_16x16x32_f16).
+// The fp32 queries, and the fp32 K|V rows rebuilt from h, enter as fp16
+// (hi, lo) pairs and every product is formed as hi*hi + hi*lo + lo*hi in the
+// fp32 accumulators (the lo*lo term lies below fp32 rounding), so the scores
+// and the weighted values keep fp32 accuracy on the fp16 MFMA pipe. Stored
+// fp16 K|V rows (the stored-K/V mode) have no lo half.
+// Same work split, masking, online softmax, key splits and outputs as
+// prefill_attn_kernel: one workgroup per (key split, 64 queries, head), wave
+// w owns queries 16w .. 16w+15 and, per tile of 64 keys staged in LDS,
+//   S^T = K Q^T   (A: K rows from LDS, B: the wave's queries in registers),
+// so lane l holds S^T[key 16kb + 4*(l/16) + i][query l%16] (kb = 0 .. 3), and
+//   O^T += V^T P^T   over two 32-key k-steps,
+// where MFMA k-slot 8g + j of lane group g in k-step ks stands for key
+// 32ks + 16 (j/4) + 4g + j%4: those are keys lane group g holds scores for,
+// so P^T comes straight from the score registers. V is staged transposed
+// (each thread loads four keys of one dimension, coalesced over the
+// dimensions, and writes them as one 8-byte row piece), so each lane's A
+// operand is two 8-byte LDS reads. |K|, |V| and |q| must stay within the
+// fp16 range (below 65504); beyond it the attention is not finite.
+template <typename T, typename KT, int DH>
+__global__ __launch_bounds__(256) void prefill_attn16_kernel(ModelView m, int n, int pos0,
+                                                             const float* q, const KT* kv, T* out,
+                                                             int lane, const int32_t* status,
+                                                             float* part, int S, int split_len,
+                                                             int n_qb) {
+  constexpr bool KV_LO = std::is_same<KT, float>::value;
+  constexpr int QB = 64, KC = kPrefillKeyTile16, KB = KC / 16, NS = DH / 32, DB = DH / 16;
+  constexpr int KLD = DH + 8;                 // K row stride (halfs), 16-byte aligned
+  constexpr int VLD = KC + 8;                 // V^T row stride (halfs), 16-byte aligned
+  constexpr int C4 = KC * DH / 4 / 256;       // 4-element chunks of K (and of V) per thread
+  static_assert(KC % 32 == 0 && C4 >= 1, "key tile");
+  __shared__ __attribute__((aligned(16))) _Float16 Kh[KC * KLD];
+  __shared__ __attribute__((aligned(16))) _Float16 Kl[KV_LO ? KC * KLD : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 Vh[DH * VLD];
+  __shared__ __attribute__((aligned(16))) _Float16 Vl[KV_LO ? DH * VLD : 8];
+  if (status && status[lane] == TL_LANE_ABORTED) return;
+  const int D = m.D;
+  const int head = blockIdx.x % m.H, qb = (blockIdx.x / m.H) % n_qb, split = blockIdx.x / (m.H * n_qb);
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63, lq = l & 15, lg = l >> 4;
+  const int qi = qb * QB + wave * 16 + lq;    // this lane's query (B operand / output column)
+  const bool qv = qi < n;
+  const int qpos = pos0 + qi;
+  // Q^T as B operand: k-step s holds dims 32s + 8lg + j of query lq
+  half8 qh[NS], ql[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float* qr = q + (size_t)(qv ? qi : 0) * D + head * DH + 32 * s + 8 * lg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      _Float16 hi, lo;
+      split_half(qv ? qr[j] : 0.f, hi, lo);
+      qh[s][j] = hi;
+      ql[s][j] = lo;
+    }
+  }
+  float4v ot[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) ot[d] = float4v{0.f, 0.f, 0.f, 0.f};
+  float mx = -__builtin_inff(), lsum = 0.f;
+  const int last_q = min(n, qb * QB + QB) - 1;
+  const int k_lo = split * split_len;
+  const int kend = min(pos0 + last_q + 1, k_lo + split_len);   // keys k_lo .. kend-1
+  if (k_lo >= kend) return;
+  // Tile loads. K: chunk c = t + 256p is key c / (DH/4), dims 4 (c % (DH/4))
+  // .. +3 (one 16- or 8-byte load). V: chunk c is dim c % DH, keys
+  // 4 (c / DH) .. +3 (four loads, each coalesced over the lanes' dims).
+  float4v kr[C4], vr[C4];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < C4; ++p) {
+      const int c = t + 256 * p;
+      {
+        const int kk = c / (DH / 4), d0 = 4 * (c % (DH / 4));
+        const KT* row = kv + (size_t)min(k0 + kk, kend - 1) * 2 * D + head * DH + d0;
+        if constexpr (KV_LO) {
+          kr[p] = *(const float4v*)row;
+        } else {
+          const half4 a = *(const half4*)row;
+          kr[p] = float4v{(float)a[0], (float)a[1], (float)a[2], (float)a[3]};
+        }
+      }
+      const int d = c % DH, k4 = 4 * (c / DH);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vr[p][e] = (float)kv[(size_t)min(k0 + k4 + e, kend - 1) * 2 * D + D + head * DH + d];
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int p = 0; p < C4; ++p) {
+      const int c = t + 256 * p;
+      half4 xh, xl;
+      {
+        const int kk = c / (DH / 4), d0 = 4 * (c % (DH / 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          _Float16 hi, lo;
+          split_half(kr[p][e], hi, lo);
+          xh[e] = hi;
+          xl[e] = lo;
+        }
+        *(half4*)&Kh[kk * KLD + d0] = xh;
+        if constexpr (KV_LO) *(half4*)&Kl[kk * KLD + d0] = xl;
+      }
+      const int d = c % DH, k4 = 4 * (c / DH);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        _Float16 hi, lo;
+        split_half(vr[p][e], hi, lo);
+        xh[e] = hi;
+        xl[e] = lo;
+      }
+      *(half4*)&Vh[d * VLD + k4] = xh;
+      if constexpr (KV_LO) *(half4*)&Vl[d * VLD + k4] = xl;
+    }
+  };
+  load_tile(k_lo);
+  for (int k0 = k_lo; k0 < kend; k0 += KC) {
+    __syncthreads();   // the previous tile is no longer read
+    store_tile();
+    __syncthreads();
+    if (k0 + KC < kend) load_tile(k0 + KC);   // next tile in flight under this one
+    // S^T for key blocks kb
+    float4v st[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      st[kb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int off = (16 * kb + lq) * KLD + 32 * s + 8 * lg;
+        const half8 ah = *(const half8*)&Kh[off];
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[s], st[kb], 0, 0, 0);
+        if constexpr (KV_LO) {
+          const half8 al = *(const half8*)&Kl[off];
+          st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[s], st[kb], 0, 0, 0);
+        }
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[s], st[kb], 0, 0, 0);
+      }
+    }
+    // mask and online softmax of query lq (keys k0 + 16kb + 4lg + i)
+    float cm = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kp = k0 + 16 * kb + 4 * lg + i;
+        if (kp > qpos || kp >= kend) st[kb][i] = -__builtin_inff();
+        cm = fmaxf(cm, st[kb][i]);
+      }
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float mn = fmaxf(mx, cm);
+    const float corr = mx == -__builtin_inff() ? 0.f : exp2f((mx - mn) * kLog2e);
+    float ps = 0.f;
+    half8 ph[KB / 2], pl[KB / 2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = st[kb][i] == -__builtin_inff() ? 0.f : exp2f((st[kb][i] - mn) * kLog2e);
+        ps += p;
+        _Float16 hi, lo;
+        split_half(p, hi, lo);
+        ph[kb / 2][4 * (kb & 1) + i] = hi;
+        pl[kb / 2][4 * (kb & 1) + i] = lo;
+      }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lsum = lsum * corr + ps;
+    mx = mn;
+    // O^T += V^T P^T: k-step ks, A = V^T[dim 16d + lq][keys 32ks + 4lg .. +3,
+    // 32ks + 16 + 4lg .. +3]
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      ot[d] *= corr;
+#pragma unroll
+      for (int ks = 0; ks < KB / 2; ++ks) {
+        const int off = (16 * d + lq) * VLD + 32 * ks + 4 * lg;
+        const half4 a0 = *(const half4*)&Vh[off], a1 = *(const half4*)&Vh[off + 16];
+        const half8 ah = half8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        ot[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pl[ks], ot[d], 0, 0, 0);
+        if constexpr (KV_LO) {
+          const half4 b0 = *(const half4*)&Vl[off], b1 = *(const half4*)&Vl[off + 16];
+          const half8 al = half8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+          ot[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, ph[ks], ot[d], 0, 0, 0);
+        }
+        ot[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ph[ks], ot[d], 0, 0, 0);
+      }
+    }
+  }
+  if (!qv) return;
+  // lane l holds O^T[dim 16d + 4lg + i][query lq]
+  if (part) {
+    float* pp = part + (((size_t)qi * m.H + head) * S + split) * (DH + 2);
+    if (lg == 0) {
+      pp[0] = mx;
+      pp[1] = lsum;
+    }
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[2 + 16 * d + 4 * lg + i] = ot[d][i];
+    return;
+  }
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[(size_t)qi * D + head * DH + 16 * d + 4 * lg + i] = from_f<T>(__fdiv_rn(ot[d][i], lsum));
+}
+
 }  // namespace
 
 hipError_t launch_kv_attn(const ModelView& m, const ReconArgs& a, hipStream_t s) {
@@ -319,7 +588,7 @@ hipError_t launch_attn_merge(const ModelView& m, int n_rows, const int32_t* row_
 }
 
 int prefill_splits(const ModelView& m, int n, int pos0, int part_floats, int* split_len) {
-  constexpr int KC = 32;
+  const int KC = m.dtype == TL_DTYPE_F32 ? 32 : kPrefillKeyTile16;   // the kernel's key tile
   const int n_qb = (n + 63) / 64;
   const int tiles = (pos0 + n + KC - 1) / KC;            // key tiles of the last query block
   // about four workgroups per CU, at least four key tiles per split, and the
@@ -344,16 +613,29 @@ hipError_t launch_prefill_attn(const ModelView& m, int n, int pos0, const float*
 #define TL_PA(T_, KT_, DH_)                                                                  \
   prefill_attn_kernel<T_, KT_, DH_><<<grid, 256, 0, s>>>(m, n, pos0, q, (const KT_*)kv, (T_*)o, \
                                                           lane, status, pp, S, split_len, n_qb)
+#define TL_PA16(T_, KT_, DH_)                                                                  \
+  prefill_attn16_kernel<T_, KT_, DH_><<<grid, 256, 0, s>>>(m, n, pos0, q, (const KT_*)kv, (T_*)o, \
+                                                            lane, status, pp, S, split_len, n_qb)
   if (m.dtype == TL_DTYPE_F32 && m.dh == 32) TL_PA(float, float, 32);
-  else if (m.dtype == TL_DTYPE_F16 && m.dh == 64 && kv_f32) TL_PA(half_t, float, 64);
-  else if (m.dtype == TL_DTYPE_F16 && m.dh == 64) TL_PA(half_t, half_t, 64);
-  else if (m.dtype == TL_DTYPE_F16 && m.dh == 128 && kv_f32) TL_PA(half_t, float, 128);
-  else if (m.dtype == TL_DTYPE_F16 && m.dh == 128) TL_PA(half_t, half_t, 128);
+  else if (m.dtype == TL_DTYPE_F16 && m.dh == 64 && kv_f32) TL_PA16(half_t, float, 64);
+  else if (m.dtype == TL_DTYPE_F16 && m.dh == 64) TL_PA16(half_t, half_t, 64);
+  else if (m.dtype == TL_DTYPE_F16 && m.dh == 128 && kv_f32) TL_PA16(half_t, float, 128);
+  else if (m.dtype == TL_DTYPE_F16 && m.dh == 128) TL_PA16(half_t, half_t, 128);
   else return hipErrorInvalidValue;
 #undef TL_PA
+#undef TL_PA16
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  return launch_attn_merge(m, n, row_lane, row_pos, status, part, S, split_len, o, s);
+  const int mgrid = (n * m.D + 255) / 256;
+#define TL_MR(T_, DH_)                                                                            \
+  merge_rows_kernel<T_, DH_><<<mgrid, 256, 0, s>>>(n, m.D, m.H, row_lane, row_pos, status, part, S, \
+                                                   split_len, o)
+  if (m.dtype == TL_DTYPE_F32 && m.dh == 32) TL_MR(float, 32);
+  else if (m.dtype == TL_DTYPE_F16 && m.dh == 64) TL_MR(half_t, 64);
+  else if (m.dtype == TL_DTYPE_F16 && m.dh == 128) TL_MR(half_t, 128);
+  else return hipErrorInvalidValue;
+#undef TL_MR
+  return hipGetLastError();
 }
 
 }  // namespace tl
