@@ -19,6 +19,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // keys per LDS tile of the fp16-MFMA prefill attention (key splits are
 // multiples of it)
 constexpr int kPrefillKeyTile16 = 64;
+// threads per workgroup of that kernel: NT / 64 waves of 16 queries each
+constexpr int kPrefillThreads16 = 512;
 
 // All-reduce (sum) over aligned groups of N lanes (N = 8 or 16) with row-level
 // data-parallel moves: partners l ^ 1, l ^ 2 (quad permutations), l ^ 7
@@ -346,9 +348,10 @@ __device__ __forceinline__ void split_half(float x, _Float16& hi, _Float16& lo) 
 // fp32 accumulators (the lo*lo term lies below fp32 rounding), so the scores
 // and the weighted values keep fp32 accuracy on the fp16 MFMA pipe. Stored
 // fp16 K|V rows (the stored-K/V mode) have no lo half.
-// Same work split, masking, online softmax, key splits and outputs as
-// prefill_attn_kernel: one workgroup per (key split, 64 queries, head), wave
-// w owns queries 16w .. 16w+15 and, per tile of 64 keys staged in LDS,
+// Same masking, online softmax, key splits and outputs as
+// prefill_attn_kernel, with 8 waves: one workgroup per (key split, 128
+// queries, head), so each staged key tile serves twice the queries; wave w
+// owns queries 16w .. 16w+15 and, per tile of 64 keys staged in LDS,
 //   S^T = K Q^T   (A: K rows from LDS, B: the wave's queries in registers),
 // so lane l holds S^T[key 16kb + 4*(l/16) + i][query l%16] (kb = 0 .. 3), and
 //   O^T += V^T P^T   over two 32-key k-steps,
@@ -360,16 +363,16 @@ __device__ __forceinline__ void split_half(float x, _Float16& hi, _Float16& lo) 
 // operand is two 8-byte LDS reads. |K|, |V| and |q| must stay within the
 // fp16 range (below 65504); beyond it the attention is not finite.
 template <typename T, typename KT, int DH>
-__global__ __launch_bounds__(256) void prefill_attn16_kernel(ModelView m, int n, int pos0,
+__global__ __launch_bounds__(kPrefillThreads16) void prefill_attn16_kernel(ModelView m, int n, int pos0,
                                                              const float* q, const KT* kv, T* out,
                                                              int lane, const int32_t* status,
                                                              float* part, int S, int split_len,
                                                              int n_qb) {
   constexpr bool KV_LO = std::is_same<KT, float>::value;
-  constexpr int QB = 64, KC = kPrefillKeyTile16, KB = KC / 16, NS = DH / 32, DB = DH / 16;
+  constexpr int NT = kPrefillThreads16, QB = NT / 4, KC = kPrefillKeyTile16, KB = KC / 16, NS = DH / 32, DB = DH / 16;
   constexpr int KLD = DH + 8;                 // K row stride (halfs), 16-byte aligned
   constexpr int VLD = KC + 8;                 // V^T row stride (halfs), 16-byte aligned
-  constexpr int C4 = KC * DH / 4 / 256;       // 4-element chunks of K (and of V) per thread
+  constexpr int C4 = KC * DH / 4 / NT;        // 4-element chunks of K (and of V) per thread
   static_assert(KC % 32 == 0 && C4 >= 1, "key tile");
   __shared__ __attribute__((aligned(16))) _Float16 Kh[KC * KLD];
   __shared__ __attribute__((aligned(16))) _Float16 Kl[KV_LO ? KC * KLD : 8];
@@ -403,14 +406,14 @@ __global__ __launch_bounds__(256) void prefill_attn16_kernel(ModelView m, int n,
   const int k_lo = split * split_len;
   const int kend = min(pos0 + last_q + 1, k_lo + split_len);   // keys k_lo .. kend-1
   if (k_lo >= kend) return;
-  // Tile loads. K: chunk c = t + 256p is key c / (DH/4), dims 4 (c % (DH/4))
+  // Tile loads. K: chunk c = t + NT p is key c / (DH/4), dims 4 (c % (DH/4))
   // .. +3 (one 16- or 8-byte load). V: chunk c is dim c % DH, keys
   // 4 (c / DH) .. +3 (four loads, each coalesced over the lanes' dims).
   float4v kr[C4], vr[C4];
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int p = 0; p < C4; ++p) {
-      const int c = t + 256 * p;
+      const int c = t + NT * p;
       {
         const int kk = c / (DH / 4), d0 = 4 * (c % (DH / 4));
         const KT* row = kv + (size_t)min(k0 + kk, kend - 1) * 2 * D + head * DH + d0;
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(256) void prefill_attn16_kernel(ModelView m, int n,
   auto store_tile = [&]() {
 #pragma unroll
     for (int p = 0; p < C4; ++p) {
-      const int c = t + 256 * p;
+      const int c = t + NT * p;
       half4 xh, xl;
       {
         const int kk = c / (DH / 4), d0 = 4 * (c % (DH / 4));
@@ -587,14 +590,19 @@ hipError_t launch_attn_merge(const ModelView& m, int n_rows, const int32_t* row_
   return hipGetLastError();
 }
 
+// queries per workgroup of the prefill attention kernel the model uses
+static int prefill_qb(const ModelView& m) { return m.dtype == TL_DTYPE_F32 ? 64 : kPrefillThreads16 / 4; }
+
 int prefill_splits(const ModelView& m, int n, int pos0, int part_floats, int* split_len) {
   const int KC = m.dtype == TL_DTYPE_F32 ? 32 : kPrefillKeyTile16;   // the kernel's key tile
-  const int n_qb = (n + 63) / 64;
+  const int n_qb = (n + prefill_qb(m) - 1) / prefill_qb(m);
   const int tiles = (pos0 + n + KC - 1) / KC;            // key tiles of the last query block
-  // about four workgroups per CU, at least four key tiles per split, and the
-  // partials within their buffer
-  int S = (1024 + m.H * n_qb - 1) / (m.H * n_qb);
-  S = std::min(S, std::max(1, tiles / 4));
+  // about four 4-wave (fp32) or two 8-wave (fp16) workgroups per CU, at
+  // least four (fp32) or two (fp16) key tiles per split, and the partials
+  // within their buffer
+  const bool f32 = m.dtype == TL_DTYPE_F32;
+  int S = ((f32 ? 1024 : 512) + m.H * n_qb - 1) / (m.H * n_qb);
+  S = std::min(S, std::max(1, tiles / (f32 ? 4 : 2)));
   S = std::min(S, std::max(1, part_floats / (n * m.H * (m.dh + 2))));
   *split_len = (tiles + S - 1) / S * KC;
   return (pos0 + n + *split_len - 1) / *split_len;
@@ -604,7 +612,7 @@ hipError_t launch_prefill_attn(const ModelView& m, int n, int pos0, const float*
                                const void* kv, int kv_f32, void* o, int lane,
                                const int32_t* status, float* part, int part_floats,
                                const int32_t* row_lane, const int32_t* row_pos, hipStream_t s) {
-  const int n_qb = (n + 63) / 64;
+  const int n_qb = (n + prefill_qb(m) - 1) / prefill_qb(m);
   int split_len = 0;
   const int S = part ? prefill_splits(m, n, pos0, part_floats, &split_len) : 1;
   if (S == 1) split_len = pos0 + n;
@@ -614,7 +622,7 @@ hipError_t launch_prefill_attn(const ModelView& m, int n, int pos0, const float*
   prefill_attn_kernel<T_, KT_, DH_><<<grid, 256, 0, s>>>(m, n, pos0, q, (const KT_*)kv, (T_*)o, \
                                                           lane, status, pp, S, split_len, n_qb)
 #define TL_PA16(T_, KT_, DH_)                                                                  \
-  prefill_attn16_kernel<T_, KT_, DH_><<<grid, 256, 0, s>>>(m, n, pos0, q, (const KT_*)kv, (T_*)o, \
+  prefill_attn16_kernel<T_, KT_, DH_><<<grid, kPrefillThreads16, 0, s>>>(m, n, pos0, q, (const KT_*)kv, (T_*)o, \
                                                             lane, status, pp, S, split_len, n_qb)
   if (m.dtype == TL_DTYPE_F32 && m.dh == 32) TL_PA(float, float, 32);
   else if (m.dtype == TL_DTYPE_F16 && m.dh == 64 && kv_f32) TL_PA16(half_t, float, 64);
