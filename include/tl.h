@@ -128,7 +128,10 @@ size_t tl_workspace_bytes(const tl_config* cfg, int mode, int n_lanes, int max_s
 
 /* Bind a cache to caller memory: d_cache (tl_cache_bytes) holds the entries,
  * d_workspace (tl_workspace_bytes) the per-lane state and scratch. Enqueues a
- * reset of every lane (length 0, status OK) on `stream`. A lane's cache layer
+ * reset of every lane (length 0, status OK) on `stream`, and zeroes the
+ * decode attention's per-(row, head group) tile counters, which every decode
+ * step leaves at zero again: the workspace belongs to the library while the
+ * cache handle lives and must not be written by the caller. A lane's cache layer
  * n_pre + i is written only by loop iteration i, so it stays valid for every
  * later call with loops >= i + 1. */
 tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, int l_max,
