@@ -407,39 +407,44 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   for (int i = 0; i < 4; ++i) epilogue<T, EPI>(g, m.D, row, fb + i, v[i]);
 }
 
-// Products of a prefill chunk (fp16, up to 512 rows): 64 x 64 output tiles
-// and 64-deep k tiles staged through LDS (rows padded to 72 halves), on
-// v_mfma_f32_16x16x32_f16. Wave w computes rows 32 (w / 2) .. +31 and
-// features 32 (w % 2) .. +31 of the tile as 2 x 2 blocks of 16 x 16; the next
-// four k tiles are in flight in registers while the current one is
-// multiplied (the products are latency-bound at these sizes). Every output
-// is one fp32 sum over k in ascending order, then the epilogue.
-template <int EPI>
+// Products of a prefill chunk (fp16, up to 512 rows): BM x 64 output tiles
+// (BM = 64, or 32 when 64-row tiles would leave CUs idle) and 64-deep k tiles
+// staged through LDS (rows padded to 72 halves), on v_mfma_f32_16x16x32_f16.
+// Wave w computes rows (BM/2) (w / 2) .. + BM/2 - 1 and features 32 (w % 2)
+// .. +31 of the tile as (BM/32) x 2 blocks of 16 x 16; the next four k tiles
+// are in flight in registers while the current one is multiplied (the
+// products are latency-bound at these sizes). Every output is one fp32 sum
+// over k in ascending order, then the epilogue, whatever BM is.
+template <int EPI, int BM>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(ModelView m, GemmArgs g) {
-  constexpr int BM = 64, BN = 64, BK = 64, LDT = BK + 8;
+  constexpr int BN = 64, BK = 64, LDT = BK + 8, RB = BM / 32, XP = BM / 32;
+  static_assert(BM == 64 || BM == 32, "row tile");
   __shared__ __attribute__((aligned(16))) half_t xs[2][BM * LDT];
   __shared__ __attribute__((aligned(16))) half_t wsm[2][BN * LDT];
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l & 15, lk = l >> 4;
-  // staging: thread t moves 16 halves (k offset 16 (t % 4)) of tile row t / 4
+  // staging: thread t moves 16 halves (k offset 16 (t % 4)) of W tile row
+  // t / 4, and 8 XP halves of X tile row t / (8 / XP) at k offset
+  // 8 XP (t % (8 / XP))
   const int srow = t >> 2, sk = (t & 3) * 16;
-  const half_t* xsrc = (const half_t*)g.X + (size_t)min(m0 + srow, g.M - 1) * g.ldx + sk;
+  const int xrow = t / (8 / XP), xk = (t % (8 / XP)) * 8 * XP;
+  const half_t* xsrc = (const half_t*)g.X + (size_t)min(m0 + xrow, g.M - 1) * g.ldx + xk;
   const half_t* wsrc = (const half_t*)g.W + (size_t)(n0 + srow) * g.ldw + sk;
   // the thread's parts of the next PF k tiles are in flight in registers
   constexpr int PF = 4;
-  half8 ring[PF][4];
+  half8 ring[PF][2 + XP];
   const int nkt = g.K / BK;
 #pragma unroll
   for (int u = 0; u < PF; ++u)
     if (u < nkt) {
-      ring[u][0] = *(const half8*)(xsrc + u * BK);
-      ring[u][1] = *(const half8*)(xsrc + u * BK + 8);
-      ring[u][2] = *(const half8*)(wsrc + u * BK);
-      ring[u][3] = *(const half8*)(wsrc + u * BK + 8);
-    }
-  float4v acc[2][2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+      for (int x = 0; x < XP; ++x) ring[u][x] = *(const half8*)(xsrc + u * BK + 8 * x);
+      ring[u][XP] = *(const half8*)(wsrc + u * BK);
+      ring[u][XP + 1] = *(const half8*)(wsrc + u * BK + 8);
+    }
+  float4v acc[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = float4v{0.f, 0.f, 0.f, 0.f};
   for (int kt0 = 0; kt0 < nkt; kt0 += PF) {
@@ -449,29 +454,29 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(ModelView m, GemmArgs g
       if (kt >= nkt) break;
       // LDS buffer b was last read two tiles ago, before the previous barrier
       const int b = kt & 1;
-      *(half8*)&xs[b][srow * LDT + sk] = ring[u][0];
-      *(half8*)&xs[b][srow * LDT + sk + 8] = ring[u][1];
-      *(half8*)&wsm[b][srow * LDT + sk] = ring[u][2];
-      *(half8*)&wsm[b][srow * LDT + sk + 8] = ring[u][3];
+#pragma unroll
+      for (int x = 0; x < XP; ++x) *(half8*)&xs[b][xrow * LDT + xk + 8 * x] = ring[u][x];
+      *(half8*)&wsm[b][srow * LDT + sk] = ring[u][XP];
+      *(half8*)&wsm[b][srow * LDT + sk + 8] = ring[u][XP + 1];
       __syncthreads();
       if (kt + PF < nkt) {
         const int k1 = (kt + PF) * BK;
-        ring[u][0] = *(const half8*)(xsrc + k1);
-        ring[u][1] = *(const half8*)(xsrc + k1 + 8);
-        ring[u][2] = *(const half8*)(wsrc + k1);
-        ring[u][3] = *(const half8*)(wsrc + k1 + 8);
+#pragma unroll
+        for (int x = 0; x < XP; ++x) ring[u][x] = *(const half8*)(xsrc + k1 + 8 * x);
+        ring[u][XP] = *(const half8*)(wsrc + k1);
+        ring[u][XP + 1] = *(const half8*)(wsrc + k1 + 8);
       }
 #pragma unroll
       for (int ks = 0; ks < BK / 32; ++ks) {
-        half8 av[2], bv[2];
+        half8 av[RB], bv[2];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          av[rb] = *(const half8*)&xs[b][(32 * (w >> 1) + 16 * rb + lr) * LDT + 32 * ks + 8 * lk];
+        for (int rb = 0; rb < RB; ++rb)
+          av[rb] = *(const half8*)&xs[b][((BM / 2) * (w >> 1) + 16 * rb + lr) * LDT + 32 * ks + 8 * lk];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
           bv[cb] = *(const half8*)&wsm[b][(32 * (w & 1) + 16 * cb + lr) * LDT + 32 * ks + 8 * lk];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
             acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[rb], bv[cb], acc[rb][cb], 0, 0, 0);
@@ -480,10 +485,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(ModelView m, GemmArgs g
   }
   // lane l holds rows 4 (l / 16) + i of each block, feature l % 16
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 32 * (w >> 1) + 16 * rb + 4 * lk + i;
+      const int row = m0 + (BM / 2) * (w >> 1) + 16 * rb + 4 * lk + i;
       if (row >= g.M) continue;
       if (g.status && g.status[g.row_lane[row]] == TL_LANE_ABORTED) continue;
 #pragma unroll
@@ -492,16 +497,25 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(ModelView m, GemmArgs g
     }
 }
 
-hipError_t launch_tiled(const ModelView& m, const GemmArgs& g, hipStream_t s) {
-  const dim3 grid(g.N / 64, (g.M + 63) / 64);
+constexpr int kCUs = 256;
+
+template <int BM>
+hipError_t launch_tiled_bm(const ModelView& m, const GemmArgs& g, hipStream_t s) {
+  const dim3 grid(g.N / 64, (g.M + BM - 1) / BM);
   switch (g.epi) {
-    case EPI_STORE_F32: gemm_tiled_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(m, g); break;
-    case EPI_STORE_T: gemm_tiled_kernel<EPI_STORE_T><<<grid, 256, 0, s>>>(m, g); break;
-    case EPI_ADD_F32: gemm_tiled_kernel<EPI_ADD_F32><<<grid, 256, 0, s>>>(m, g); break;
-    case EPI_GELU_T: gemm_tiled_kernel<EPI_GELU_T><<<grid, 256, 0, s>>>(m, g); break;
+    case EPI_STORE_F32: gemm_tiled_kernel<EPI_STORE_F32, BM><<<grid, 256, 0, s>>>(m, g); break;
+    case EPI_STORE_T: gemm_tiled_kernel<EPI_STORE_T, BM><<<grid, 256, 0, s>>>(m, g); break;
+    case EPI_ADD_F32: gemm_tiled_kernel<EPI_ADD_F32, BM><<<grid, 256, 0, s>>>(m, g); break;
+    case EPI_GELU_T: gemm_tiled_kernel<EPI_GELU_T, BM><<<grid, 256, 0, s>>>(m, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_tiled(const ModelView& m, const GemmArgs& g, hipStream_t s) {
+  // 32-row tiles when 64-row ones would leave CUs without a workgroup
+  if ((g.N / 64) * ((g.M + 63) / 64) < kCUs) return launch_tiled_bm<32>(m, g, s);
+  return launch_tiled_bm<64>(m, g, s);
 }
 
 template <typename T, int KS, int NU>
@@ -574,7 +588,6 @@ hipError_t launch_ks(const ModelView& m, const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-constexpr int kCUs = 256;
 
 template <typename T>
 hipError_t launch_t(const ModelView& m, const GemmArgs& g, hipStream_t s) {
