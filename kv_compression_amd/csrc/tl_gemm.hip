@@ -591,7 +591,12 @@ hipError_t launch_ks(const ModelView& m, const GemmArgs& g, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_t(const ModelView& m, const GemmArgs& g, hipStream_t s) {
-  if (g.N / 16 < kCUs && g.K % (32 * 16) == 0) return launch_ks<T, 16>(m, g, s);
+  // 16 waves when the output has too few 16-feature groups for every CU, and
+  // when the row work needs them: its threads cover a d_model row two
+  // elements each (the stored-K/V projection of 3 d_model features at
+  // d_model 2048 has groups enough for 4 waves, but not the threads)
+  const bool row_threads = g.norm_gain && g.row_tasks && 64 * 4 * 2 < m.D;
+  if ((g.N / 16 < kCUs || row_threads) && g.K % (32 * 16) == 0) return launch_ks<T, 16>(m, g, s);
   return launch_ks<T, 4>(m, g, s);
 }
 

@@ -78,3 +78,30 @@ def test_2b_speculative_matches_oracle_greedy():
         r = orc.decode_step([0], [4], [prev])
         assert token_ok(g, r["logits"][0]), (i, g)
         prev = g
+
+
+@pytest.mark.parametrize("mode", ["kv", "f16"])
+def test_2b_chunked_prefill_and_decode(mode):
+    """The prefill attention at 128-wide heads: fp16 stored K|V (no lo half)
+    and fp32 K|V rebuilt from fp16 h (hi and lo halves), over three chunks of
+    128 tokens (later chunks attend over earlier ones), then two decode steps."""
+    torch_gpu()
+    w, gm = gpu_model(S2B, random_gains=True)
+    pr = _prompt(300, 34)
+    c = gm.cache(mode, 1, 310, 2)
+    orc = oracle.LoopedOracle(S2B, w, mode, 1, 310, 2)
+    nxt, lg = c.prefill(0, pr, 2, chunk=128)
+    ro = orc.prefill(0, pr, 2)
+    e = rel_err(lg.cpu().numpy(), ro["logits"][-1])
+    record("2b_chunked_prefill", mode=mode, rel=e)
+    assert e <= REL_TOL, (mode, e)
+    tok = int(nxt.cpu()[0])
+    assert token_ok(tok, ro["logits"][-1])
+    for step in range(2):
+        t, lgd, st = decode(c, [0], [2], [tok])
+        r = orc.decode_step([0], [2], [tok])
+        e = rel_err(lgd[0], r["logits"][0])
+        record("2b_chunked_decode", mode=mode, step=step, rel=e)
+        assert st[0] == 0 and e <= REL_TOL, (mode, step, e)
+        assert token_ok(int(t[0]), r["logits"][0])
+        tok = int(t[0])
