@@ -80,11 +80,12 @@ def test_2b_speculative_matches_oracle_greedy():
         prev = g
 
 
-@pytest.mark.parametrize("mode", ["kv", "f16"])
+@pytest.mark.parametrize("mode", ["kv", "f16", "int8"])
 def test_2b_chunked_prefill_and_decode(mode):
     """The prefill attention at 128-wide heads: fp16 stored K|V (no lo half)
-    and fp32 K|V rebuilt from fp16 h (hi and lo halves), over three chunks of
-    128 tokens (later chunks attend over earlier ones), then two decode steps."""
+    and fp32 K|V rebuilt from h (hi and lo halves), over three chunks of 128
+    tokens (later chunks attend over earlier ones), then two decode steps
+    (INT8: the reconstruction kernel's 256-row variant at 128-wide heads)."""
     torch_gpu()
     w, gm = gpu_model(S2B, random_gains=True)
     pr = _prompt(300, 34)
