@@ -289,3 +289,27 @@ def test_abi_errors_do_not_enqueue():
     with pytest.raises(tl.TLError) as e:
         decode(c, [1, 1], [1, 1], [1, 1])
     assert e.value.status == tl.TL_E_ARG
+
+
+@pytest.mark.parametrize("mode", ["f32", "kv"])
+def test_tiny_fp32_chunked_prefill(mode):
+    """The fp32 model's prefill: the fp32-MFMA attention kernel, and chunks of
+    20 tokens late in a 300-token prompt, whose keys are split over
+    workgroups and merged row-parallel; then two decode steps."""
+    w, gm = gpu_model(TINY)
+    pr = synth.make_prompts(TINY.vocab, 1, 300, 12)[0]
+    c = gm.cache(mode, 1, 310, 2)
+    orc = oracle.LoopedOracle(TINY, w, mode, 1, 310, 2)
+    nxt, lg = c.prefill(0, pr, 2, chunk=20)
+    ro = orc.prefill(0, pr, 2)
+    e = rel_err(lg.cpu().numpy(), ro["logits"][-1])
+    record("tiny_chunked_prefill", mode=mode, rel=e)
+    assert e <= REL_TOL, (mode, e)
+    tok = int(nxt.cpu().numpy()[0])
+    assert token_ok(tok, ro["logits"][-1])
+    for step in range(2):
+        t, lgd, st = decode(c, [0], [2], [tok])
+        r = orc.decode_step([0], [2], [tok])
+        assert st[0] == 0 and rel_err(lgd[0], r["logits"][0]) <= REL_TOL, (mode, step)
+        assert token_ok(int(t[0]), r["logits"][0])
+        tok = int(t[0])
