@@ -325,46 +325,51 @@ __global__ __launch_bounds__(256) void absorbed_merge_kernel(int D, int H, const
                                                              const int32_t* status,
                                                              const float* part, int S,
                                                              int split_len, float* out) {
+  constexpr int U = 64;   // splits whose column values a thread loads at once
   __shared__ float ms[1024];
   __shared__ float wgt[1024];
+  __shared__ float red[4];
   __shared__ float lsh;
   const int parts = D / 256, q4 = blockIdx.x % parts, rh = blockIdx.x / parts;
   const int r = rh / H, h = rh % H;
   if (status[row_lane[r]] == TL_LANE_ABORTED || row_pos[r] < 0) return;
   const int T = row_pos[r] + 1;
-  const int ns = (T + split_len - 1) / split_len;
+  const int ns = (T + split_len - 1) / split_len;   // >= 1, <= S
   const size_t sstride = (size_t)H * (D + 2);
   const float* p = part + (size_t)r * S * sstride + (size_t)h * (D + 2);
   const int t = threadIdx.x;
-  for (int s = t; s < ns; s += 256) {
-    ms[s] = p[s * sstride];
-    wgt[s] = p[s * sstride + 1];
-  }
-  __syncthreads();
-  if (t == 0) {
-    float M = -__builtin_inff();
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ms[s]);
-    float L = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = exp2f((ms[s] - M) * kLog2e);
-      L = fmaf(wgt[s], w, L);
-      ms[s] = w;
-    }
-    lsh = L;
-  }
-  __syncthreads();
   const int c = q4 * 256 + t;
   const float* pc = p + 2 + c;
-  float acc = 0.f;
-  int s = 0;
-  for (; s + 16 <= ns; s += 16) {
-    float v[16];
+  // the first U splits' values of this column go out with the maxima and sums
+  float v[U];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = pc[(size_t)(s + u) * sstride];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) acc = fmaf(v[u], ms[s + u], acc);
+  for (int u = 0; u < U; ++u) v[u] = pc[(size_t)min(u, ns - 1) * sstride];
+  float mloc = -__builtin_inff();
+  for (int s = t; s < ns; s += 256) {
+    const float m = p[s * sstride];
+    ms[s] = m;
+    wgt[s] = p[s * sstride + 1];
+    mloc = fmaxf(mloc, m);
   }
-  for (; s < ns; ++s) acc = fmaf(pc[(size_t)s * sstride], ms[s], acc);
+  const float M = block_max(mloc, red);   // (its barriers also publish ms, wgt)
+  for (int s = t; s < ns; s += 256) ms[s] = exp2f((ms[s] - M) * kLog2e);
+  __syncthreads();
+  if (t == 0) {
+    float L = 0.f;
+    for (int s = 0; s < ns; ++s) L = fmaf(wgt[s], ms[s], L);
+    lsh = L;
+  }
+  float acc = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += U) {
+    if (c0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = pc[(size_t)min(c0 + u, ns - 1) * sstride];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c0 + u < ns) acc = fmaf(v[u], ms[c0 + u], acc);
+  }
+  __syncthreads();
   out[((size_t)r * H + h) * D + c] = __fdiv_rn(acc, lsh);
 }
 
