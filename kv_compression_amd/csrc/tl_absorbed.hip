@@ -18,6 +18,9 @@
 
 #include "tl_device.h"
 
+#define TL_LDS __attribute__((address_space(3)))
+typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
 namespace tl {
 namespace {
 
@@ -139,7 +142,8 @@ struct AbsArgs {
 //     order;
 //   online softmax per head;
 //   R[head][d] += P[head][pos] h'[pos][d]: the lane's eight weights are exactly
-//     the A operand (row = head, k = 8 (l / 16) + j); B = h' from LDS.
+//     the A operand (row = head, k = 8 (l / 16) + j); B = h' from LDS through
+//     two transpose reads (ds_read_b64_tr_b16) per product.
 // LDS row of position p starts at p * LDR + 8 ((p / 8) % 4) halves and its
 // 64-element blocks are 72 halves apart: the row shift keeps the weighted
 // sum's strided B reads (rows 8 (l / 16) + j) on distinct banks, the block
@@ -288,15 +292,18 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
     half8 ph;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ph[j] = (half_t)pv[j];
-    int brow[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) brow[j] = row_of(8 * lg + j);
+    // B = h'[8 lg + j][c0 + 16 n + lq] (j = 0 .. 7) through two LDS transpose
+    // reads: within each group of 16 lanes, output lane i gets element i % 4
+    // of the 8 bytes read by lane 4 k + i / 4, as its element k. So lane lq
+    // reads columns 4 (lq % 4) .. +3 of row 8 lg + lq / 4 (then of row
+    // 8 lg + 4 + lq / 4), and lane lq receives column lq of rows 8 lg + k.
+    const int trow0 = row_of(8 * lg + (lq >> 2)), trow1 = row_of(8 * lg + 4 + (lq >> 2));
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const int col = col_of(c0 + 16 * n + lq);
-      half8 bv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bv[j] = hs[brow[j] + col];
+      const int tcol = col_of(c0 + 16 * n + 4 * (lq & 3));
+      const half4 b0 = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((TL_LDS fp16x4*)(hs + trow0 + tcol)));
+      const half4 b1 = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((TL_LDS fp16x4*)(hs + trow1 + tcol)));
+      const half8 bv = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
       float4v r = R[n];
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] *= ci[i];
