@@ -94,7 +94,7 @@ def load_traffic(workload: str, mode: str):
         return None
 
 
-def cpu_baseline(shape, w, mode, context, loops, budget_s=12.0, max_steps=8):
+def cpu_baseline(shape, w, mode, context, loops, budget_s=12.0, max_steps=64):
     """The CPU oracle decoding one lane of the same workload (context `context`,
     same mode and loops); the lane's cache is filled through the oracle's own
     codec from N(0, 1) draws (the contents do not change the work)."""
