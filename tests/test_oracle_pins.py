@@ -519,3 +519,148 @@ def test_cache_bytes_closed_form():
     # 4 lanes x 10 layers x 4224 positions x 576 B
     assert looped.cache_bytes("int4", 1024, "f16", 4, 4224, 8, 2) == 97_320_960
     assert looped.cache_bytes("kv", 1024, "f16", 4, 4224, 8, 2) == 692_060_160
+
+
+# ------------------------------------------------ rounding points of the fp16 model
+BF16 = synth.ModelShape("bf-f16", 64, 2, 32, 128, 1, 13, "f16")
+BF16_POINTS = {
+    "f16": frozenset(("R1", "R4o", "R4u", "R4a", "R4z")),
+    "kv": frozenset(("R1", "R4o", "R4u", "R4a", "R4z", "R5")),
+    "int4": frozenset(("R1", "R3", "R4o", "R4u", "R4a", "R4z")),
+    "int8": frozenset(("R1", "R3", "R4o", "R4u", "R4a", "R4z")),
+}
+
+
+def _as_lists(w):
+    return {
+        "embed": w["embed"].astype(float).tolist(),
+        "lm_head": w["lm_head"].astype(float).tolist(),
+        "final_norm": w["final_norm"].astype(float).tolist(),
+        "layers": [{k: v.astype(float).tolist() for k, v in lw.items()} for lw in w["layers"]],
+    }
+
+
+def _oracle_sequence_logits(shape, w, mode, toks, L, n_prefill=3):
+    o = oracle.LoopedOracle(shape, w, mode, 1, len(toks) + 1, L)
+    r = o.prefill(0, toks[:n_prefill], L)
+    got = [r["logits"][i] for i in range(n_prefill)]
+    for t in toks[n_prefill:]:
+        got.append(o.decode_step([0], [L], [t])["logits"][0])
+    return np.array(got)
+
+
+@pytest.mark.parametrize("mode", ["f16", "kv", "int4", "int8"])
+def test_bruteforce_fp16_model_rounding_points(mode):
+    """The fp16 model rounds at fixed points: h before it is stored and
+    projected (R1), the codec's h' = fp16(q s) (R3), o, the norm-2 output, the
+    GELU output and the final-norm output before their products (R4), and
+    stored K/V (R5). A scalar brute force that rounds through the standard
+    library's binary16 packing, and codes INT4 / INT8 h by its own scalar
+    codec, matches the oracle to float64 rounding; and dropping any one of
+    those points moves the brute force's logits by far more than that
+    tolerance, so the comparison sees every rounding point."""
+    w = synth.make_weights(BF16, 3, random_gains=True, std=0.3)
+    wl = _as_lists(w)
+    toks = [3, 11, 0, 7, 5]
+    L = 2
+    points = BF16_POINTS[mode]
+    bf, _ = _bruteforce.run_sequence(wl, BF16.n_heads, BF16.n_pre, L, toks, BF16.norm_eps,
+                                     rounding=points, mode=mode if mode != "f16" else "h")
+    bf = np.array(bf)
+    scale = np.max(np.abs(bf))
+    got = _oracle_sequence_logits(BF16, w, mode, toks, L)
+    assert np.max(np.abs(got - bf)) <= 1e-12 * scale
+    for p in sorted(points):
+        alt, _ = _bruteforce.run_sequence(wl, BF16.n_heads, BF16.n_pre, L, toks, BF16.norm_eps,
+                                          rounding=points - {p}, mode=mode if mode != "f16" else "h")
+        assert np.max(np.abs(np.array(alt) - bf)) > 1e-8 * scale, p
+
+
+def test_bruteforce_codec_matches_oracle_codec():
+    """The brute force's scalar codec gives the oracle's codes and scales
+    (both INT widths, groups along d_model), so its end-to-end INT runs test
+    the oracle's model, not a second reading of the codec."""
+    rng = np.random.default_rng(21)
+    h = (rng.standard_normal((6, 64)) * rng.uniform(0.05, 20, size=(6, 1))).astype(np.float16)
+    h[2, :32] = 0
+    for kind, enc, group, qmax, qmin in (("int4", looped.int4_encode, 32, 7, -8),
+                                         ("int8", looped.int8_encode, 64, 127, -127)):
+        q, s = enc(h)
+        hp = looped.decode_int(q, s)
+        for r in range(h.shape[0]):
+            codes, scales, out = _bruteforce.codec_roundtrip([float(t) for t in h[r]], group, qmax, qmin)
+            assert codes == q[r].tolist(), kind
+            assert scales == s[r].astype(float).tolist(), kind
+            assert [_bruteforce.f16(t) for t in out] == hp[r].astype(float).tolist(), kind
+
+
+# ------------------------------------------------ safety check on a degenerate state
+def test_safety_fires_on_nan_residual():
+    """A degenerate hidden state fires the check (novel-contributions page,
+    'Per-Iteration Safety Check': the check exists to catch degenerate states).
+    An infinite embedding element makes the first norm's output NaN, so the
+    residual is NaN by loop iteration 0; not (NaN <= threshold) holds, so the
+    lane aborts there with no token and keeps its length, while its batch mate
+    decodes exactly as it would alone."""
+    w = synth.make_weights(SMALL16, 5, random_gains=True)
+    bad = 7
+    w["embed"] = w["embed"].copy()
+    w["embed"][bad, 3] = np.inf
+    L = 3
+    o = oracle.LoopedOracle(SMALL16, w, "int4", 2, 12, L)
+    t0 = o.prefill(0, [1, 2, 3, 4], L)["next_token"]
+    t1 = o.prefill(1, [5, 6, 8, 9], L)["next_token"]
+    r = o.decode_step([0, 1], [L, L], [bad, t1], 1e30)
+    assert r["status"].tolist() == [oracle.LANE_ABORTED, oracle.LANE_OK]
+    assert r["tokens"][0] == -1 and o.length[0] == 4 and o.length[1] == 5
+    assert np.all(np.isnan(o.norms[0]))
+    # the lane ran iteration 0 and stopped there
+    o2 = oracle.LoopedOracle(SMALL16, w, "int4", 1, 12, L)
+    o2.prefill(0, [1, 2, 3, 4], L)
+    f = o2.forward(0, [bad], L, check_safety=True, threshold=1e30)
+    assert f["aborted_at"] == 0 and f["logits"] is None
+    assert np.isnan(f["norms"][0, 0]) and np.all(np.isnan(f["norms"][0, 1:]))
+    alone = oracle.LoopedOracle(SMALL16, w, "int4", 1, 12, L)
+    assert alone.prefill(0, [5, 6, 8, 9], L)["next_token"] == t1
+    ra = alone.decode_step([0], [L], [t1], 1e30)
+    assert np.array_equal(ra["logits"][0], r["logits"][1]) and ra["tokens"][0] == r["tokens"][1]
+
+
+# ------------------------------------------------ argmax ties
+def test_argmax_ties_lowest_index():
+    assert oracle.argmax_lowest(np.array([1.0, 3.0, -2.0, 3.0, 3.0])) == 1
+    assert oracle.argmax_lowest(np.zeros(9)) == 0
+    assert oracle.argmax_lowest(np.array([-1.0, -5.0, -1.0])) == 0
+
+
+def tie_head(vocab, d_model, k, sign, ties, value=5.0, others=(1.0, 2.0, 3.0, 4.0)):
+    """An LM head whose logits tie exactly at the top: row r is c_r times the
+    unit vector on coordinate k, so logit r = c_r * z_k is one exact product
+    (the other terms are zeros). c_r = value at the rows in ``ties``, a
+    smaller value at every other row; ``sign`` (the sign of z_k) makes the
+    tied rows the largest."""
+    head = np.zeros((vocab, d_model), np.float64)
+    c = np.array([others[r % len(others)] for r in range(vocab)], np.float64)
+    c[list(ties)] = value
+    head[:, k] = sign * c
+    return head
+
+
+def test_decode_argmax_tie_goes_to_lowest_index():
+    """End to end: with an LM head whose top logits tie exactly, the decode
+    step emits the lowest tied index."""
+    w = synth.make_weights(SMALL16, 11, random_gains=True)
+    L = 2
+    o = oracle.LoopedOracle(SMALL16, w, "f16", 1, 8, L)
+    o.prefill(0, [4, 2, 9], L)
+    f = o.forward(0, [17], L, check_safety=False, keep_trace=True)
+    z = dict(o.trace[0])["final_ln"][0]
+    k = int(np.argmax(np.abs(z)))
+    ties = (40, 13, 88)
+    w["lm_head"] = tie_head(SMALL16.vocab, SMALL16.d_model, k, np.sign(z[k]), ties).astype(np.float16)
+    o = oracle.LoopedOracle(SMALL16, w, "f16", 1, 8, L)
+    t = o.prefill(0, [4, 2, 9], L)["next_token"]
+    r = o.decode_step([0], [L], [17])
+    lg = r["logits"][0]
+    assert lg[13] == lg[40] == lg[88] == np.max(lg) and np.sum(lg == np.max(lg)) == 3
+    assert r["tokens"][0] == 13
