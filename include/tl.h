@@ -118,7 +118,13 @@ void tl_model_destroy(tl_model* m);
 
 /* Exact payload bytes of a cache of n_pre + l_max layers x n_lanes x max_seq
  * entries in `mode` (closed form; features page, "Variable-L KV cache": the
- * cache is sized by n_pre + L_max). 0 if the arguments are invalid. */
+ * cache is sized by n_pre + L_max). 0 if the arguments are invalid, including
+ * a max_seq whose code rows of one (layer, lane) would reach 2^31 bytes
+ * (max_seq x row bytes without the INT scales; the delta mode counts its
+ * 2 * d_model-byte anchor rows): the decode attention addresses one such slab
+ * in 32 bits. At d_model
+ * 2048 that caps max_seq below 1,048,576 in INT8-h, 2,097,152 in INT4-h and
+ * 524,288 in fp16-h. */
 size_t tl_cache_bytes(const tl_config* cfg, int mode, int n_lanes, int max_seq, int l_max);
 
 /* Bytes of device workspace a cache needs: per-lane state (length, status,
@@ -133,7 +139,9 @@ size_t tl_workspace_bytes(const tl_config* cfg, int mode, int n_lanes, int max_s
  * step leaves at zero again: the workspace belongs to the library while the
  * cache handle lives and must not be written by the caller. A lane's cache layer
  * n_pre + i is written only by loop iteration i, so it stays valid for every
- * later call with loops >= i + 1. */
+ * later call with loops >= i + 1. Errors: TL_E_UNSUPPORTED for a mode the
+ * model cannot store or a max_seq past the per-slab limit of tl_cache_bytes;
+ * TL_E_ARG for bad sizes and short or unaligned buffers. */
 tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, int l_max,
                          void* d_cache, size_t cache_bytes, void* d_workspace, size_t ws_bytes,
                          void* stream, tl_cache** out);

@@ -151,6 +151,28 @@ struct Layout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The decode attention kernels address one (layer, lane) slab of codes
+// through a buffer resource whose extent and offsets are 32-bit, so every
+// slab (max_seq rows of one layer and lane, without the INT scales, which
+// live in their own array; in the delta mode the fp16 anchor rows) stays
+// below 2^31 bytes. A layout past that is refused.
+constexpr size_t kMaxSlabBytes = (size_t)1 << 31;
+bool slab_ok(const tl_config* c, int mode, int max_seq, std::string* why) {
+  const size_t D = c->d_model;
+  size_t row = 0;
+  switch (mode) {
+    case TL_CACHE_H_INT8: row = D; break;
+    case TL_CACHE_H_INT4: row = D / 2; break;
+    case TL_CACHE_H_DELTA8: row = 2 * D; break;
+    default: row = entry_bytes(c, mode);
+  }
+  if ((size_t)max_seq * row >= kMaxSlabBytes) {
+    *why = "one layer and lane of the cache would reach 2^31 bytes (max_seq x entry bytes)";
+    return false;
+  }
+  return true;
+}
+
 Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, int l_max) {
   Layout L{};
   const size_t D = c->d_model, F = c->d_mlp, V = c->vocab, es = dtype_size(c->dtype);
@@ -259,13 +281,17 @@ void tl_model_destroy(tl_model* m) { delete m; }
 
 size_t tl_cache_bytes(const tl_config* cfg, int mode, int n_lanes, int max_seq, int l_max) {
   std::string why;
-  if (!config_ok(cfg, &why) || !mode_ok(cfg, mode, &why) || !dims_ok(n_lanes, max_seq, l_max)) return 0;
+  if (!config_ok(cfg, &why) || !mode_ok(cfg, mode, &why) || !dims_ok(n_lanes, max_seq, l_max) ||
+      !slab_ok(cfg, mode, max_seq, &why))
+    return 0;
   return (size_t)n_lanes * max_seq * position_bytes(cfg, mode, l_max);
 }
 
 size_t tl_workspace_bytes(const tl_config* cfg, int mode, int n_lanes, int max_seq, int l_max) {
   std::string why;
-  if (!config_ok(cfg, &why) || !mode_ok(cfg, mode, &why) || !dims_ok(n_lanes, max_seq, l_max)) return 0;
+  if (!config_ok(cfg, &why) || !mode_ok(cfg, mode, &why) || !dims_ok(n_lanes, max_seq, l_max) ||
+      !slab_ok(cfg, mode, max_seq, &why))
+    return 0;
   return workspace_layout(cfg, mode, n_lanes, max_seq, l_max).total;
 }
 
@@ -279,6 +305,7 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   const tl_config* cfg = &m->cfg;
   if (!mode_ok(cfg, mode, &why)) return fail(TL_E_UNSUPPORTED, "mode: %s", why.c_str());
   if (!dims_ok(n_lanes, max_seq, l_max)) return fail(TL_E_ARG, "bad n_lanes / max_seq / l_max");
+  if (!slab_ok(cfg, mode, max_seq, &why)) return fail(TL_E_UNSUPPORTED, "max_seq %d: %s", max_seq, why.c_str());
   const size_t need = tl_cache_bytes(cfg, mode, n_lanes, max_seq, l_max);
   const Layout L = workspace_layout(cfg, mode, n_lanes, max_seq, l_max);
   if (!d_cache || cache_bytes < need) return fail(TL_E_ARG, "cache buffer: need %zu bytes", need);
