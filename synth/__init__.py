@@ -33,7 +33,9 @@ Random streams
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -213,9 +215,13 @@ def prior_h(seed: int, layer: int, lane: int, positions, d_model: int) -> np.nda
     k = np.arange(d_model, dtype=np.uint32)
     key = np.array([seed, PHILOX_H_KEY1], dtype=np.uint32)
     res = np.empty((pos.size, d_model), dtype=np.float32)
-    # chunks of positions keep the generator's temporaries in cache
+    # chunks of positions keep the generator's temporaries in cache; numpy
+    # releases the interpreter lock inside its array operations, so large
+    # requests run their chunks on a few threads (each chunk writes its own
+    # rows, the values do not depend on the split)
     step = max(1, (1 << 16) // max(d_model, 1))
-    for p0 in range(0, pos.size, step):
+
+    def chunk(p0):
         pc = pos[p0:p0 + step]
         ctr = np.empty((pc.size, d_model, 4), dtype=np.uint32)
         ctr[..., 0] = k[None, :]
@@ -228,4 +234,13 @@ def prior_h(seed: int, layer: int, lane: int, positions, d_model: int) -> np.nda
         s = lo.sum(axis=-1) + hi.sum(axis=-1)             # sum of eight 16-bit uniforms
         centred = (s - 262140).astype(np.float32)         # exact: |value| < 2**24
         res[p0:p0 + pc.size] = centred * NORMAL_SCALE_F32  # one fp32 rounding
+
+    starts = range(0, pos.size, step)
+    workers = min(16, len(os.sched_getaffinity(0)), len(starts))
+    if workers > 1 and pos.size * d_model >= (1 << 22):
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(chunk, starts))
+    else:
+        for p0 in starts:
+            chunk(p0)
     return res
