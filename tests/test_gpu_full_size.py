@@ -8,7 +8,9 @@ context length without a long prefill in the oracle. The oracle recomputes a
 sample of the lanes (each lane is independent of its batch mates); where even
 one lane is out of its reach (32768 positions at the 2B shape) the test checks
 properties that hold at any size instead: run-to-run and batch-composition
-bitwise equality and the bit-exact cache encoding at far positions."""
+bitwise equality and the bit-exact cache encoding at far positions; and one
+sampled lane of that workload is recomputed by the oracle in full (about
+6e12 FP64 flop per pass over its 33280 positions)."""
 import math
 
 import numpy as np
@@ -276,3 +278,50 @@ def test_2b_ctx32k_b8_properties():
     for (t1, l1, _), (t3, l3, _) in zip(out1, out3):
         assert int(t1[5]) == int(t3[0])
         assert np.array_equal(l1[5].view(np.uint32), l3[0].view(np.uint32))
+
+
+def test_2b_ctx32k_b8_sampled_lane_matches_oracle():
+    """The 2B long-context workload at its full size and in the benchmark's
+    launch configuration: 8 lanes with 32768 synthetic prior positions in all
+    10 layers, one 512-token prefill chunk per lane, then one decode step of
+    the 8 lanes. Lane 5 is recomputed by the oracle (features page, "Store-h
+    KV cache": long contexts are what store-h is for): the chunk's last logits
+    and the decode step's logits within 2e-3, tokens with the near-tie rule,
+    and the step's residual norms within 2e-3. At 33281 positions the decode
+    attention merges 131 position tiles per row (its merge loads partials in
+    batches of 32 tiles) and the chunk's causal attention splits 33k keys."""
+    torch = torch_gpu()
+    wl = synth.workload("2b-int4h-ctx32k-b8")
+    sh = wl.shape
+    w, gm = gpu_model(sh)
+    L = wl.l_max
+    lane = 5
+    chunks = synth.make_prompts(sh.vocab, wl.lanes, wl.chunk, wl.seed_prompt)
+    lanes = list(range(wl.lanes))
+    c = gm.cache("int4", wl.lanes, wl.max_seq, L)
+    n_layers = sh.n_pre + L
+    fill_gpu(c, lanes, lambda k: n_layers, wl.context, wl.seed_prior)
+    toks, last = [], None
+    for k in lanes:
+        nxt, lg = c.prefill(k, chunks[k], L)
+        toks.append(int(nxt.cpu().numpy()[0]))
+        if k == lane:
+            last = lg.cpu().numpy().astype(np.float64)
+    t, lgd, st = decode(c, lanes, [L] * wl.lanes, toks)
+    assert np.all(st == 0)
+    norms = c.tl_residual_norms(lane)[:L]
+    del c
+    orc = oracle.LoopedOracle(sh, w, "int4", 1, wl.max_seq, L)
+    orc.prime_synthetic(0, range(n_layers), wl.context,
+                        lambda layer: synth.prior_h(wl.seed_prior, layer, lane, np.arange(wl.context), sh.d_model))
+    rp = orc.prefill(0, chunks[lane], L)
+    e_pre = rel_err(last, rp["logits"][-1])
+    record("ctx32k_lane_prefill", lane=lane, rel=e_pre)
+    assert e_pre <= REL_TOL, e_pre
+    assert token_ok(toks[lane], rp["logits"][-1])
+    r = orc.decode_step([0], [L], [toks[lane]])
+    e_dec = rel_err(lgd[lane], r["logits"][0])
+    record("ctx32k_lane_decode", lane=lane, rel=e_dec)
+    assert e_dec <= REL_TOL, e_dec
+    assert token_ok(int(t[lane]), r["logits"][0])
+    assert np.allclose(norms, orc.norms[0][:L], rtol=REL_TOL)
