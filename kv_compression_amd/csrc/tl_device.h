@@ -54,19 +54,21 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 // Merge of one (row, head)'s ns >= 1 key-split partials p[s] = (max m_s, sum
-// l_s, unnormalised o_s[DH]) by a block of 256 threads: o = sum_s w_s o_s /
-// sum_s w_s l_s with w_s = exp(m_s - M), M the largest m_s. Thread (dim,
-// group g) sums the splits s = g, g + G, ... for its dimension and the G group
-// sums are added in order g = 0, 1, ..., so the result depends only on ns and
-// the partials. Each thread loads its (m, l, o[dim]) of 32 / G splits at a
-// time, the first batch together with the maxima. Scratch: osum [256],
-// lsum [G], red [4] in LDS. Every thread of the block must call it. COHERENT:
-// read the partials with device-coherent loads (written in the same launch by
-// workgroups on other XCDs with device-coherent stores).
-template <typename T, int DH, bool COHERENT = false>
+// l_s, unnormalised o_s[DH]) by a block of NTH threads (blockDim.x == NTH):
+// o = sum_s w_s o_s / sum_s w_s l_s with w_s = exp(m_s - M), M the largest
+// m_s. Thread (dim, group g) sums the splits s = g, g + G, ... (G = NTH / DH)
+// for its dimension and the G group sums are added in order g = 0, 1, ...,
+// so the result depends only on ns, NTH and the partials. Each thread loads
+// its (m, l, o[dim]) of max(32 / G, 1) splits at a time, the first batch
+// together with the maxima. Scratch: osum [NTH], lsum [G], red [NTH / 64] in
+// LDS. Every thread of the block must call it. COHERENT: read the partials
+// with device-coherent loads (written in the same launch by workgroups on
+// other XCDs with device-coherent stores).
+template <typename T, int DH, bool COHERENT = false, int NTH = 256>
 __device__ __forceinline__ void merge_splits(const float* p, int ns, T* out, float* osum,
                                              float* lsum, float* red) {
-  constexpr int G = 256 / DH, U = 32 / G;
+  constexpr int G = NTH / DH, U = 32 / G > 1 ? 32 / G : 1;
+  static_assert(G * DH == NTH, "threads per merge");
   constexpr float kL2e = 1.4426950408889634f;
   const int t = threadIdx.x, dim = t % DH, g = t / DH;
   auto ld = [](const float* a) -> float {
@@ -85,7 +87,7 @@ __device__ __forceinline__ void merge_splits(const float* p, int ns, T* out, flo
   };
   load(0);
   float M = -__builtin_inff();
-  for (int s = t; s < ns; s += 256) M = fmaxf(M, ld(p + (size_t)s * (DH + 2)));
+  for (int s = t; s < ns; s += NTH) M = fmaxf(M, ld(p + (size_t)s * (DH + 2)));
   M = block_max(M, red);
   float acc = 0.f, lacc = 0.f;
   for (int c = 0; c < ns; c += G * U) {
@@ -144,19 +146,21 @@ __device__ __forceinline__ int int4_shift(int j) { return (j & 1) ? 16 + 4 * (j 
 // Dequantise 8 INT4 codes (one word) with scale s into 8 fp16: fp16(q * s).
 // (1024 + u) is exact in fp16; subtracting 1032 gives q exactly; the product
 // with s is one correctly rounded fp16 multiply.
+// (w >> 4i) & 0x000F000F | 0x64006400 is one three-input bitwise op (truth
+// table 0xEA: (a & b) | c); the four pairs are formed, then offset, then
+// scaled, so no packed op waits on the one right before it.
 __device__ __forceinline__ half8 int4_dequant8(uint32_t w, half_t s) {
-  half8 r;
   const half2v bias = {(half_t)1032.f, (half_t)1032.f};
   const half2v sv = {s, s};
+  half2v x[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t v = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-    half2v x = __builtin_bit_cast(half2v, v);
-    x = (x - bias) * sv;
-    r[2 * i] = x[0];
-    r[2 * i + 1] = x[1];
-  }
-  return r;
+  for (int i = 0; i < 4; ++i)
+    x[i] = __builtin_bit_cast(half2v, __builtin_amdgcn_bitop3_b32(w >> (4 * i), 0x000F000Fu, 0x64006400u, 0xEA));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = x[i] - bias;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = x[i] * sv;
+  return half8{x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
 }
 
 // Dequantise 4 INT8 codes (one word, two's complement bytes) into fp16(q * s).

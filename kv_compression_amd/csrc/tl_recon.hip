@@ -56,7 +56,9 @@ template <int DH> struct Cfg<half_t, TL_CACHE_H_INT4, DH> : CfgCodes<TL_CACHE_H_
 // INT4 codes with 64-wide heads: one head (K and V rows) per workgroup and two
 // workgroups per CU, so one workgroup's prologue and epilogue run under the
 // other's MFMAs, and a dispatch round that is only partly filled still
-// spreads over twice as many CUs
+// spreads over twice as many CUs. (Eight waves over 512 positions, one
+// workgroup per CU, time the same at 4096 positions and lose a third
+// dispatch round just past it.)
 template <> struct Cfg<half_t, TL_CACHE_H_INT4, 64> {
   static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 2;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
@@ -65,9 +67,9 @@ template <int MODE, int DH> struct Cfg<float, MODE, DH> {
   static constexpr int BF = 128, BJ = 128, WF = 64, WJ = 64, BK = 64, OCC = 1;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
-// every fp16 configuration shares BJ and WJ (split length)
-static_assert(Cfg<half_t, TL_CACHE_H_INT4, 64>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
-              Cfg<half_t, TL_CACHE_H_INT4, 128>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
+// the fp16 configurations other than INT4 at 64-wide heads share BJ and WJ
+// (split length)
+static_assert(Cfg<half_t, TL_CACHE_H_INT4, 128>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
               Cfg<half_t, TL_CACHE_H_INT8, 64>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
               Cfg<half_t, TL_CACHE_H_INT4, 64>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ &&
               Cfg<half_t, TL_CACHE_H_INT8, 64>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ, "fp16 tiles");
@@ -691,7 +693,123 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) vo
       if (st + 1 < nst) stage(std::integral_constant<int, 1>{}, nb_c, st + 1, ca, fbc, raw);
       dma_sync<0>();   // no copy may still be writing LDS past this point
     };
-    dispatch_nb<CB>(ncb, loop);
+    // A tile with at most one live 32-position block (the tile just past a
+    // multiple of BJ, or a context of a few positions) would leave its MFMAs
+    // to one wave: instead every wave takes RB / NW of the block's row blocks
+    // over the same stages, and the waves then hand their rows to wave 0,
+    // which runs the epilogue as if it had computed the block alone.
+    // With more waves than row blocks the waves past the row blocks only copy.
+    constexpr int RBT = RB >= NW ? RB / NW : 1;
+    static_assert((RB >= NW ? RBT * NW == RB : NW % RB == 0) && RB * 16 * 64 * 4 <= RING, "tail split");
+    const bool tail = Tn - j0 <= 32;
+    if (tail) {
+      const bool trows = wave_u * RBT < RB;
+      const int trow = min(wave_u * RBT, RB - RBT) * 32 + (l & 31);
+      const uint32_t tmask = j0 + (l & 31) < Tn ? 1u : 0u;
+      auto read_at = [&](const char* rb, int kk, Frag (&fa)[RBT]) {
+        const char* base = rb + trow * (BK * ES) + (((kk * 2 + hb) ^ aswz) * 16);
+#pragma unroll
+        for (int i = 0; i < RBT; ++i) fa[i] = *(const Frag*)(base + i * 32 * (BK * ES));
+      };
+      // block 0 of the tile: position l % 32, the same for every wave
+      auto read_rawt = [&](const char* rb, R& raw) {
+        const int pos = l & 31;
+        const char* hs = rb + W_BYTES + ((pos >> 4) * (32 * NQ) + hb * NQ * 16 + (pos & 15)) * 16;
+        if constexpr (MODE == TL_CACHE_H_INT4) {
+          raw.w[0] = *(const u32x4*)hs;
+          raw.s[0] = *(const uint32_t*)(rb + W_BYTES + H_BYTES + pos * 4);
+        } else {
+          raw.w[0][0] = *(const u32x4*)hs;
+          raw.w[0][1] = *(const u32x4*)(hs + 16 * 16);
+        }
+      };
+      half_t s8t = (half_t)0.f;
+      if constexpr (MODE == TL_CACHE_H_INT8)
+        s8t = tmask ? h_from_bits(*cv.int8_scale(a.layer, lane, j0 + (l & 31))) : (half_t)0.f;
+      auto b_fragt = [&](const R& raw, int kk) -> half8 {
+        if constexpr (MODE == TL_CACHE_H_INT4) {
+          const uint32_t sv = tmask ? raw.s[0] : 0u;
+          const half_t sc = h_from_bits((uint16_t)(kk < 2 ? (sv & 0xFFFFu) : (sv >> 16)));
+          return int4_dequant8(raw.w[0][kk], sc);
+        } else {
+          const u32x4& w = raw.w[0][kk >> 1];
+          const half4 lo = int8_dequant4(w[(kk & 1) * 2], s8t);
+          const half4 hi = int8_dequant4(w[(kk & 1) * 2 + 1], s8t);
+          return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+      };
+      // the copies go out and are waited for exactly as in `stage`
+      auto stage_t = [&](auto buf_c, int st, Frag (&ca)[RBT], half8& fbc, R& raw) {
+        constexpr int BUF = decltype(buf_c)::value;
+        constexpr int NXT = (BUF + 1) % 3, PREV = (BUF + 2) % 3;
+        const char* rb = Ring<BUF, RING>::p();
+        const int st2 = min(st + 2, nst - 1);
+        Frag na[RBT];
+        half8 fbn;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+          if (kk == 0) issue_ops(std::integral_constant<int, PREV>{}, IA1{}, IB1{}, st2);
+          if (kk == 1) issue_ops(std::integral_constant<int, PREV>{}, IB1{}, IC1{}, st2);
+          read_at(rb, kk + 1, na);
+          fbn = b_fragt(raw, kk + 1);
+          if (trows)
+#pragma unroll
+            for (int i = 0; i < RBT; ++i) acc[i][0] = Mma<T>::mma(ca[i], fbc, acc[i][0]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < RBT; ++i) ca[i] = na[i];
+          fbc = fbn;
+        }
+        dma_sync<DMA_PER_STAGE>();
+        issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IA1{}, min(st + 3, nst - 1));
+        read_rawt(Ring<NXT, RING>::p(), raw);
+        read_at(Ring<NXT, RING>::p(), 0, na);
+        fbn = b_fragt(raw, 0);
+        if (trows)
+#pragma unroll
+          for (int i = 0; i < RBT; ++i) acc[i][0] = Mma<T>::mma(ca[i], fbc, acc[i][0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < RBT; ++i) ca[i] = na[i];
+        fbc = fbn;
+      };
+      {
+        Frag ca[RBT];
+        half8 fbc;
+        R raw;
+        read_rawt(Ring<0, RING>::p(), raw);
+        read_at(Ring<0, RING>::p(), 0, ca);
+        fbc = b_fragt(raw, 0);
+        int st = 0;
+        for (; st + 3 <= nst; st += 3) {
+          stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+          stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
+          stage_t(std::integral_constant<int, 2>{}, st + 2, ca, fbc, raw);
+        }
+        if (st < nst) stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+        if (st + 1 < nst) stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
+        dma_sync<0>();
+      }
+      // row blocks w*RBT .. w*RBT+RBT-1 of wave w -> wave 0, through ring
+      // buffer 0 (no copy is in flight any more): [row block][element][lane]
+      float* xch = (float*)Ring<0, RING>::p();
+      if (wave_u > 0 && trows) {
+#pragma unroll
+        for (int i = 0; i < RBT; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) xch[((wave_u * RBT + i) * 16 + e) * 64 + l] = acc[i][0][e];
+      }
+      lds_sync();
+      if (wave_u == 0) {
+#pragma unroll
+        for (int i = RBT; i < RB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][0][e] = xch[(i * 16 + e) * 64 + l];
+      }
+      __syncthreads();   // the exchange is read before the epilogue reuses LDS
+    } else {
+      dispatch_nb<CB>(ncb, loop);
+    }
   } else {
     // ---- fp16 / fp32 h staged through LDS ----------------------------------
     // positions past T read the entry of position T-1 (always in bounds) and are
@@ -940,12 +1058,12 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) vo
       }
       __syncthreads();
       if (!last_tile) return;
-      static_assert(NWV * HPW_T * (DH + 2) >= 256 + 256 / DH + 4, "merge scratch within comb_lds");
+      static_assert(NWV * HPW_T * (DH + 2) >= NT + NT / DH + NT / 64, "merge scratch within comb_lds");
 #pragma unroll
       for (int g = 0; g < HPW; ++g) {
         const int head = hg * (BF / (2 * DH)) + g;
-        merge_splits<half_t, DH, true>(part_of(head, 0), n_t, (half_t*)a.o + (size_t)r * D + head * DH,
-                                       comb, comb + 256, comb + 256 + 256 / DH);
+        merge_splits<half_t, DH, true, NT>(part_of(head, 0), n_t, (half_t*)a.o + (size_t)r * D + head * DH,
+                                           comb, comb + NT, comb + NT + NT / DH);
       }
     }
   } else if constexpr (!kCross) {
@@ -1018,10 +1136,6 @@ bool combined_splits(const ModelView& m, int mode) {
   return m.dtype == TL_DTYPE_F16 && (mode == TL_CACHE_H_INT4 || mode == TL_CACHE_H_INT8);
 }
 
-int recon_split_len(const ModelView& m, int mode) {
-  if (combined_splits(m, mode)) return Cfg<half_t, TL_CACHE_H_INT4, 64>::BJ;
-  return m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32, 32>::WJ : Cfg<half_t, TL_CACHE_H_F16, 64>::WJ;
-}
 
 // features (K and V rows) per workgroup and positions per tile of the
 // configuration dispatch() picks
@@ -1034,14 +1148,21 @@ static int recon_bf(const ModelView& m, int mode) {
                 "other fp16 configurations");
   return 256;
 }
-static int recon_bj(const ModelView& m) {
-  return m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32, 32>::BJ : Cfg<half_t, TL_CACHE_H_F16, 64>::BJ;
+static int recon_bj(const ModelView& m, int mode) {
+  if (m.dtype == TL_DTYPE_F32) return Cfg<float, TL_CACHE_H_F32, 32>::BJ;
+  if (mode == TL_CACHE_H_INT4 && m.dh == 64) return Cfg<half_t, TL_CACHE_H_INT4, 64>::BJ;
+  return Cfg<half_t, TL_CACHE_H_F16, 64>::BJ;
+}
+
+int recon_split_len(const ModelView& m, int mode) {
+  if (combined_splits(m, mode)) return recon_bj(m, mode);
+  return m.dtype == TL_DTYPE_F32 ? Cfg<float, TL_CACHE_H_F32, 32>::WJ : Cfg<half_t, TL_CACHE_H_F16, 64>::WJ;
 }
 
 hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t s) {
   if (r.tilecnt && (!r.o || !combined_splits(m, r.cache.mode))) return hipErrorInvalidValue;
   const int BF = recon_bf(m, r.cache.mode);
-  const int BJ = recon_bj(m);
+  const int BJ = recon_bj(m, r.cache.mode);
   KArgs k{};
   k.cache = r.cache;
   k.layer = r.layer;
@@ -1079,7 +1200,7 @@ hipError_t launch_recon_store(const ModelView& m, const CacheView& c, int layer,
                               const void* w_qkv, void* kvbuf, const int32_t* status,
                               hipStream_t s) {
   const int BF = recon_bf(m, c.mode);
-  const int BJ = recon_bj(m);
+  const int BJ = recon_bj(m, c.mode);
   KArgs k{};
   k.cache = c;
   k.layer = layer;
