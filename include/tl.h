@@ -216,6 +216,30 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
                          int32_t* d_tokens_out, float* d_logits, int32_t* d_lane_status,
                          void* stream);
 
+/* For callers that cannot allocate device memory or take a workspace per
+ * call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): tl_decode_step with the same arguments, results and
+ * errors, whose step scratch (the rows' activations, logits, attention
+ * partials, argmax partials and tile counters) lives in a static array of the
+ * library, 16 MiB per GPU, held until the process ends; the cache's per-lane
+ * state stays in its workspace. It allocates nothing and enqueues the same
+ * kernels plus one fill that zeroes the tile counters. The step must fit:
+ * about n x (16 d_model + 2 d_mlp + 4 vocab) bytes for an fp16 model
+ * (24 d_model + 4 d_mlp + 4 vocab for fp32) plus
+ * n x n_heads x ceil(context / 64) x (d_head + 2) x 4 bytes of attention
+ * partials (ceil(context / 32) splits for stored K/V), where context is the
+ * longest lane's length + 1; a larger step returns TL_E_CAPACITY before
+ * anything is enqueued (the 407M shape with 4 lanes at 4224 positions needs
+ * about 2 MB). Explicit attention order only, and not
+ * the delta-KV mode (TL_E_UNSUPPORTED). Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads, other
+ * caches) race, and the caller must serialise them. The stream must belong to
+ * the current device. */
+tl_status tl_decode_step_static(tl_cache* c, int n, const int32_t* lanes, const int32_t* loops,
+                                const int32_t* d_tokens_in, float safety_threshold,
+                                int32_t* d_tokens_out, float* d_logits, int32_t* d_lane_status,
+                                void* stream);
+
 /* Self-speculative decoding, chain mode (features page, "Self-speculative
  * decoding"; the greedy-equality claim is in its "Tree speculative decoding"
  * section): one round for `lane`, whose cache holds positions 0 .. len-1 at

@@ -22,6 +22,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -658,17 +659,22 @@ tl_status tl_extend_depth(tl_cache* c, int lane, int pos0, int n, int old_loops,
   return TL_OK;
 }
 
-tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t* loops,
-                         const int32_t* d_tokens_in, float safety_threshold,
-                         int32_t* d_tokens_out, float* d_logits, int32_t* d_lane_status,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a decode call, before anything is enqueued; returns the deepest
+// loop count and the longest context of the call.
+tl_status decode_validate(tl_cache* c, int n, const int32_t* lanes, const int32_t* loops,
+                          const int32_t* d_tokens_in, float safety_threshold,
+                          const int32_t* d_tokens_out, const int32_t* d_lane_status, int* lmax_out,
+                          int* t_ub_out) {
   if (!c) return fail(TL_E_ARG, "null cache");
   if (n < 1 || n > c->ws.Bmax) return fail(TL_E_ARG, "n = %d not in [1, %d]", n, c->ws.Bmax);
   if (!lanes || !loops || !d_tokens_in || !d_tokens_out || !d_lane_status)
     return fail(TL_E_ARG, "null argument");
   if (isnan(safety_threshold)) return fail(TL_E_ARG, "NaN threshold");
-  const tl_model* m = c->m;
-  const ModelView& mv = m->mv;
+  const ModelView& mv = c->m->mv;
   std::vector<char> seen(c->n_lanes, 0);
   int lmax_call = 0, t_ub = 0;
   for (int k = 0; k < n; ++k) {
@@ -684,6 +690,19 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     lmax_call = std::max(lmax_call, L);
     t_ub = std::max(t_ub, c->host_len[lane] + 1);
   }
+  *lmax_out = lmax_call;
+  *t_ub_out = t_ub;
+  return TL_OK;
+}
+
+// The launches of one validated decode step on the step scratch of `ws` (the
+// cache's per-lane state, its other fields, is shared by every variant).
+tl_status decode_enqueue(tl_cache* c, const Workspace& ws, int n, const int32_t* lanes,
+                         const int32_t* loops, const int32_t* d_tokens_in, float safety_threshold,
+                         int32_t* d_tokens_out, float* d_logits, int32_t* d_lane_status, void* stream,
+                         int lmax_call, int t_ub) {
+  const tl_model* m = c->m;
+  const ModelView& mv = m->mv;
   // rows sorted by loop count, deepest first: the active rows of every layer form a prefix
   std::vector<int> order(n);
   for (int k = 0; k < n; ++k) order[k] = k;
@@ -695,7 +714,6 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     map.slot[r] = order[r];
   }
   hipStream_t s = (hipStream_t)stream;
-  const Workspace& ws = c->ws;
   const int D = mv.D;
   const float qscale = (float)(1.0 / sqrt((double)mv.dh));
   const bool check = !(safety_threshold == INFINITY);
@@ -822,6 +840,113 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
     c->host_len[lane] += 1;
   }
   return TL_OK;
+}
+
+// Step scratch of tl_decode_step_static, for callers that cannot allocate:
+// one array per GPU, held until the process ends. Host code uses only its
+// device address from hipGetSymbolAddress (taken once per device, on the
+// first call with that device current), never the name itself.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+tl_status static_scratch(char** out) {
+  int dev = -1;
+  TL_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TL_E_ARG, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(TL_E_HIP, "static scratch address: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t* loops,
+                         const int32_t* d_tokens_in, float safety_threshold,
+                         int32_t* d_tokens_out, float* d_logits, int32_t* d_lane_status,
+                         void* stream) {
+  int lmax_call = 0, t_ub = 0;
+  tl_status st = decode_validate(c, n, lanes, loops, d_tokens_in, safety_threshold, d_tokens_out,
+                                 d_lane_status, &lmax_call, &t_ub);
+  if (st != TL_OK) return st;
+  return decode_enqueue(c, c->ws, n, lanes, loops, d_tokens_in, safety_threshold, d_tokens_out,
+                        d_logits, d_lane_status, stream, lmax_call, t_ub);
+}
+
+tl_status tl_decode_step_static(tl_cache* c, int n, const int32_t* lanes, const int32_t* loops,
+                                const int32_t* d_tokens_in, float safety_threshold,
+                                int32_t* d_tokens_out, float* d_logits, int32_t* d_lane_status,
+                                void* stream) {
+  int lmax_call = 0, t_ub = 0;
+  tl_status st = decode_validate(c, n, lanes, loops, d_tokens_in, safety_threshold, d_tokens_out,
+                                 d_lane_status, &lmax_call, &t_ub);
+  if (st != TL_OK) return st;
+  if (c->mode == TL_CACHE_H_DELTA8 || c->order != TL_ATTN_EXPLICIT)
+    return fail(TL_E_UNSUPPORTED, "the static-scratch step covers the explicit order of the K/V and h modes "
+                                  "other than delta-KV");
+  // the step scratch of this call: rows, activations, logits, attention
+  // partials (splits of the longest context), argmax partials, tile counters
+  const tl_config& cfg = c->m->cfg;
+  const size_t D = cfg.d_model, F = cfg.d_mlp, V = cfg.vocab, es = dtype_size(cfg.dtype);
+  const int min_split = c->mode == TL_CACHE_KV ? kKvSplit : 64;
+  const int S = (t_ub + min_split - 1) / min_split;
+  const size_t sizes[15] = {
+      (size_t)n * 4, (size_t)n * 4, (size_t)n * 4, (size_t)n * 4,   // row_lane, row_slot, row_pos, row_dead
+      (size_t)n * D * 4, (size_t)n * D * es, (size_t)n * D * 4,      // x, h, q
+      (size_t)n * D * es, (size_t)n * D * es, (size_t)n * F * es,    // o, u, a
+      (size_t)n * D * es, (size_t)n * V * 4,                         // z, logits
+      (size_t)n * cfg.n_heads * S * (cfg.d_head + 2) * 4,            // part
+      (size_t)n * kArgChunks * 8,                                    // amax_v, amax_i
+      (size_t)n * (2 * D / 128) * 4,                                 // tilecnt
+  };
+  size_t off[15], total = 0;
+  for (int i = 0; i < 15; ++i) {
+    off[i] = total;
+    total = align256(total + sizes[i]);
+  }
+  if (total > kStaticScratchBytes)
+    return fail(TL_E_CAPACITY, "the step needs %zu bytes of static scratch (%d lanes, context %d); the limit is %zu",
+                total, n, t_ub, kStaticScratchBytes);
+  char* base = nullptr;
+  st = static_scratch(&base);
+  if (st != TL_OK) return st;
+  Workspace w = c->ws;   // per-lane state stays in the cache's workspace
+  w.row_lane = (int32_t*)(base + off[0]);
+  w.row_slot = (int32_t*)(base + off[1]);
+  w.row_pos = (int32_t*)(base + off[2]);
+  w.row_dead = (int32_t*)(base + off[3]);
+  w.x = (float*)(base + off[4]);
+  w.h = base + off[5];
+  w.q = (float*)(base + off[6]);
+  w.o = base + off[7];
+  w.u = base + off[8];
+  w.a = base + off[9];
+  w.z = base + off[10];
+  w.logits = (float*)(base + off[11]);
+  w.part = (float*)(base + off[12]);
+  w.amax_v = (float*)(base + off[13]);
+  w.amax_i = (int32_t*)(base + off[13] + (size_t)n * kArgChunks * 4);
+  w.tilecnt = (int32_t*)(base + off[14]);
+  w.S = S;
+  w.R = n;
+  w.Bmax = n;
+  w.kvbuf = nullptr; w.ppart = nullptr; w.ppart_floats = 0; w.spec = nullptr;
+  w.hrec = nullptr; w.hmat = nullptr; w.qt = nullptr; w.apart = nullptr; w.apair_cap = 0;
+  // the array keeps the last call's contents: the attention's tile counters
+  // must start at zero (a fill kernel, so the call can be captured in a graph)
+  TL_HIP(launch_fill_i32(w.tilecnt, n * (int)(2 * D / 128), 0, (hipStream_t)stream));
+  return decode_enqueue(c, w, n, lanes, loops, d_tokens_in, safety_threshold, d_tokens_out, d_logits,
+                        d_lane_status, stream, lmax_call, t_ub);
 }
 
 tl_status tl_spec_step(tl_cache* c, int lane, int draft_loops, int verify_loops, int draft_ahead,

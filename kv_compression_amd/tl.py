@@ -56,7 +56,8 @@ EXPORTS = ("tl_version", "tl_last_error", "tl_model_create", "tl_model_destroy",
            "tl_prefill_chunk", "tl_decode_step", "tl_residual_norms", "tl_lane_residual",
            "tl_cache_write_h", "tl_cache_fill_synthetic", "tl_cache_set_length",
            "tl_cache_read", "tl_cache_reset_lane", "tl_profile_start", "tl_profile_stop",
-           "tl_prefill_chunk_x", "tl_extend_depth", "tl_spec_step", "tl_cache_set_attention")
+           "tl_prefill_chunk_x", "tl_extend_depth", "tl_spec_step", "tl_cache_set_attention",
+           "tl_decode_step_static")
 
 
 def load(path: str = LIB_PATH):
@@ -82,6 +83,7 @@ def load(path: str = LIB_PATH):
         "tl_prefill_chunk_x": (I, [P, I, I, P, I, P, P, P, P]),
         "tl_extend_depth": (I, [P, I, I, I, I, I, P, P, P, P]),
         "tl_decode_step": (I, [P, I, P, P, P, F, P, P, P, P]),
+        "tl_decode_step_static": (I, [P, I, P, P, P, F, P, P, P, P]),
         "tl_spec_step": (I, [P, I, I, I, I, P, P, ctypes.POINTER(I), P]),
         "tl_cache_set_attention": (I, [P, I]),
         "tl_residual_norms": (I, [P, I, P, P]),
@@ -226,6 +228,15 @@ class Cache:
         _check(_lib.tl_decode_step(self.handle, n, la, lo, _ptr(d_tokens_in), float(threshold),
                                    _ptr(d_tokens_out), _ptr(d_logits), _ptr(d_lane_status),
                                    _stream(stream)))
+
+    def tl_decode_step_static(self, lanes: Sequence[int], loops: Sequence[int], d_tokens_in, threshold,
+                              d_tokens_out, d_logits, d_lane_status, stream=None):
+        n = len(lanes)
+        la = (ctypes.c_int32 * n)(*lanes)
+        lo = (ctypes.c_int32 * n)(*loops)
+        _check(_lib.tl_decode_step_static(self.handle, n, la, lo, _ptr(d_tokens_in), float(threshold),
+                                          _ptr(d_tokens_out), _ptr(d_logits), _ptr(d_lane_status),
+                                          _stream(stream)))
 
     def tl_spec_step(self, lane, draft_loops, verify_loops, draft_ahead, d_token_in, d_tokens_out,
                      stream=None) -> int:
