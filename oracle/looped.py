@@ -268,6 +268,15 @@ class LoopedOracle:
         self.status = [LANE_OK] * n_lanes
         self.norms = [np.full(l_max, np.nan) for _ in range(n_lanes)]
         self.trace: Dict[int, list] = {}           # per-lane stage snapshots of the last call
+        # Test hooks, inert unless a test sets them (they change no arithmetic):
+        # h_log, when a dict, receives for every row write_h stores the h row in
+        # the h dtype and the float32 row its codec is applied to (the h itself;
+        # in the delta mode's loop layers h minus the reconstruction below), keyed
+        # (layer, lane, pos); row_override maps (layer, lane, pos) to a row stored
+        # in place of the encoded one: dict(q=int8 codes, s=fp16 scales) for the
+        # INT codecs, dict(h=row) for float h.
+        self.h_log: Optional[dict] = None
+        self.row_override: Dict[Tuple[int, int, int], dict] = {}
 
     # -- rounding points ----------------------------------------------------
     def _rd(self, a: np.ndarray) -> np.ndarray:
@@ -303,6 +312,7 @@ class LoopedOracle:
         n = h.shape[0]
         if pos0 + n > self.max_seq:
             raise CapacityError("cache full")
+        codec_in = None
         if self.mode in ("f32", "f16"):
             slot["h"][pos0:pos0 + n] = h
         elif self.mode == "int8":
@@ -319,6 +329,7 @@ class LoopedOracle:
                 # the reader rebuilds it, so quantisation errors do not pile up
                 r_prev = self.delta_rec(layer - 1, lane, pos0, n)
                 d = h.astype(np.float16).astype(np.float32) - r_prev
+                codec_in = d
                 q, s = delta_encode(d, self.d)
                 slot["q"][pos0:pos0 + n], slot["s"][pos0:pos0 + n] = q, s
         else:
@@ -326,6 +337,19 @@ class LoopedOracle:
             hf = np.asarray(h, dtype=np.float64)
             slot["k"][pos0:pos0 + n] = self._rd(hf @ W["wk"].T)      # R5
             slot["v"][pos0:pos0 + n] = self._rd(hf @ W["wv"].T)
+        if self.mode != "kv" and (self.h_log is not None or self.row_override):
+            for r in range(n):
+                key = (layer, lane, pos0 + r)
+                if self.h_log is not None:
+                    hr = np.asarray(h[r]) if self.exact else np.asarray(h[r]).astype(self.dt)
+                    cin = codec_in[r] if codec_in is not None else hr.astype(np.float32)
+                    self.h_log[key] = (hr.copy(), np.array(cin, np.float32))
+                ov = self.row_override.get(key)
+                if ov is not None:
+                    if "h" in ov:
+                        slot["h"][pos0 + r] = ov["h"]
+                    else:
+                        slot["q"][pos0 + r], slot["s"][pos0 + r] = ov["q"], ov["s"]
 
     def delta_rec(self, layer: int, lane: int, pos0: int, n: int) -> np.ndarray:
         """Delta mode, float32 rows of positions pos0..pos0+n-1: a unique layer's

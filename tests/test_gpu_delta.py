@@ -15,14 +15,11 @@ import pytest
 
 import oracle
 import synth
-from tests._gpu_util import REL_TOL, decode, gpu_model, record, rel_err, token_ok, torch_gpu
+from tests._gpu_util import REL_TOL, decode, decode_synced, gpu_model, record, rel_err, token_ok, torch_gpu
 
 pytestmark = pytest.mark.gpu
 
 S407 = synth.SHAPES["407m"]
-INT_FLIP_TOL = 3e-2
-
-
 def _trajectory(n, n_layers, seed, D):
     """fp16 h rows per layer that settle geometrically (like the loop's
     converging trajectory), with edge rows: identical layers (zero deltas),
@@ -133,15 +130,17 @@ def test_delta_first_tokens_on_empty_lane():
     orc = oracle.LoopedOracle(S407, w, "delta8", 2, 24, 3)
     toks = [17, 31999]
     for step in range(12):
-        t, lg, st = decode(c, [0, 1], [3, 1], toks)
-        r = orc.decode_step([0, 1], [3, 1], toks)
+        # delta codes decided on the other side of a rounding boundary are
+        # proven rounding-boundary decisions on the oracle's h and adopted by
+        # the oracle
+        t, lg, st, r, _ = decode_synced(c, orc, [0, 1], [3, 1], toks)
         assert np.all(st == 0) and np.all((t >= 0) & (t < S407.vocab))
         for k in range(2):
             ref = r["logits"][k]
             e = rel_err(lg[k], ref)
             record("delta_empty_lane", lane=k, step=step, rel=e)
-            assert e <= INT_FLIP_TOL, (step, k, e)
-            assert ref[t[k]] >= ref.max() - INT_FLIP_TOL * np.abs(ref).max(), (step, k)
+            assert e <= REL_TOL, (step, k, e)
+            assert token_ok(int(t[k]), ref), (step, k)
         toks = [int(x) for x in t]
 
 

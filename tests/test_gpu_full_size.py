@@ -18,16 +18,11 @@ import pytest
 
 import oracle
 import synth
-from tests._gpu_util import REL_TOL, decode, gpu_model, record, rel_err, token_ok, torch_gpu
+from tests._gpu_util import REL_TOL, decode, decode_synced, gpu_model, record, rel_err, token_ok, torch_gpu
 
 pytestmark = pytest.mark.gpu
 
 _PRIOR = {}
-
-# Logit band for INT4 / INT8 caches at contexts of a few positions, where a
-# single code that upstream FP32-vs-FP64 rounding flips is not diluted.
-INT_FLIP_TOL = 3e-2
-
 
 def prior(seed, layer, lane, n, d_model):
     key = (seed, layer, lane, n, d_model)
@@ -137,19 +132,15 @@ def test_first_token_on_empty_lane(mode):
     """A lane with nothing cached decodes its first tokens: T = 1, 2, 3, one
     position in a 256-position tile, every layer appending before it reads.
 
-    With the float caches the logits meet the 2e-3 bar. With INT4 / INT8 the
-    attention output at T = 1 is the decoded h' of that single token, and a
-    code or scale that upstream rounding (FP32 against FP64 residuals) puts
-    on the other side of a rounding boundary changes it by a whole
-    quantisation step, which no later position dilutes: there the test
-    checks what is unique instead (layer 0, whose h depends on the token
-    alone, holds the oracle's codes in all but at most one group; the step is
-    bitwise repeatable; statuses and tokens are valid) and holds the logits
-    to the code-flip band INT_FLIP_TOL: flips move them by at most about
-    2e-2 of their peak here (falling with T as later positions dilute the
-    flipped ones), while a wrong row, position or tile mask moves them by
-    O(1). The GPU's token must then be within that band of the oracle's best
-    logit. The 2e-3 bar for the INT modes is checked at long contexts."""
+    Every step meets the 2e-3 bar and the near-tie token rule. With INT4 /
+    INT8 the attention output at T = 1 is the decoded h' of that single
+    token, so a code or scale that the FP32 (GPU) and FP64 (oracle) residuals
+    put on different sides of a rounding boundary changes it by a whole
+    quantisation step that no later position dilutes. Each such group is
+    proven to be exactly that (the codec's result for an h within the 2e-3
+    float bar of the oracle's own, normwise over the row) and the oracle then
+    adopts it (decode_synced), so the comparison is of the same caches; any
+    other code difference fails. The steps are also bitwise repeatable."""
     torch = torch_gpu()
     sh = synth.SHAPES["407m"]
     w, gm = gpu_model(sh)
@@ -160,37 +151,25 @@ def test_first_token_on_empty_lane(mode):
         orc = oracle.LoopedOracle(sh, w, mode, 2, 48, 3)
         toks = [17, 31999]
         outs = []
+        adopted = 0
         for step in range(36):
-            t, lg, st = decode(c, [0, 1], [3, 1], toks)
-            r = orc.decode_step([0, 1], [3, 1], toks)
-            assert np.all(st == 0) and np.all((t >= 0) & (t < sh.vocab))
             if exact_codec:
-                check_lanes("edge_empty_lane", [0, 1], r, t, lg, st, dict(mode=mode, step=step))
+                t, lg, st = decode(c, [0, 1], [3, 1], toks)
+                r = orc.decode_step([0, 1], [3, 1], toks)
             else:
-                for k in range(2):
-                    ref = r["logits"][k]
-                    e = rel_err(lg[k], ref)
-                    record("edge_empty_lane_int", lane=k, mode=mode, step=step, rel=e)
-                    assert e <= INT_FLIP_TOL, (mode, step, k, e)
-                    assert ref[t[k]] >= ref.max() - INT_FLIP_TOL * np.abs(ref).max(), (mode, step, k)
+                t, lg, st, r, n = decode_synced(c, orc, [0, 1], [3, 1], toks)
+                adopted += n
+            assert np.all(st == 0) and np.all((t >= 0) & (t < sh.vocab))
+            check_lanes("edge_empty_lane", [0, 1], r, t, lg, st, dict(mode=mode, step=step))
             outs.append((t.copy(), lg.copy()))
             toks = [int(x) for x in t]
-        return c, orc, outs
+        record("edge_empty_lane_adopted_rows", mode=mode, rows=adopted)
+        return outs
 
-    c, orc, outs = run()
-    if not exact_codec:
-        ng = sh.d_model // 32 if mode == "int4" else 1
-        codes = torch.empty((1, sh.d_model), dtype=torch.int8, device="cuda")
-        scales = torch.empty((1, ng), dtype=torch.int16, device="cuda")
-        c.tl_cache_read(0, 0, 0, 1, codes, scales)
-        torch.cuda.synchronize()
-        q_ref, s_ref = orc.read_codes(0, 0, 0, 1)
-        q, sc = codes.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
-        bad = np.any((q != q_ref).reshape(ng, -1), axis=-1) | (sc[0] != s_ref.view(np.uint16)[0])
-        assert bad.sum() <= 1, bad.sum()
-        _, _, outs2 = run()
-        for (t1, l1), (t2, l2) in zip(outs, outs2):
-            assert np.array_equal(t1, t2) and np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+    outs = run()
+    outs2 = run()
+    for (t1, l1), (t2, l2) in zip(outs, outs2):
+        assert np.array_equal(t1, t2) and np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
 def test_max_batch_256_lanes():
