@@ -57,27 +57,34 @@ def recon_flops_bytes(shape, mode_entry_bytes, lanes, loops, t_values):
     return flops, hbytes, launches
 
 
-KERNEL_SOURCES = ("kv_compression_amd/csrc/tl_recon.hip", "kv_compression_amd/csrc/tl_device.h",
-                  "kv_compression_amd/csrc/tl_internal.h")
+# the source files each measured kernel is built from: traffic counters taken
+# on other sources do not describe the kernel that runs
+_COMMON = ("kv_compression_amd/csrc/tl_device.h", "kv_compression_amd/csrc/tl_internal.h")
+KERNEL_SOURCES = {
+    "recon_attn": ("kv_compression_amd/csrc/tl_recon.hip",) + _COMMON,
+    "kv_attn": ("kv_compression_amd/csrc/tl_attn.hip",) + _COMMON,
+    "absorbed_attn": ("kv_compression_amd/csrc/tl_absorbed.hip",) + _COMMON,
+    "delta_mat": ("kv_compression_amd/csrc/tl_rowops.hip",) + _COMMON,
+    "decode_gemm": ("kv_compression_amd/csrc/tl_gemm.hip",) + _COMMON,
+}
 
 
-def kernel_sources_sha256() -> str:
-    """Hash of the attention kernel's sources: traffic counters taken on other
-    sources do not describe the kernel that runs."""
+def kernel_sources_sha256(kernel: str = "recon_attn") -> str:
+    """Hash of a kernel's sources."""
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def load_traffic(workload: str, mode: str):
-    """HBM bytes per launch of the attention kernel from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE passes, each calibrated on a copy of
-    known size), or None if there is none for this workload or it was taken on
-    different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "recon_attn_%s_%s_traffic.txt" % (workload, mode))
+def load_traffic(workload: str, mode: str, kernel: str = "recon_attn"):
+    """HBM bytes per launch of `kernel` from its committed counter summary
+    (profiles/<kernel>_<workload>_<mode>_traffic.txt: FETCH_SIZE and
+    WRITE_SIZE passes, each calibrated on a copy of known size), or None if
+    there is none or it was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_%s_traffic.txt" % (kernel, workload, mode))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -86,12 +93,26 @@ def load_traffic(workload: str, mode: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def blas_info() -> str:
+    """The BLAS numpy runs on, with its version, threading layer and threads."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            i = info[0]
+            return "%s %s (%s), %d threads" % (i.get("internal_api"), i.get("version"),
+                                              i.get("threading_layer"), i.get("num_threads", 0))
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def cpu_baseline(shape, w, mode, context, loops, budget_s=12.0, max_steps=64):
@@ -121,11 +142,12 @@ def cpu_baseline(shape, w, mode, context, loops, budget_s=12.0, max_steps=64):
             break
     dt = time.perf_counter() - t0
     return {"value": steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "blas": blas_info(),
             "sample": "1 lane x %d decode steps at context %d, %s-h, L=%d, FP64 numpy oracle "
                       "(%.1f s)" % (steps, context, mode, L, dt)}
 
 
-def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, order="explicit"):
+def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, order="explicit", repeats=1):
     """Prefill the workload's lanes in `mode`, time K decode steps after W
     warm-up steps (inputs resident in HBM), then, if `profile`, time the
     attention kernel alone over another K steps with HIP events on its stream.
@@ -185,6 +207,15 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, orde
     assert np.all(st_host == 0), "a lane aborted during the benchmark"
     value = wl.lanes * K / wall
     log("%s decode %d steps: %.1f ms wall, %.1f ms events, %.0f tok/s" % (mode, K, wall * 1e3, gpu_ms, value))
+    runs = [value]
+    for _ in range(repeats - 1):
+        # the same K steps again from the same state
+        reset()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        run(K)
+        torch.cuda.synchronize()
+        runs.append(wl.lanes * K / (time.perf_counter() - t1))
 
     roof = None
     extra = {}
@@ -203,7 +234,8 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, orde
         flops, hbytes, n_launch = recon_flops_bytes(shape, eb, lanes, loops, t_values)
         assert n_launch == launches, (n_launch, launches)
         avg_ms = kern_ms / launches
-        traffic = load_traffic(wl.name, mode) if order == "explicit" else None
+        kname = ("absorbed_attn" if order == "absorbed" else "recon_attn") if mode != "kv" else "kv_attn"
+        traffic = load_traffic(wl.name, mode, kname)
         if order == "absorbed":
             roof = dict(absorbed_roofline(shape, loops, t_values, kern_ms, eb), traffic=traffic)
         elif mode == "kv":
@@ -215,6 +247,7 @@ def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, orde
             roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": traffic}
         extra = {"kernel": ("absorbed_attn" if order == "absorbed" else "recon_attn") if mode != "kv" else "kv_attn",
+                 "runs_tok_s": [round(v, 2) for v in runs], "median_tok_s": round(float(np.median(runs)), 2),
                  "kernel_avg_us": round(avg_ms * 1e3, 2), "kernel_launches": launches,
                  "kernel_share_of_step": round(kern_ms / gpu_ms, 3),
                  "flops_per_launch": flops / launches,
@@ -318,7 +351,7 @@ def absorbed_roofline(shape, loops, t_values, kern_ms, entry_bytes):
             "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
-def decode_both_orders(torch, tl, wl, loops, steps, warmup, label):
+def decode_both_orders(torch, tl, wl, loops, steps, warmup, label, orders=("explicit", "absorbed")):
     """A 2B INT4-h batch over wl.context synthetic prior positions in every
     layer a lane uses, decoded in both attention orders: tokens/s, the
     attention kernel's average launch time and its roofline (MFMA for the
@@ -359,7 +392,7 @@ def decode_both_orders(torch, tl, wl, loops, steps, warmup, label):
     st = torch.empty_like(tin)
     start = ctx + wl.chunk
     t_values = [start + warmup + 1 + s for s in range(steps)]
-    for order in ("explicit", "absorbed"):
+    for order in orders:
         cache.tl_cache_set_attention(order)
         for k in range(wl.lanes):
             cache.tl_cache_set_length(k, start, sh.n_pre + loops[k])
@@ -387,9 +420,11 @@ def decode_both_orders(torch, tl, wl, loops, steps, warmup, label):
             # fp16 MFMA peak
             tf = flops / (kern_ms * 1e-3) / 1e12
             out[order]["roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP16_TFLOPS,
-                                      "unit": "TFLOP/s", "frac": round(tf / PEAK_FP16_TFLOPS, 4)}
+                                      "unit": "TFLOP/s", "frac": round(tf / PEAK_FP16_TFLOPS, 4),
+                                      "traffic": load_traffic(wl.name, "int4", "recon_attn")}
         else:
-            out[order]["roofline"] = absorbed_roofline(sh, loops, t_values, kern_ms, eb)
+            out[order]["roofline"] = dict(absorbed_roofline(sh, loops, t_values, kern_ms, eb),
+                                          traffic=load_traffic(wl.name, "int4", "absorbed_attn"))
         log("%s %s: %.1f tok/s, %.2f ms/step, %s" % (label, order, wl.lanes * steps / wall, wall * 1e3 / steps,
                                                     out[order]["roofline"]))
     del cache, model
@@ -397,21 +432,126 @@ def decode_both_orders(torch, tl, wl, loops, steps, warmup, label):
     return out
 
 
-def measure_laware(torch, tl, steps=64, warmup=1):
+def measure_tiny(torch, tl, steps=256, warmup=8):
+    """The tiny fp32 looped decoder (d_model 128, 4 heads of 32, MLP 512,
+    n_pre 1, L = 2, vocab 256, one lane): one decode step after 64 synthetic
+    prior positions in every layer, with the safety norm checked against 50,
+    repeated from the same state (the length is set back before each step), in
+    fp32-h (K/V rebuilt on fp32 MFMA) and in the stored-K/V reference mode."""
+    import synth
+    wl = synth.workload("tiny-f32-ctx64")
+    sh, ctx, L = wl.shape, wl.context, wl.l_max
+    model = tl.Model(sh, tl.upload_weights(sh, synth.make_weights(sh, wl.seed_weights)))
+    tok = torch.tensor(synth.make_prompts(sh.vocab, 1, 1, wl.seed_prompt)[:, 0].astype(np.int32), device="cuda")
+    out = {"workload": wl.name, "context": ctx, "loops": L, "threshold": wl.threshold}
+    for mode in wl.modes:
+        c = tl.Cache(model, mode, 1, ctx + 2, L)
+        for layer in range(sh.n_pre + L):
+            c.tl_cache_fill_synthetic(0, layer, 0, ctx, wl.seed_prior)
+        tout = torch.empty_like(tok)
+        st = torch.empty_like(tok)
+
+        def run(n):
+            for _ in range(n):
+                c.tl_cache_set_length(0, ctx, sh.n_pre + L)
+                c.tl_decode_step([0], [L], tok, wl.threshold, tout, None, st)
+
+        run(warmup)
+        torch.cuda.synchronize()
+        c.tl_profile_start()
+        t0 = time.perf_counter()
+        run(steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms, launches = c.tl_profile_stop()
+        assert int(st.cpu()[0]) == 0
+        out[mode] = {"ms_per_step": round(wall * 1e3 / steps, 4), "tok_s": round(steps / wall, 1),
+                     "attention_kernel_avg_us": round(kern_ms * 1e3 / launches, 2)}
+        log("tiny fp32 %s: %.3f ms per step, attention %.2f us" % (mode, wall * 1e3 / steps,
+                                                                  kern_ms * 1e3 / launches))
+        del c
+    del model
+    torch.cuda.synchronize()
+    return out
+
+
+def measure_f16h_ctx1024(torch, tl, steps=128, warmup=2):
+    """The 407M shape with fp16 h, one lane: a 1024-token prompt prefilled in
+    chunks of 512, then greedy decoding at L = 8 (128 steps), with the attention
+    kernel's MFMA roofline."""
+    import synth
+    wl = synth.workload("407m-f16h-ctx1024")
+    sh, ctx, L = wl.shape, wl.context, wl.l_max
+    model = tl.Model(sh, tl.upload_weights(sh, synth.make_weights(sh, wl.seed_weights)))
+    prompt = synth.make_prompts(sh.vocab, 1, ctx, wl.seed_prompt)[0]
+    c = tl.Cache(model, "f16", 1, ctx + steps + warmup + 1, L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    nxt, _ = c.prefill(0, prompt, L)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t0
+    a, b = nxt.clone(), torch.empty_like(nxt)
+    st = torch.empty_like(nxt)
+    for _ in range(warmup):
+        c.tl_decode_step([0], [L], a, wl.threshold, b, None, st)
+        a, b = b, a
+    c.tl_cache_set_length(0, ctx, sh.n_pre + L)
+    a.copy_(nxt)
+    torch.cuda.synchronize()
+    c.tl_profile_start()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        c.tl_decode_step([0], [L], a, wl.threshold, b, None, st)
+        a, b = b, a
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms, launches = c.tl_profile_stop()
+    assert int(st.cpu()[0]) == 0
+    eb = c.cache_bytes / ((sh.n_pre + L) * (ctx + steps + warmup + 1))
+    flops, _, n_launch = recon_flops_bytes(sh, eb, [0], [L], [ctx + 1 + s for s in range(steps)])
+    assert n_launch == launches, (n_launch, launches)
+    tf = flops / (kern_ms * 1e-3) / 1e12
+    out = {"workload": wl.name, "context": ctx, "loops": L, "decode_steps": steps,
+           "prefill_s": round(prefill_s, 4), "decode_tok_s": round(steps / wall, 1),
+           "ms_per_step": round(wall * 1e3 / steps, 4),
+           "attention_kernel_avg_us": round(kern_ms * 1e3 / launches, 2),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_FP16_TFLOPS, 4),
+                        "traffic": load_traffic(wl.name, "f16", "recon_attn")}}
+    log("407M fp16-h context 1024: %.1f tok/s, attention %.2f us, %s" % (steps / wall, kern_ms * 1e3 / launches,
+                                                                      out["roofline"]))
+    del c, model
+    torch.cuda.synchronize()
+    return out
+
+
+def measure_laware(torch, tl, steps=64, warmup=1, orders=("explicit", "absorbed")):
     """The 2B L-aware batch: 48 lanes with loops [4, 16, 32] on one 34-layer
     cache, 2048 positions."""
     import synth
     wl = synth.workload("2b-int4h-laware-b48")
-    return decode_both_orders(torch, tl, wl, wl.lane_loops(), steps, warmup, "L-aware 2B")
+    return decode_both_orders(torch, tl, wl, wl.lane_loops(), steps, warmup, "L-aware 2B", orders)
 
 
-def measure_long(torch, tl, steps=32, warmup=1):
+def measure_long(torch, tl, steps=32, warmup=1, orders=("explicit", "absorbed")):
     """The 2B long-context batch: 8 lanes at L = 8 over 32768 positions in all
     10 layers, one 512-token prefill chunk per lane, then the decode steps."""
     import synth
     wl = synth.workload("2b-int4h-ctx32k-b8")
     L = max(wl.lane_loops())
-    return decode_both_orders(torch, tl, wl, [L] * wl.lanes, steps, warmup, "long-context 2B")
+    return decode_both_orders(torch, tl, wl, [L] * wl.lanes, steps, warmup, "long-context 2B", orders)
+
+
+def calib_copy(torch):
+    """Three device copies of 64 MiB: what the FETCH_SIZE / WRITE_SIZE counters
+    read for a known number of bytes, which calibrates a counter run."""
+    src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("calibration copy: 3 x 64 MiB")
 
 
 def main():
@@ -427,8 +567,10 @@ def main():
     ap.add_argument("--no-profile-pass", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="measure only --mode (skip the workload's other cache modes)")
-    ap.add_argument("--leg", choices=["laware_2b", "long_context_2b"],
+    ap.add_argument("--leg", choices=["laware_2b", "long_context_2b", "tiny_f32", "f16h_ctx1024"],
                     help="run only this 2B measurement and print its JSON object (for profiling it)")
+    ap.add_argument("--leg-orders", default="both", choices=["both", "explicit"],
+                    help="attention orders a 2B leg decodes in (explicit: the reconstruction kernel alone)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="end with a 64 MiB device copy (calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
     args = ap.parse_args()
@@ -446,8 +588,15 @@ def main():
         sys.exit(1)
     tl.load()
     if args.leg:
-        fn = measure_laware if args.leg == "laware_2b" else measure_long
-        print(json.dumps({args.leg: fn(torch, tl)}), flush=True)
+        fn = {"laware_2b": measure_laware, "long_context_2b": measure_long, "tiny_f32": measure_tiny,
+              "f16h_ctx1024": measure_f16h_ctx1024}[args.leg]
+        if args.leg in ("laware_2b", "long_context_2b") and args.leg_orders == "explicit":
+            res = fn(torch, tl, orders=("explicit",))
+        else:
+            res = fn(torch, tl)
+        if args.calib_copy:
+            calib_copy(torch)
+        print(json.dumps({args.leg: res}), flush=True)
         return
     wl = synth.workload(args.workload)
     shape = wl.shape
@@ -461,7 +610,7 @@ def main():
 
     value, wall, roof, extra, prefill_s, kv_bytes = measure_mode(
         torch, tl, model, wl, shape, args.mode, prompts, K, W, not args.no_profile_pass,
-        order=args.order)
+        order=args.order, repeats=3)
 
     # the absorbed evaluation order of the same decode (attention over h'
     # with W_k^T q, W_v applied to the weighted sums)
@@ -503,10 +652,12 @@ def main():
         spec = measure_spec(torch, tl, rc, shape, context, L, int(nxt.cpu()[0]))
         del rc
 
-    laware = long2b = None
+    laware = long2b = tiny = f16h = None
     if not args.headline_only:
         laware = measure_laware(torch, tl)
         long2b = measure_long(torch, tl)
+        tiny = measure_tiny(torch, tl)
+        f16h = measure_f16h_ctx1024(torch, tl)
 
     # the other cache modes of the workload (fewer steps), each with its own
     # attention kernel roofline
@@ -522,13 +673,7 @@ def main():
                          "roofline": r2, "prefill": x2.get("prefill")}
 
     if args.calib_copy:
-        src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
-        src.fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("calibration copy: 3 x 64 MiB")
+        calib_copy(torch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -561,6 +706,8 @@ def main():
         "absorbed_order": absorbed,
         "laware_2b": laware,
         "long_context_2b": long2b,
+        "tiny_f32": tiny,
+        "f16h_ctx1024": f16h,
         "warm_start": resume,
         "speculative": spec,
     }
