@@ -786,7 +786,7 @@ tl_status decode_enqueue(tl_cache* c, const Workspace& ws, int n, const int32_t*
                                    W.w_qkv, ws.qt, ws.o, s));
         split_len = 0;
       } else {
-        // INT4 / INT8 h: the attention kernel merges its own tiles into o
+        // fp16 models: the attention kernel merges its own tiles into o
         const bool fused = combined_splits(mv, ra.cache.mode);
         if (fused) {
           ra.o = ws.o;

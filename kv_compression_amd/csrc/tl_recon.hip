@@ -992,12 +992,57 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) vo
   auto part_of = [&](int head, int sp) -> float* {
     return a.part + (((size_t)r * a.H + head) * a.S + sp) * (DH + 2);
   };
+  constexpr int HG = BF / (2 * DH);   // heads of the workgroup
+  // Partial of head g (0 .. HG-1) of the tile: M, L, O[dim] to the partial
+  // buffer, with device-coherent stores when the launch merges its own tiles
+  // (the merging workgroup may sit on another XCD).
+  auto store_partial = [&](int g, int dim, float M, float L, float O) {
+    float* dst = part_of(hg * HG + g, ptile);
+    if (a.tilecnt) {
+      if (dim == 0) {
+        __hip_atomic_store(dst, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(dst + 2 + dim, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (dim == 0) { dst[0] = M; dst[1] = L; }
+      dst[2 + dim] = O;
+    }
+  };
+  // The workgroup that completes a (row, head group) merges the row's tiles
+  // for those heads, exactly as the split merge would. The partials went out
+  // with device-coherent stores, which have completed (vmcnt 0) before the
+  // workgroup counts itself; the last one reads them with device-coherent
+  // loads. No cache is written back or invalidated, so the W rows and h codes
+  // other workgroups share in L2 stay there. It also zeroes the count for the
+  // next launch. scratch: NT + NT / DH + NT / 64 floats of LDS.
+  auto count_and_merge = [&](float* scratch) {
+    __shared__ int last_tile;
+    const int n_t = (Tn + BJ - 1) / BJ;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      int* cnt = a.tilecnt + r * a.n_hg + hg;
+      const int done = atomicAdd(cnt, 1) + 1;
+      last_tile = done == n_t;
+      if (done == n_t) atomicExch(cnt, 0);
+    }
+    __syncthreads();
+    if (!last_tile) return;
+#pragma unroll
+    for (int g = 0; g < HG; ++g) {
+      const int head = hg * HG + g;
+      merge_splits<T, DH, true, NT>(part_of(head, 0), n_t, (T*)a.o + (size_t)r * D + head * DH, scratch,
+                                    scratch + NT, scratch + NT + NT / DH);
+    }
+  };
   if constexpr (B_REG) {
     // Every wave holds all heads of the tile for its positions: each writes
     // its (max, sum, o) per head to LDS (a wave with no position < T writes
     // the neutral partial), and one partial per (row, head, tile) is formed by
     // combining the waves in order w = 0, 1, ...
     static_assert(!kCross, "copied-operand tiles hold whole heads");
+    static_assert(HPW == HG, "a wave covers the workgroup's heads");
     float* comb = (float*)comb_lds;   // [NWV][HPW][DH + 2]
 #pragma unroll
     for (int g = 0; g < HPW; ++g) {
@@ -1025,52 +1070,86 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) vo
         L = fmaf(c[1], e, L);
         O = fmaf(c[2 + dim], e, O);
       }
-      float* dst = part_of(hg * (BF / (2 * DH)) + g, ptile);
-      if (a.tilecnt) {
-        // device-coherent stores: the merging workgroup may sit on another XCD
-        if (dim == 0) {
-          __hip_atomic_store(dst, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(dst + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __hip_atomic_store(dst + 2 + dim, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        if (dim == 0) { dst[0] = M; dst[1] = L; }
-        dst[2 + dim] = O;
-      }
+      store_partial(g, dim, M, L, O);
     }
     if (a.tilecnt) {
-      // The workgroup that completes a (row, head group) merges the row's
-      // tiles for those heads, exactly as the split merge would. The partials
-      // go out with device-coherent stores, which have completed (vmcnt 0)
-      // before the workgroup counts itself; the last one reads them with
-      // device-coherent loads. No cache is written back or invalidated, so
-      // the W rows and h codes other workgroups share in L2 stay there. It
-      // also zeroes the count for the next launch.
-      __shared__ int last_tile;
-      const int n_t = (Tn + BJ - 1) / BJ;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) {
-        int* cnt = a.tilecnt + r * a.n_hg + hg;
-        const int done = atomicAdd(cnt, 1) + 1;
-        last_tile = done == n_t;
-        if (done == n_t) atomicExch(cnt, 0);
-      }
-      __syncthreads();
-      if (!last_tile) return;
       static_assert(NWV * HPW_T * (DH + 2) >= NT + NT / DH + NT / 64, "merge scratch within comb_lds");
+      count_and_merge(comb);
+    }
+  } else if (a.tilecnt) {
+    // LDS-staged h with the tile merge in the launch: the position waves'
+    // partials of each head go to LDS (the staging buffers are free once the
+    // last stage has been multiplied), are combined in position order into
+    // one partial per (row, head, tile), and the last tile of a (row, head
+    // group) merges the row's tiles.
+    float* ex = (float*)smem;                          // [WJN][WJ] p, then [WJN][2] (m, l)
+    float* comb = ex + WJN * WJ + 2 * WJN;             // [HG][WJN][DH + 2]
+    float* scratch = comb + HG * WJN * (DH + 2);       // merge scratch
+    static_assert((WJN * WJ + 2 * WJN + HG * WJN * (DH + 2) + NT + NT / DH + NT / 64) * 4 <= 2 * TILE_BYTES,
+                  "combine and merge scratch within the staging buffers");
+    __syncthreads();
+    if constexpr (!kCross) {
 #pragma unroll
       for (int g = 0; g < HPW; ++g) {
-        const int head = hg * (BF / (2 * DH)) + g;
-        merge_splits<half_t, DH, true, NT>(part_of(head, 0), n_t, (half_t*)a.o + (size_t)r * D + head * DH,
-                                           comb, comb + NT, comb + NT + NT / DH);
+        float* dst = comb + ((wf * HPW + g) * WJN + wj) * (DH + 2);
+        if (wave_live) {
+          const int head = hg * HG + wf * HPW + g;
+          float s[CB], m, lsum;
+          scores(g * 2 * KB, a.q + (size_t)r * D + head * DH, s);
+          softmax(s, m, lsum);
+          values(g * 2 * KB + KB, dst, s, m, lsum);
+        } else {
+          for (int e = l; e < DH + 2; e += 64) dst[e] = e == 0 ? -__builtin_inff() : 0.f;
+        }
+      }
+    } else {
+      // K rows live in wave wf = 0, V rows in wf = 1 (same positions): the
+      // weights p pass through LDS
+      if (wf == 0 && wave_live) {
+        float s[CB], m, lsum;
+        scores(0, a.q + (size_t)r * D + hg * DH, s);
+        softmax(s, m, lsum);
+        if (l < 32)
+#pragma unroll
+          for (int j = 0; j < CB; ++j) ex[wj * WJ + j * 32 + l] = s[j];
+        if (l == 0) { ex[WJN * WJ + 2 * wj] = m; ex[WJN * WJ + 2 * wj + 1] = lsum; }
+      }
+      __syncthreads();
+      if (wf == 1) {
+        float* dst = comb + wj * (DH + 2);
+        if (wave_live) {
+          float p[CB];
+#pragma unroll
+          for (int j = 0; j < CB; ++j) p[j] = ex[wj * WJ + j * 32 + (l & 31)];
+          values(0, dst, p, ex[WJN * WJ + 2 * wj], ex[WJN * WJ + 2 * wj + 1]);
+        } else {
+          for (int e = l; e < DH + 2; e += 64) dst[e] = e == 0 ? -__builtin_inff() : 0.f;
+        }
       }
     }
+    __syncthreads();
+    if (tid < HG * DH) {
+      const int g = tid / DH, dim = tid % DH;
+      const float* cg = comb + g * WJN * (DH + 2);
+      float M = cg[0];
+#pragma unroll
+      for (int w = 1; w < WJN; ++w) M = fmaxf(M, cg[w * (DH + 2)]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < WJN; ++w) {
+        const float* c = cg + w * (DH + 2);
+        const float e = c[0] == -__builtin_inff() ? 0.f : exp2f((c[0] - M) * kLog2e);
+        L = fmaf(c[1], e, L);
+        O = fmaf(c[2 + dim], e, O);
+      }
+      store_partial(g, dim, M, L, O);
+    }
+    count_and_merge(scratch);
   } else if constexpr (!kCross) {
     if (!wave_live) return;
 #pragma unroll
     for (int g = 0; g < HPW; ++g) {
-      const int head = hg * (BF / (2 * DH)) + wf * HPW + g;
+      const int head = hg * HG + wf * HPW + g;
       float s[CB], m, lsum;
       scores(g * 2 * KB, a.q + (size_t)r * D + head * DH, s);
       softmax(s, m, lsum);
@@ -1133,7 +1212,8 @@ hipError_t dispatch(const ModelView& m, const KArgs& k, int grid, hipStream_t s,
 }  // namespace
 
 bool combined_splits(const ModelView& m, int mode) {
-  return m.dtype == TL_DTYPE_F16 && (mode == TL_CACHE_H_INT4 || mode == TL_CACHE_H_INT8);
+  return m.dtype == TL_DTYPE_F16 &&
+         (mode == TL_CACHE_H_INT4 || mode == TL_CACHE_H_INT8 || mode == TL_CACHE_H_F16);
 }
 
 

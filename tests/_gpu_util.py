@@ -87,6 +87,11 @@ def decode(tlc, lanes, loops, tokens, threshold=math.inf, want_logits=True):
 # ---------------------------------------------------------------------------
 # INT / delta codes decided differently by FP32 (GPU) and FP64 (oracle) h
 # ---------------------------------------------------------------------------
+# cache modes whose rows are codes decided by rounding (the synced helpers'
+# adoption applies to them only)
+CODED_MODES = ("int4", "int8", "delta8")
+
+
 def _codec(mode, shape):
     """(group, qmax, qmin) of the mode's codec."""
     if mode == "int4":
@@ -178,6 +183,10 @@ def decode_synced(c, orc, lanes, loops, toks, threshold=math.inf):
     hold the same entries; the oracle's final result is returned with the
     GPU's (tokens, logits, status) and the number of rows adopted."""
     mode, sh = orc.mode, orc.shape
+    if mode not in CODED_MODES:
+        # fp16 / fp32 h and stored K/V: nothing is decided discretely
+        t, lg, st = decode(c, lanes, loops, toks, threshold)
+        return t, lg, st, orc.decode_step(lanes, loops, toks, threshold), 0
     group, qmax, qmin = _codec(mode, sh)
     t, lg, st = decode(c, lanes, loops, toks, threshold)
     pos = {k: orc.length[k] for k in lanes}
@@ -241,10 +250,12 @@ def prefill_synced(c, orc, lane, tokens, loops):
     both caches agree. Returns the GPU's next token and last logits, the
     oracle's result and the number of rows adopted."""
     mode, sh = orc.mode, orc.shape
-    group, qmax, qmin = _codec(mode, sh)
-    n = len(tokens)
     nxt, lg = c.prefill(lane, tokens, loops)
     g_next, g_last = int(nxt.cpu().numpy()[0]), lg.cpu().numpy()
+    if mode not in CODED_MODES:
+        return g_next, g_last, orc.prefill(lane, tokens, loops), 0
+    group, qmax, qmin = _codec(mode, sh)
+    n = len(tokens)
     pos0 = orc.length[lane]
     nl = sh.n_pre + loops
     gpu = {(layer, p): _gpu_row(c, mode, lane, layer, pos0 + p, sh) for layer in range(nl) for p in range(n)}

@@ -1,7 +1,7 @@
-"""The INT4 / INT8 decode attention merges its own 256-position tiles: the
-last workgroup of each (row, head group) to finish combines the row's tile
-partials, counted by a per-(row, head group) tile counter that it zeroes again
-for the next launch. These cases change what a counter slot stands for from
+"""The fp16 models' decode attention (INT4, INT8 and fp16 h) merges its own
+256-position tiles: the last workgroup of each (row, head group) to finish
+combines the row's tile partials, counted by a per-(row, head group) tile
+counter that it zeroes again for the next launch. These cases change what a counter slot stands for from
 one launch to the next and check every step against the oracle:
 
 * rows that move to other lanes, with 1, 2 and 3 tiles in one launch and a
@@ -34,7 +34,7 @@ def _both(gm, w, mode, prompts, loops, max_seq, l_max):
     return orc, c, toks
 
 
-@pytest.mark.parametrize("mode", ["int4", "int8"])
+@pytest.mark.parametrize("mode", ["int4", "int8", "f16"])
 def test_rows_change_lanes_and_tile_counts(mode):
     w, gm = gpu_model(S407)
     # 1, 2 and 3 position tiles; at a context of a few dozen positions a code
@@ -59,7 +59,8 @@ def test_rows_change_lanes_and_tile_counts(mode):
             toks[k] = int(t[i])
 
 
-def test_abort_mid_step_leaves_counters_clean():
+@pytest.mark.parametrize("mode", ["int4", "f16"])
+def test_abort_mid_step_leaves_counters_clean(mode):
     w, gm = gpu_model(S407)
     L = 4
     # prompts whose lanes' largest residual norms of the first decode step are
@@ -67,7 +68,7 @@ def test_abort_mid_step_leaves_counters_clean():
     # aborts one lane and not the other
     for seed in range(30, 40):
         prompts = [synth.make_prompts(S407.vocab, 1, n, seed + 100 * i)[0] for i, n in enumerate([300, 520])]
-        probe = gm.cache("int4", 2, 540, L)
+        probe = gm.cache(mode, 2, 540, L)
         toks = [int(probe.prefill(lane, pr, L)[0].cpu().numpy()[0]) for lane, pr in enumerate(prompts)]
         decode(probe, [0, 1], [L, L], toks)
         n0, n1 = probe.tl_residual_norms(0)[:L], probe.tl_residual_norms(1)[:L]
@@ -81,7 +82,7 @@ def test_abort_mid_step_leaves_counters_clean():
     # the lane with the larger norm aborts at the first iteration above thr
     thr = float(np.float32(0.5 * (nl.max() + nh.max())))
     assert not np.any(nl > thr)
-    orc, c, toks = _both(gm, w, "int4", prompts, [L, L], 540, L)
+    orc, c, toks = _both(gm, w, mode, prompts, [L, L], 540, L)
     r = orc.decode_step([0, 1], [L, L], toks, thr)
     t, lg, st = decode(c, [0, 1], [L, L], toks, thr)
     assert st[hi] == oracle.LANE_ABORTED == r["status"][hi] and t[hi] == -1
@@ -94,7 +95,7 @@ def test_abort_mid_step_leaves_counters_clean():
         t, lg, st = decode(c, [0, 1], [L, L], [tok, tok])
         assert st[hi] == oracle.LANE_ABORTED and t[hi] == -1
         e = rel_err(lg[lo], r["logits"][lo])
-        record("fused_merge_abort", step=step, rel=e)
+        record("fused_merge_abort", mode=mode, step=step, rel=e)
         assert st[lo] == 0 and e <= REL_TOL, (step, e)
         assert token_ok(int(t[lo]), r["logits"][lo])
         tok = int(t[lo])
