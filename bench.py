@@ -554,6 +554,22 @@ def calib_copy(torch):
     log("calibration copy: 3 x 64 MiB")
 
 
+def measure_hbm_read(mib=(10, 64, 256, 1024)):
+    """The streaming-read reference (kv_compression_amd/probe/hbm_read, built
+    with the library): how fast a kernel that only reads cold data moves the
+    given sizes on this GPU. A child process: it allocates its own 4 GiB pool."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kv_compression_amd", "probe", "hbm_read")
+    if not os.path.exists(exe):
+        raise RuntimeError("%s is missing: build the package first" % exe)
+    r = subprocess.run([exe, *[str(m) for m in mib]], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        raise RuntimeError("hbm_read failed: " + r.stderr[-2000:])
+    res = [json.loads(line) for line in r.stdout.splitlines() if line.startswith("{")]
+    log("stream read: " + ", ".join("%d MiB %.1f us" % (x["bytes"] >> 20, x["us_back_to_back"]) for x in res))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -567,7 +583,7 @@ def main():
     ap.add_argument("--no-profile-pass", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="measure only --mode (skip the workload's other cache modes)")
-    ap.add_argument("--leg", choices=["laware_2b", "long_context_2b", "tiny_f32", "f16h_ctx1024"],
+    ap.add_argument("--leg", choices=["laware_2b", "long_context_2b", "tiny_f32", "f16h_ctx1024", "hbm_read"],
                     help="run only this 2B measurement and print its JSON object (for profiling it)")
     ap.add_argument("--leg-orders", default="both", choices=["both", "explicit"],
                     help="attention orders a 2B leg decodes in (explicit: the reconstruction kernel alone)")
@@ -589,8 +605,10 @@ def main():
     tl.load()
     if args.leg:
         fn = {"laware_2b": measure_laware, "long_context_2b": measure_long, "tiny_f32": measure_tiny,
-              "f16h_ctx1024": measure_f16h_ctx1024}[args.leg]
-        if args.leg in ("laware_2b", "long_context_2b") and args.leg_orders == "explicit":
+              "f16h_ctx1024": measure_f16h_ctx1024}.get(args.leg)
+        if args.leg == "hbm_read":
+            res = measure_hbm_read((8, 10, 16, 32, 64, 128, 256, 512, 1024))
+        elif args.leg in ("laware_2b", "long_context_2b") and args.leg_orders == "explicit":
             res = fn(torch, tl, orders=("explicit",))
         else:
             res = fn(torch, tl)
@@ -672,6 +690,16 @@ def main():
                          "attention_kernel": x2.get("kernel"), "kernel_avg_us": x2.get("kernel_avg_us"),
                          "roofline": r2, "prefill": x2.get("prefill")}
 
+    # what a kernel that only streams cold data reaches at the HBM-bound
+    # kernels' sizes (the stored-K/V and absorbed attention launches move
+    # about 64 and 10 MiB at this workload)
+    hbm_ref = None
+    if not args.headline_only:
+        hbm_ref = measure_hbm_read()
+        if "kv" in modes and modes["kv"]["roofline"]:
+            ref = min(hbm_ref, key=lambda x: abs(x["bytes"] - 64 * 2 ** 20))
+            modes["kv"]["vs_stream_read"] = round(modes["kv"]["roofline"]["achieved"] / ref["GBs_back_to_back"], 3)
+
     if args.calib_copy:
         calib_copy(torch)
 
@@ -710,6 +738,7 @@ def main():
         "f16h_ctx1024": f16h,
         "warm_start": resume,
         "speculative": spec,
+        "hbm_read_reference": hbm_ref,
     }
     print(json.dumps(out), flush=True)
 
