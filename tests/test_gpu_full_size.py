@@ -268,7 +268,10 @@ def test_2b_ctx32k_b8_sampled_lane_matches_oracle():
     and the decode step's logits within 2e-3, tokens with the near-tie rule,
     and the step's residual norms within 2e-3. At 33281 positions the decode
     attention merges 131 position tiles per row (its merge loads partials in
-    batches of 32 tiles) and the chunk's causal attention splits 33k keys."""
+    batches of 32 tiles) and the chunk's causal attention splits 33k keys. A
+    second step runs in the absorbed order (novel-contributions page, store-h
+    and MLA), whose rows are then long enough for its one-workgroup-per-CU
+    key split, and is checked the same way."""
     torch = torch_gpu()
     wl = synth.workload("2b-int4h-ctx32k-b8")
     sh = wl.shape
@@ -289,6 +292,9 @@ def test_2b_ctx32k_b8_sampled_lane_matches_oracle():
     t, lgd, st = decode(c, lanes, [L] * wl.lanes, toks)
     assert np.all(st == 0)
     norms = c.tl_residual_norms(lane)[:L]
+    c.tl_cache_set_attention("absorbed")
+    t2, lgd2, st2 = decode(c, lanes, [L] * wl.lanes, [int(x) for x in t])
+    assert np.all(st2 == 0)
     del c
     orc = oracle.LoopedOracle(sh, w, "int4", 1, wl.max_seq, L)
     orc.prime_synthetic(0, range(n_layers), wl.context,
@@ -304,3 +310,8 @@ def test_2b_ctx32k_b8_sampled_lane_matches_oracle():
     assert e_dec <= REL_TOL, e_dec
     assert token_ok(int(t[lane]), r["logits"][0])
     assert np.allclose(norms, orc.norms[0][:L], rtol=REL_TOL)
+    r2 = orc.decode_step([0], [L], [int(t[lane])])
+    e_abs = rel_err(lgd2[lane], r2["logits"][0])
+    record("ctx32k_lane_decode_absorbed", lane=lane, rel=e_abs)
+    assert e_abs <= REL_TOL, e_abs
+    assert token_ok(int(t2[lane]), r2["logits"][0])
