@@ -145,7 +145,7 @@ size_t position_bytes(const tl_config* c, int mode, int l_max) {
 }
 
 struct Layout {
-  size_t off[27];
+  size_t off[25];
   size_t total;
   int R, Bmax, S, apair_cap;
 };
@@ -190,7 +190,7 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
   const bool absorbed = c->dtype == TL_DTYPE_F16 && c->n_heads == 16 && mode != TL_CACHE_KV &&
                         ((c->d_model == 1024 && c->d_head == 64) || (c->d_model == 2048 && c->d_head == 128));
   L.apair_cap = absorbed ? std::min(1024, L.Bmax * 64) : 0;
-  const size_t sizes[27] = {
+  const size_t sizes[25] = {
       (size_t)n_lanes * 4,                        // len
       (size_t)n_lanes * 4,                        // status
       (size_t)n_lanes * l_max * 4,                // norms
@@ -213,12 +213,10 @@ Layout workspace_layout(const tl_config* c, int mode, int n_lanes, int max_seq, 
       delta ? (size_t)n_lanes * max_seq * D * 2 : 0,   // hmat
       absorbed ? (size_t)L.Bmax * c->n_heads * D * 4 : 0,                    // qt
       (size_t)L.apair_cap * c->n_heads * (D + 2) * 4,                       // apart
-      (size_t)L.Bmax * kArgChunks * 4,            // amax_v
-      (size_t)L.Bmax * kArgChunks * 4,            // amax_i
       (size_t)L.Bmax * (2 * D / 128) * 4,         // tilecnt
   };
   size_t o = 0;
-  for (int i = 0; i < 27; ++i) {
+  for (int i = 0; i < 25; ++i) {
     L.off[i] = o;
     o = align256(o + sizes[i]);
   }
@@ -354,9 +352,7 @@ tl_status tl_cache_alloc(const tl_model* m, int mode, int n_lanes, int max_seq, 
   s.qt = L.apair_cap ? (float*)(w + L.off[22]) : nullptr;
   s.apart = L.apair_cap ? (float*)(w + L.off[23]) : nullptr;
   s.apair_cap = L.apair_cap;
-  s.amax_v = (float*)(w + L.off[24]);
-  s.amax_i = (int32_t*)(w + L.off[25]);
-  s.tilecnt = (int32_t*)(w + L.off[26]);
+  s.tilecnt = (int32_t*)(w + L.off[24]);
   v.n_pre = cfg->n_pre; v.H = cfg->n_heads; v.dh = cfg->d_head;
   if (mode == TL_CACHE_H_DELTA8) {
     v.scales = (uint16_t*)(v.base + (size_t)n_lanes * max_seq *
@@ -895,22 +891,21 @@ tl_status tl_decode_step_static(tl_cache* c, int n, const int32_t* lanes, const 
     return fail(TL_E_UNSUPPORTED, "the static-scratch step covers the explicit order of the K/V and h modes "
                                   "other than delta-KV");
   // the step scratch of this call: rows, activations, logits, attention
-  // partials (splits of the longest context), argmax partials, tile counters
+  // partials (splits of the longest context), tile counters
   const tl_config& cfg = c->m->cfg;
   const size_t D = cfg.d_model, F = cfg.d_mlp, V = cfg.vocab, es = dtype_size(cfg.dtype);
   const int min_split = c->mode == TL_CACHE_KV ? kKvSplit : 64;
   const int S = (t_ub + min_split - 1) / min_split;
-  const size_t sizes[15] = {
+  const size_t sizes[14] = {
       (size_t)n * 4, (size_t)n * 4, (size_t)n * 4, (size_t)n * 4,   // row_lane, row_slot, row_pos, row_dead
       (size_t)n * D * 4, (size_t)n * D * es, (size_t)n * D * 4,      // x, h, q
       (size_t)n * D * es, (size_t)n * D * es, (size_t)n * F * es,    // o, u, a
       (size_t)n * D * es, (size_t)n * V * 4,                         // z, logits
       (size_t)n * cfg.n_heads * S * (cfg.d_head + 2) * 4,            // part
-      (size_t)n * kArgChunks * 8,                                    // amax_v, amax_i
       (size_t)n * (2 * D / 128) * 4,                                 // tilecnt
   };
-  size_t off[15], total = 0;
-  for (int i = 0; i < 15; ++i) {
+  size_t off[14], total = 0;
+  for (int i = 0; i < 14; ++i) {
     off[i] = total;
     total = align256(total + sizes[i]);
   }
@@ -934,9 +929,7 @@ tl_status tl_decode_step_static(tl_cache* c, int n, const int32_t* lanes, const 
   w.z = base + off[10];
   w.logits = (float*)(base + off[11]);
   w.part = (float*)(base + off[12]);
-  w.amax_v = (float*)(base + off[13]);
-  w.amax_i = (int32_t*)(base + off[13] + (size_t)n * kArgChunks * 4);
-  w.tilecnt = (int32_t*)(base + off[14]);
+  w.tilecnt = (int32_t*)(base + off[13]);
   w.S = S;
   w.R = n;
   w.Bmax = n;

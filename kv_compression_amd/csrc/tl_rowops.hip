@@ -226,44 +226,22 @@ __device__ int block_argmax(const float* lg, int V) {
   return ib == 0x7fffffff ? 0 : ib;
 }
 
-// Argmax of the logits in 32 chunks per row, one workgroup per (row, chunk):
-// the chunk's (value, index) under the lowest-index-on-ties order. The
-// merge of the chunks in finish_kernel gives the same token as one scan.
-__global__ __launch_bounds__(kRowThreads) void argmax_part_kernel(ModelView m, Workspace ws,
-                                                                  const float* logits, int ld,
-                                                                  int by_slot) {
-  __shared__ float sv[kRowThreads / 64];
-  __shared__ int si[kRowThreads / 64];
-  const int r = blockIdx.x / kArgChunks, c = blockIdx.x % kArgChunks;
-  const int slot = ws.row_slot[r];
-  const float* lg = logits + (size_t)(by_slot ? slot : r) * ld;
-  const int ch = (m.V + kArgChunks - 1) / kArgChunks;
-  const int lo = c * ch, hi = min(m.V, lo + ch);
-  float best = -__builtin_inff();
-  int bi = 0x7fffffff;
-  for (int j = lo + threadIdx.x; j < hi; j += blockDim.x) argmax_merge(best, bi, lg[j], j);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(best, o, 64);
-    const int i2 = __shfl_xor(bi, o, 64);
-    argmax_merge(best, bi, v2, i2);
-  }
-  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float b = sv[0];
-    int ib = si[0];
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_merge(b, ib, sv[w], si[w]);
-    ws.amax_v[r * kArgChunks + c] = b;
-    ws.amax_i[r * kArgChunks + c] = ib;
-  }
-}
-
-__global__ __launch_bounds__(kRowThreads) void finish_kernel(ModelView m, Workspace ws,
-                                                             const float* logits, int ld,
-                                                             int by_slot, int32_t* tokens_out,
-                                                             int32_t* lane_status,
-                                                             float* user_logits) {
+// End of a decode step, one workgroup of kFinishThreads per row: the row's
+// token (the argmax of its logits, ties to the lowest index), the residual
+// kept for a later resume, the lane's new length and the step's outputs.
+// Every thread issues its kFinishLoads logit loads of a batch together (one
+// batch covers a 32768-entry vocabulary); each thread, then each wave, then
+// the waves in order merge (value, index) pairs, and since that merge (larger
+// value, then lower index) does not depend on the order, the token is the one
+// a sequential scan finds.
+constexpr int kFinishThreads = 1024, kFinishLoads = 32;
+__global__ __launch_bounds__(kFinishThreads) void finish_kernel(ModelView m, Workspace ws,
+                                                                const float* logits, int ld,
+                                                                int by_slot, int32_t* tokens_out,
+                                                                int32_t* lane_status,
+                                                                float* user_logits) {
+  __shared__ float sv[kFinishThreads / 64];
+  __shared__ int si[kFinishThreads / 64];
   const int r = blockIdx.x;
   const int lane = ws.row_lane[r], slot = ws.row_slot[r];
   const bool started = ws.row_pos[r] >= 0;
@@ -277,16 +255,37 @@ __global__ __launch_bounds__(kRowThreads) void finish_kernel(ModelView m, Worksp
         ws.xres[(size_t)lane * m.D + i] = ws.x[(size_t)r * m.D + i];
     return;
   }
-  // the chunks' (value, index) pairs, merged in chunk order
-  float b = ws.amax_v[r * kArgChunks];
-  int ib = ws.amax_i[r * kArgChunks];
-  for (int c = 1; c < kArgChunks; ++c) argmax_merge(b, ib, ws.amax_v[r * kArgChunks + c], ws.amax_i[r * kArgChunks + c]);
-  const int tok = ib == 0x7fffffff ? 0 : ib;
-  (void)logits; (void)ld; (void)by_slot;
+  const float* lg = logits + (size_t)(by_slot ? slot : r) * ld;
+  float best = -__builtin_inff();
+  int bi = 0x7fffffff;
+  for (int base = 0; base < m.V; base += kFinishThreads * kFinishLoads) {
+    float v[kFinishLoads];
+#pragma unroll
+    for (int u = 0; u < kFinishLoads; ++u) {
+      const int j = base + u * kFinishThreads + (int)threadIdx.x;
+      v[u] = j < m.V ? lg[j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kFinishLoads; ++u) {
+      const int j = base + u * kFinishThreads + (int)threadIdx.x;
+      if (j < m.V) argmax_merge(best, bi, v[u], j);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(best, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    argmax_merge(best, bi, v2, i2);
+  }
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
   for (int i = threadIdx.x; i < m.D; i += blockDim.x)
     ws.xres[(size_t)lane * m.D + i] = ws.x[(size_t)r * m.D + i];
+  __syncthreads();
   if (threadIdx.x == 0) {
-    tokens_out[slot] = tok;
+    float b = sv[0];
+    int ib = si[0];
+    for (int w = 1; w < kFinishThreads / 64; ++w) argmax_merge(b, ib, sv[w], si[w]);
+    tokens_out[slot] = ib == 0x7fffffff ? 0 : ib;
     lane_status[slot] = TL_LANE_OK;
     ws.len[lane] = ws.row_pos[r] + 1;
   }
@@ -464,11 +463,8 @@ hipError_t launch_rmsnorm(const ModelView& m, int n, const float* x, const void*
 hipError_t launch_finish(const ModelView& m, const Workspace& ws, int n, const float* logits,
                          int ld_logits, int logits_by_slot, int32_t* tokens_out,
                          int32_t* lane_status, float* user_logits, hipStream_t s) {
-  argmax_part_kernel<<<n * kArgChunks, kRowThreads, 0, s>>>(m, ws, logits, ld_logits, logits_by_slot);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  finish_kernel<<<n, kRowThreads, 0, s>>>(m, ws, logits, ld_logits, logits_by_slot, tokens_out,
-                                          lane_status, user_logits);
+  finish_kernel<<<n, kFinishThreads, 0, s>>>(m, ws, logits, ld_logits, logits_by_slot, tokens_out,
+                                             lane_status, user_logits);
   return hipGetLastError();
 }
 
