@@ -277,11 +277,14 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
     // the rows' sums of squares, inverse RMS and dead flags; a row is dead
     // when its lane stopped before the step (negative position) or fails this
     // layer's safety check (a lane that stopped at an earlier layer of the
-    // step kept its residual, so it fails again)
+    // step kept its residual, so it fails again); products without row work
+    // also skip the rows the step's checks have stopped so far (row_dead,
+    // written by the attention input's row work, an earlier launch)
     auto finish_row = [&](int rr, float ss, int rpos) {
       rss[rr] = ss;
       rinv[rr] = __fdiv_rn(1.f, __fsqrt_rn(__fdiv_rn(ss, (float)g.K) + m.eps));
-      rdead[rr] = rpos < 0 || (g.row_tasks && g.check_iter >= 0 && g.check && !(__fsqrt_rn(ss) <= g.thr));
+      rdead[rr] = rpos < 0 || (!g.row_tasks && g.row_dead && g.row_dead[m0 + rr]) ||
+                  (g.row_tasks && g.check_iter >= 0 && g.check && !(__fsqrt_rn(ss) <= g.thr));
     };
     if (ng == 1) {
       // from the operand loads: lane l holds 8 elements of row l % 16 per step
@@ -524,6 +527,7 @@ hipError_t launch_norm(const ModelView& m, const GemmArgs& g, dim3 grid, hipStre
     case EPI_GELU_T: gemm_kernel<T, EPI_GELU_T, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     case EPI_STORE_F32: gemm_kernel<T, EPI_STORE_F32, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     case EPI_QKV: gemm_kernel<T, EPI_QKV, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
+    case EPI_LOGITS: gemm_kernel<T, EPI_LOGITS, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

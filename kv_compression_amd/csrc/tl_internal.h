@@ -300,12 +300,15 @@ hipError_t launch_prefill_attn(const ModelView& m, int n, int pos0, const float*
                                const int32_t* status, float* part, int part_floats,
                                const int32_t* row_lane, const int32_t* row_pos, hipStream_t s);
 
-// Per decode row: argmax of logits (lowest index on ties; chunk partials,
-// then their merge) -> tokens_out[slot],
-// lane_status[slot]; len[lane] += 1 unless aborted; xres[lane] = x[row].
+// Per decode row: the safety check of the row's last loop iteration (norm of
+// the final residual x[row] -> chk.norms; a failure stops the lane), then the
+// argmax of logits (lowest index on ties) -> tokens_out[slot],
+// lane_status[slot]; len[lane] += 1 unless stopped (stopped rows: token -1,
+// user_logits NaN); xres[lane] = x[row].
 hipError_t launch_finish(const ModelView& m, const Workspace& ws, int n, const float* logits,
                          int ld_logits, int logits_by_slot, int32_t* tokens_out,
-                         int32_t* lane_status, float* user_logits, hipStream_t s);
+                         int32_t* lane_status, float* user_logits, const NormCheck& chk,
+                         hipStream_t s);
 // Prefill: argmax of the last row's logits -> next_token; len[lane] = new_len.
 hipError_t launch_prefill_finish(const ModelView& m, const Workspace& ws, int lane, int new_len,
                                  const float* logits, int32_t* next_token, hipStream_t s);

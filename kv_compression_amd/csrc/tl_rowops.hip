@@ -226,9 +226,12 @@ __device__ int block_argmax(const float* lg, int V) {
   return ib == 0x7fffffff ? 0 : ib;
 }
 
-// End of a decode step, one workgroup of kFinishThreads per row: the row's
-// token (the argmax of its logits, ties to the lowest index), the residual
-// kept for a later resume, the lane's new length and the step's outputs.
+// End of a decode step, one workgroup of kFinishThreads per row: the safety
+// check of the row's last loop iteration on its final residual (the norm is
+// recorded; a failure, NaN included, stops the lane, whose logits from the LM
+// head are then replaced by NaN), the row's token (the argmax of its logits,
+// ties to the lowest index), the residual kept for a later resume, the lane's
+// new length and the step's outputs.
 // Every thread issues its kFinishLoads logit loads of a batch together (one
 // batch covers a 32768-entry vocabulary); each thread, then each wave, then
 // the waves in order merge (value, index) pairs, and since that merge (larger
@@ -239,13 +242,29 @@ __global__ __launch_bounds__(kFinishThreads) void finish_kernel(ModelView m, Wor
                                                                 const float* logits, int ld,
                                                                 int by_slot, int32_t* tokens_out,
                                                                 int32_t* lane_status,
-                                                                float* user_logits) {
+                                                                float* user_logits, NormCheck chk) {
   __shared__ float sv[kFinishThreads / 64];
   __shared__ int si[kFinishThreads / 64];
   const int r = blockIdx.x;
   const int lane = ws.row_lane[r], slot = ws.row_slot[r];
   const bool started = ws.row_pos[r] >= 0;
-  if (ws.status[lane] == TL_LANE_ABORTED) {
+  bool stopped = ws.status[lane] == TL_LANE_ABORTED;
+  if (!stopped) {
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < m.D; i += blockDim.x) {
+      const float v = ws.x[(size_t)r * m.D + i];
+      ss += v * v;
+    }
+    ss = block_sum(ss, sv);
+    const float nrm = __fsqrt_rn(ss);
+    if (threadIdx.x == 0) chk.norms[(size_t)lane * chk.l_max + chk.iter[r]] = nrm;
+    if (chk.check && !(nrm <= chk.thr)) {
+      stopped = true;
+      if (threadIdx.x == 0) ws.status[lane] = TL_LANE_ABORTED;
+    }
+    __syncthreads();   // sv is reused below
+  }
+  if (stopped) {
     if (threadIdx.x == 0) { tokens_out[slot] = -1; lane_status[slot] = TL_LANE_ABORTED; }
     if (user_logits)
       for (int j = threadIdx.x; j < m.V; j += blockDim.x)
@@ -462,9 +481,10 @@ hipError_t launch_rmsnorm(const ModelView& m, int n, const float* x, const void*
 
 hipError_t launch_finish(const ModelView& m, const Workspace& ws, int n, const float* logits,
                          int ld_logits, int logits_by_slot, int32_t* tokens_out,
-                         int32_t* lane_status, float* user_logits, hipStream_t s) {
+                         int32_t* lane_status, float* user_logits, const NormCheck& chk,
+                         hipStream_t s) {
   finish_kernel<<<n, kFinishThreads, 0, s>>>(m, ws, logits, ld_logits, logits_by_slot, tokens_out,
-                                             lane_status, user_logits);
+                                             lane_status, user_logits, chk);
   return hipGetLastError();
 }
 
