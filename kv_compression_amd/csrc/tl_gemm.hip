@@ -24,7 +24,9 @@
 // attention input the same kernel does the row work that precedes the
 // projection: the safety check of the previous loop iteration on the entering
 // residual (every workgroup evaluates it from its own sums, so all agree on
-// which rows stop) and the append of h to the cache, one row per workgroup.
+// which rows stop) and the append of h to the cache, one row per workgroup,
+// done once the row norms are known and while the weight loads, issued after
+// the operand rows', are still in flight.
 #include "tl_device.h"
 
 namespace tl {
@@ -234,13 +236,14 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
 #pragma unroll
       for (int u = 0; u < U; ++u) xb[u] = F::load((const T*)X[0] + 32 * u);   // rows past M read row 0
     } else if constexpr (XS == XS_NORM) {
-      // kq == 32 * U: the whole range in one batch, no guards
-#pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = wrow ? F::load(W + 32 * u) : F::zero();
+      // kq == 32 * U: the whole range in one batch, no guards; the operand
+      // rows first, so the norms (and the row work) need not wait for W
       if (ng == 1) {
 #pragma unroll
         for (int u = 0; u < U; ++u) xr[u] = xraw(0, 32 * u);   // rows past M read row 0
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u) a[u] = wrow ? F::load(W + 32 * u) : F::zero();
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) a[u] = (wrow && k + 32 * u < kq) ? F::load(W + k + 32 * u) : F::zero();
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   int task_lane = 0, rpos_l = 0;
   if constexpr (XS == XS_NORM) {
     // position of row l % 16 of the first row group (negative: stopped), and
-    // the row-work inputs, which are only used after the products
+    // the row-work inputs, which are used once the row norms are known
     rpos_l = g.row_pos[m0 + min(l & 15, nrows - 1)];
     if (task) {
       task_lane = g.row_lane[m0 + blockIdx.x];
@@ -333,6 +336,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
     }
     __syncthreads();
     if (task) pre.status = g.status[task_lane];
+    // the row work now, under the weight loads already in flight
+    if (g.row_tasks) row_tasks_ept<T, 2>(m, g, m0, nrows, rss, rinv, rdead, rmax, pre);
   }
   if constexpr (XS == XS_ONE) {
     // one batch, loaded above (kq == 32 * U)
@@ -380,9 +385,6 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
       }
     }
   }
-  }
-  if constexpr (XS == XS_NORM) {
-    if (g.row_tasks) row_tasks_ept<T, 2>(m, g, m0, nrows, rss, rinv, rdead, rmax, pre);
   }
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) red[wave][gi][l] = acc[gi];
