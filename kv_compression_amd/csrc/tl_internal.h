@@ -183,9 +183,10 @@ struct AppendArgs {
 hipError_t launch_norm_append(const ModelView& m, const CacheView& c, const AppendArgs& a,
                               hipStream_t s);
 
-// Safety check folded into a row norm: row r holds the residual after loop
-// iteration iter[r]; its FP32 norm goes to norms[lane, iter[r]] and, if check
-// and !(norm <= thr), the lane aborts.
+// The safety check of each decode row's last loop iteration (done by the
+// step's end kernel): row r holds the residual after loop iteration iter[r];
+// its FP32 norm goes to norms[lane, iter[r]] and, if check and
+// !(norm <= thr), the lane aborts.
 struct NormCheck {
   float* norms;
   int32_t* status;
@@ -194,11 +195,9 @@ struct NormCheck {
   int32_t iter[kMaxBatch];
 };
 
-// out[row] = dtype(RMSNorm(x[row]) * g) for rows 0..n-1 (skips aborted rows);
-// with chk, also the safety check of each row (a row that aborts is skipped).
+// out[row] = dtype(RMSNorm(x[row]) * g) for rows 0..n-1 (skips aborted rows).
 hipError_t launch_rmsnorm(const ModelView& m, int n, const float* x, const void* gain, void* out,
-                          const int32_t* row_lane, const int32_t* status, hipStream_t s,
-                          const NormCheck* chk = nullptr);
+                          const int32_t* row_lane, const int32_t* status, hipStream_t s);
 
 
 

@@ -150,11 +150,11 @@ __global__ __launch_bounds__(256) void delta_rec_kernel(CacheView c, int layer, 
   for (int k = 0; k < EPT; ++k) rec[(size_t)i * c.D + e0 + k] = acc[k];
 }
 
-template <typename T, int EPT, bool CHECK>
+template <typename T, int EPT>
 __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(ModelView m, const float* x,
                                                               const void* gain, void* out,
                                                               const int32_t* row_lane,
-                                                              const int32_t* status, NormCheck chk) {
+                                                              const int32_t* status) {
   __shared__ float red[kRowThreads / 64];
   const int r = blockIdx.x;
   if (status && status[row_lane[r]] == TL_LANE_ABORTED) return;
@@ -166,15 +166,6 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(ModelView m, const
     ss += xv[i] * xv[i];
   }
   ss = block_sum(ss, red);
-  if constexpr (CHECK) {
-    const int lane = row_lane[r];
-    const float nrm = __fsqrt_rn(ss);
-    if (threadIdx.x == 0) chk.norms[(size_t)lane * chk.l_max + chk.iter[r]] = nrm;
-    if (chk.check && !(nrm <= chk.thr)) {
-      if (threadIdx.x == 0) chk.status[lane] = TL_LANE_ABORTED;
-      return;
-    }
-  }
   const float inv = __fdiv_rn(1.f, __fsqrt_rn(__fdiv_rn(ss, (float)D) + m.eps));
   const T* g = (const T*)gain;
   T* o = (T*)out + (size_t)r * D;
@@ -459,17 +450,10 @@ hipError_t launch_norm_append(const ModelView& m, const CacheView& c, const Appe
 }
 
 hipError_t launch_rmsnorm(const ModelView& m, int n, const float* x, const void* gain, void* out,
-                          const int32_t* row_lane, const int32_t* status, hipStream_t s,
-                          const NormCheck* chk) {
+                          const int32_t* row_lane, const int32_t* status, hipStream_t s) {
   const int nt = row_threads(m.D);
   const int ept = m.D / nt;
-  NormCheck c{};
-  if (chk) c = *chk;
-#define TL_RN(T_, E_)                                                                        \
-  do {                                                                                       \
-    if (chk) rmsnorm_kernel<T_, E_, true><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status, c); \
-    else rmsnorm_kernel<T_, E_, false><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status, c);   \
-  } while (0)
+#define TL_RN(T_, E_) rmsnorm_kernel<T_, E_><<<n, nt, 0, s>>>(m, x, gain, out, row_lane, status)
   if (m.dtype == TL_DTYPE_F32 && ept == 1) TL_RN(float, 1);
   else if (m.dtype == TL_DTYPE_F16 && ept == 1) TL_RN(half_t, 1);
   else if (m.dtype == TL_DTYPE_F16 && ept == 4) TL_RN(half_t, 4);
