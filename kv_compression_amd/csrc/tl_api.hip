@@ -816,18 +816,20 @@ tl_status decode_enqueue(tl_cache* c, const Workspace& ws, int n, const int32_t*
     gd.row_lane = ws.row_lane; gd.status = ws.status; gd.row_dead = ws.row_dead;
     TL_HIP(launch_gemm(mv, gd, s));
   }
-  // the LM head forms the final RMSNorm of the residual rows itself; every
-  // row's last loop iteration is checked on the final residual at the step's
-  // end (the earlier ones were checked on entry to the next layer), and a row
-  // stopped there has its logits replaced
+  // the final RMSNorm, the LM head, then the step's end: every row's last
+  // loop iteration is checked there on the final residual (the earlier ones
+  // were checked on entry to the next layer), and a row stopped there has its
+  // logits replaced. (The LM head forming the norm itself, as the Q and MLP-up
+  // products do, was slower: its 2000 workgroups each repeat the norm.)
   NormCheck fc{};
   fc.norms = ws.norms; fc.status = ws.status; fc.l_max = c->l_max;
   fc.check = check ? 1 : 0; fc.thr = safety_threshold;
   for (int r = 0; r < n; ++r) fc.iter[r] = loops[order[r]] - 1;
   float* lg = d_logits ? d_logits : ws.logits;
-  GemmArgs gh = gemm_args(mv.lm_head, D, ws.x, D, n, mv.V, D, EPI_LOGITS, lg, mv.V);
-  gh.row_lane = ws.row_lane; gh.status = ws.status; gh.row_dead = ws.row_dead; gh.row_pos = ws.row_pos;
-  gh.row_slot = d_logits ? ws.row_slot : nullptr; gh.norm_gain = mv.final_norm;
+  TL_HIP(launch_rmsnorm(mv, n, ws.x, mv.final_norm, ws.z, ws.row_lane, ws.status, s));
+  GemmArgs gh = gemm_args(mv.lm_head, D, ws.z, D, n, mv.V, D, EPI_LOGITS, lg, mv.V);
+  gh.row_lane = ws.row_lane; gh.status = ws.status; gh.row_dead = ws.row_dead;
+  gh.row_slot = d_logits ? ws.row_slot : nullptr;
   TL_HIP(launch_gemm(mv, gh, s));
   TL_HIP(launch_finish(mv, ws, n, lg, mv.V, d_logits ? 1 : 0, d_tokens_out, d_lane_status,
                        d_logits, fc, s));

@@ -24,9 +24,7 @@
 // attention input the same kernel does the row work that precedes the
 // projection: the safety check of the previous loop iteration on the entering
 // residual (every workgroup evaluates it from its own sums, so all agree on
-// which rows stop) and the append of h to the cache, one row per workgroup,
-// done once the row norms are known and while the weight loads, issued after
-// the operand rows', are still in flight.
+// which rows stop) and the append of h to the cache, one row per workgroup.
 #include "tl_device.h"
 
 namespace tl {
@@ -236,14 +234,13 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
 #pragma unroll
       for (int u = 0; u < U; ++u) xb[u] = F::load((const T*)X[0] + 32 * u);   // rows past M read row 0
     } else if constexpr (XS == XS_NORM) {
-      // kq == 32 * U: the whole range in one batch, no guards; the operand
-      // rows first, so the norms (and the row work) need not wait for W
+      // kq == 32 * U: the whole range in one batch, no guards
+#pragma unroll
+      for (int u = 0; u < U; ++u) a[u] = wrow ? F::load(W + 32 * u) : F::zero();
       if (ng == 1) {
 #pragma unroll
         for (int u = 0; u < U; ++u) xr[u] = xraw(0, 32 * u);   // rows past M read row 0
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = wrow ? F::load(W + 32 * u) : F::zero();
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) a[u] = (wrow && k + 32 * u < kq) ? F::load(W + k + 32 * u) : F::zero();
@@ -256,7 +253,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
   int task_lane = 0, rpos_l = 0;
   if constexpr (XS == XS_NORM) {
     // position of row l % 16 of the first row group (negative: stopped), and
-    // the row-work inputs, which are used once the row norms are known
+    // the row-work inputs, which are only used after the products
     rpos_l = g.row_pos[m0 + min(l & 15, nrows - 1)];
     if (task) {
       task_lane = g.row_lane[m0 + blockIdx.x];
@@ -336,8 +333,6 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
     }
     __syncthreads();
     if (task) pre.status = g.status[task_lane];
-    // the row work now, under the weight loads already in flight
-    if (g.row_tasks) row_tasks_ept<T, 2>(m, g, m0, nrows, rss, rinv, rdead, rmax, pre);
   }
   if constexpr (XS == XS_ONE) {
     // one batch, loaded above (kq == 32 * U)
@@ -385,6 +380,9 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(ModelView m, GemmArgs g) 
       }
     }
   }
+  }
+  if constexpr (XS == XS_NORM) {
+    if (g.row_tasks) row_tasks_ept<T, 2>(m, g, m0, nrows, rss, rinv, rdead, rmax, pre);
   }
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) red[wave][gi][l] = acc[gi];
@@ -529,7 +527,6 @@ hipError_t launch_norm(const ModelView& m, const GemmArgs& g, dim3 grid, hipStre
     case EPI_GELU_T: gemm_kernel<T, EPI_GELU_T, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     case EPI_STORE_F32: gemm_kernel<T, EPI_STORE_F32, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     case EPI_QKV: gemm_kernel<T, EPI_QKV, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
-    case EPI_LOGITS: gemm_kernel<T, EPI_LOGITS, KS, XS_NORM, NU><<<grid, 64 * KS, 0, s>>>(m, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
