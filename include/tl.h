@@ -206,8 +206,8 @@ tl_status tl_extend_depth(tl_cache* c, int lane, int pos0, int n, int old_loops,
  * (novel-contributions page, "Per-Iteration Safety Check"); +INF turns the
  * check off. An abort is not an error: the lane's remaining iterations and its
  * token are skipped, d_lane_status[k] = TL_LANE_ABORTED, d_tokens_out[k] = -1,
- * its length does not advance, and later calls skip it until
- * tl_cache_reset_lane.
+ * its row of d_logits (if given) is NaN, its length does not advance, and
+ * later calls skip it until tl_cache_reset_lane.
  * d_tokens_out: device int32 [n]. d_logits (nullable): device f32 [n, vocab].
  * d_lane_status: device int32 [n].
  * Errors: TL_E_ARG, TL_E_CAPACITY, TL_E_CACHE_GAP (as for prefill). */
@@ -220,7 +220,7 @@ tl_status tl_decode_step(tl_cache* c, int n, const int32_t* lanes, const int32_t
  * call (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation): tl_decode_step with the same arguments, results and
  * errors, whose step scratch (the rows' activations, logits, attention
- * partials, argmax partials and tile counters) lives in a static array of the
+ * partials and tile counters) lives in a static array of the
  * library, 16 MiB per GPU, held until the process ends; the cache's per-lane
  * state stays in its workspace. It allocates nothing and enqueues the same
  * kernels plus one fill that zeroes the tile counters. The step must fit:

@@ -212,6 +212,44 @@ def test_safety_threshold_bracket_gpu():
     assert st[0] == 0 and t[0] >= 0
 
 
+def test_last_iteration_check_at_step_end():
+    """Each row's last loop iteration is checked at the end of the step, on
+    its final residual, with the row's own iteration index (rows of 1 and 3
+    loops in one step): a threshold just under the 1-loop row's only norm
+    stops that row there (status, token -1, NaN logits, the norm recorded),
+    while its batch mate stops exactly where its own norms first exceed the
+    threshold, or decodes bitwise as without the check."""
+    w, gm = gpu_model(S407)
+    prompts = synth.make_prompts(S407.vocab, 2, 60, 12)
+    loops = [1, 3]
+
+    def fresh():
+        c = gm.cache("int4", 2, 80, 3)
+        toks = [int(c.prefill(k, prompts[k], loops[k])[0].cpu().numpy()[0]) for k in range(2)]
+        return c, toks
+
+    c, toks = fresh()
+    t, lg, st = decode(c, [0, 1], loops, toks, math.inf)
+    assert np.all(st == 0)
+    n0 = c.tl_residual_norms(0)[:1].astype(np.float64)
+    n1 = c.tl_residual_norms(1)[:3].astype(np.float64)
+    assert np.all(np.isfinite(n0)) and np.all(np.isfinite(n1))
+    thr = float(np.float32(n0[0] * (1 - 1e-4)))
+    c, toks2 = fresh()
+    assert toks2 == toks
+    t2, lg2, st2 = decode(c, [0, 1], loops, toks, thr)
+    assert st2[0] == oracle.LANE_ABORTED and t2[0] == -1 and np.all(np.isnan(lg2[0]))
+    assert c.tl_residual_norms(0)[0] == np.float32(n0[0])
+    if np.any(n1 > thr):
+        first = int(np.argmax(n1 > thr))
+        got = c.tl_residual_norms(1)
+        assert st2[1] == oracle.LANE_ABORTED and t2[1] == -1
+        assert np.all(np.isfinite(got[:first + 1])) and np.all(np.isnan(got[first + 1:3]))
+    else:
+        assert st2[1] == 0 and t2[1] == t[1]
+        assert np.array_equal(lg2[1].view(np.uint32), lg[1].view(np.uint32))
+
+
 # ------------------------------------------------------------------ invariants on the GPU
 def test_lane_result_independent_of_batch_mates():
     """A mixed-loops batch gives each lane exactly (bitwise) what it gets alone."""

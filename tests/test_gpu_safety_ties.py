@@ -6,8 +6,9 @@ through the C ABI, against the oracle.
   is not (norm <= threshold)). An infinite embedding element makes the first
   norm's output NaN, so the residual is NaN by loop iteration 0.
 * Argmax ties go to the lowest index: an LM head whose top logits tie exactly
-  (each logit a single exact product), with tied rows inside one of the
-  argmax kernel's chunks and across chunks.
+  (each logit a single exact product), with tied indices close together and
+  far apart in the vocabulary (the same and different threads, waves and
+  load batches of the step's end kernel).
 """
 import numpy as np
 import pytest
