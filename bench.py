@@ -520,6 +520,33 @@ def measure_f16h_ctx1024(torch, tl, steps=128, warmup=2):
                         "traffic": load_traffic(wl.name, "f16", "recon_attn")}}
     log("407M fp16-h context 1024: %.1f tok/s, attention %.2f us, %s" % (steps / wall, kern_ms * 1e3 / launches,
                                                                       out["roofline"]))
+    # the same steps in the absorbed order (one row leaves the explicit
+    # kernel 40 workgroups; the absorbed one splits the keys over ~512)
+    c.tl_cache_set_attention("absorbed")
+    c.tl_cache_set_length(0, ctx, sh.n_pre + L)
+    a.copy_(nxt)
+    for _ in range(warmup):
+        c.tl_decode_step([0], [L], a, wl.threshold, b, None, st)
+        a, b = b, a
+    c.tl_cache_set_length(0, ctx, sh.n_pre + L)
+    a.copy_(nxt)
+    torch.cuda.synchronize()
+    c.tl_profile_start()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        c.tl_decode_step([0], [L], a, wl.threshold, b, None, st)
+        a, b = b, a
+    torch.cuda.synchronize()
+    wall_a = time.perf_counter() - t0
+    kern_a, launches_a = c.tl_profile_stop()
+    assert int(st.cpu()[0]) == 0
+    out["absorbed"] = {"decode_tok_s": round(steps / wall_a, 1), "ms_per_step": round(wall_a * 1e3 / steps, 4),
+                       "attention_kernel": "absorbed_attn",
+                       "attention_kernel_avg_us": round(kern_a * 1e3 / launches_a, 2),
+                       "roofline": dict(absorbed_roofline(sh, [L], [ctx + 1 + s for s in range(steps)], kern_a, eb),
+                                        traffic=None)}
+    log("407M fp16-h context 1024, absorbed order: %.1f tok/s, attention %.2f us"
+        % (steps / wall_a, kern_a * 1e3 / launches_a))
     del c, model
     torch.cuda.synchronize()
     return out
