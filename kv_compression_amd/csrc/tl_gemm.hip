@@ -500,8 +500,6 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(ModelView m, GemmArgs g
     }
 }
 
-constexpr int kCUs = 256;
-
 template <int BM>
 hipError_t launch_tiled_bm(const ModelView& m, const GemmArgs& g, hipStream_t s) {
   const dim3 grid(g.N / 64, (g.M + BM - 1) / BM);

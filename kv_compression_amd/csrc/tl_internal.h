@@ -15,6 +15,7 @@ constexpr int kMaxChunk = 512;        // tokens per prefill call
 constexpr int kKBlock = 64;           // d_model elements per tiled cache block
 constexpr int kInt4Group = 32;        // INT4-h scale group along d_model
 constexpr int kKvSplit = 32;          // positions per split in the stored-K/V attention
+constexpr int kCUs = 256;             // compute units of the GPU (grid sizing heuristics)
 constexpr int kSpecMax = 15;          // drafted tokens per speculative round
 constexpr int kSpecRows = 16;         // verification rows of a round (kSpecMax + 1)
 

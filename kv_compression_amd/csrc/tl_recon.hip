@@ -42,8 +42,21 @@ namespace {
 //   fp32: 4 waves of 64 x 64.
 // OCC: workgroups resident per CU (waves per SIMD), which sets the register
 // budget of a wave (512 / OCC, accumulators included).
-template <typename T, int MODE, int DH> struct Cfg {
+template <typename T, int MODE, int DH, int VAR = 0> struct Cfg {
   static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1;
+  static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+};
+// fp16 h at 64-wide heads when a launch has too few rows and position tiles
+// to give every CU a workgroup of the configuration above (one lane at a
+// context of about a thousand: 40 workgroups): one head (its 64 K and 64 V
+// rows) per workgroup, so twice the workgroups with half the work each.
+template <> struct Cfg<half_t, TL_CACHE_H_F16, 64, 1> {
+  static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1;
+  static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+};
+// ... and with 128-position tiles when even that leaves CUs idle
+template <> struct Cfg<half_t, TL_CACHE_H_F16, 64, 2> {
+  static constexpr int BF = 128, BJ = 128, WF = 128, WJ = 64, BK = 64, OCC = 1;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
 // integer codes: every wave covers all BF features of its positions
@@ -70,6 +83,8 @@ template <int MODE, int DH> struct Cfg<float, MODE, DH> {
 // the fp16 configurations other than INT4 at 64-wide heads share BJ and WJ
 // (split length)
 static_assert(Cfg<half_t, TL_CACHE_H_INT4, 128>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
+              Cfg<half_t, TL_CACHE_H_F16, 64, 1>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
+              Cfg<half_t, TL_CACHE_H_F16, 64, 2>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ &&
               Cfg<half_t, TL_CACHE_H_INT8, 64>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
               Cfg<half_t, TL_CACHE_H_INT4, 64>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ &&
               Cfg<half_t, TL_CACHE_H_INT8, 64>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ, "fp16 tiles");
@@ -116,7 +131,7 @@ struct KArgs {
 
 // chunks of 16 bytes per thread per stage for an LDS-staged h tile
 template <int MODE> struct HLoad { static constexpr int NCH = 1, CPP = 1; };
-template <> struct HLoad<TL_CACHE_H_F16> { static constexpr int NCH = 4, CPP = 8; };   // 512 threads
+template <> struct HLoad<TL_CACHE_H_F16> { static constexpr int NCH = 4, CPP = 8; };   // (NCH of 512 threads)
 template <> struct HLoad<TL_CACHE_H_F32> { static constexpr int NCH = 8, CPP = 16; };  // 256 threads
 
 // Value of lane partner(l) for a data-parallel-primitive pattern within each
@@ -266,9 +281,9 @@ __device__ __forceinline__ void lds_sync() {
 // a 256-byte bank window, and any 8 consecutive rows on 8 distinct slots.
 __device__ __forceinline__ int w_swz(int R) { return ((R >> 1) ^ (R << 2)) & 7; }
 
-template <typename T, int MODE, int DH, int EPI>
-__global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) void recon_kernel(KArgs a) {
-  typedef Cfg<T, MODE, DH> C;
+template <typename T, int MODE, int DH, int EPI, int VAR = 0>
+__global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>::OCC)) void recon_kernel(KArgs a) {
+  typedef Cfg<T, MODE, DH, VAR> C;
   constexpr int BF = C::BF, BJ = C::BJ, WF = C::WF, WJ = C::WJ, BK = C::BK, NT = C::NT;
   constexpr int WJN = BJ / WJ;                // waves along positions
   constexpr int ES = sizeof(T);
@@ -277,7 +292,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) vo
   constexpr int A_CPR = BK * ES / 16;         // 16-byte chunks per W row per stage
   constexpr int A_NCH = BF * A_CPR / NT;      // per thread
   constexpr bool B_REG = MODE == TL_CACHE_H_INT4 || MODE == TL_CACHE_H_INT8;
-  constexpr int B_NCH = HLoad<MODE>::NCH;
+  constexpr int B_NCH = B_REG ? HLoad<MODE>::NCH : BJ * HLoad<MODE>::CPP / NT;   // h chunks per thread
   constexpr int B_CPP = HLoad<MODE>::CPP;     // chunks per position
   static_assert(B_REG || BJ * B_CPP == NT * B_NCH, "h tile chunks");
   static_assert(!B_REG || (std::is_same<T, half_t>::value && BK == kKBlock), "register h path");
@@ -1183,14 +1198,21 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH>::NT), (Cfg<T, MODE, DH>::OCC)) vo
   }
 }
 
-template <typename T, int MODE, int DH>
+template <typename T, int MODE, int DH, int VAR = 0>
 hipError_t launch_mode(const KArgs& k, int grid, hipStream_t s, int epi) {
-  if (epi == EPI_ATTN) recon_kernel<T, MODE, DH, EPI_ATTN><<<grid, Cfg<T, MODE, DH>::NT, 0, s>>>(k);
-  else recon_kernel<T, MODE, DH, EPI_KVSTORE><<<grid, Cfg<T, MODE, DH>::NT, 0, s>>>(k);
+  if (epi == EPI_ATTN) recon_kernel<T, MODE, DH, EPI_ATTN, VAR><<<grid, Cfg<T, MODE, DH, VAR>::NT, 0, s>>>(k);
+  else recon_kernel<T, MODE, DH, EPI_KVSTORE, VAR><<<grid, Cfg<T, MODE, DH, VAR>::NT, 0, s>>>(k);
   return hipGetLastError();
 }
 
-hipError_t dispatch(const ModelView& m, const KArgs& k, int grid, hipStream_t s, int epi) {
+// var 1, 2: the one-head fp16-h configurations (decode attention only)
+hipError_t dispatch(const ModelView& m, const KArgs& k, int grid, hipStream_t s, int epi, int var = 0) {
+  if (var == 1 || var == 2) {
+    if (!(m.dtype == TL_DTYPE_F16 && k.cache.mode == TL_CACHE_H_F16 && m.dh == 64 && epi == EPI_ATTN))
+      return hipErrorInvalidValue;
+    return var == 1 ? launch_mode<half_t, TL_CACHE_H_F16, 64, 1>(k, grid, s, epi)
+                    : launch_mode<half_t, TL_CACHE_H_F16, 64, 2>(k, grid, s, epi);
+  }
   if (m.dtype == TL_DTYPE_F32) {
     if (m.dh == 32 && k.cache.mode == TL_CACHE_H_F32)
       return launch_mode<float, TL_CACHE_H_F32, 32>(k, grid, s, epi);
@@ -1219,7 +1241,9 @@ bool combined_splits(const ModelView& m, int mode) {
 
 // features (K and V rows) per workgroup and positions per tile of the
 // configuration dispatch() picks
-static int recon_bf(const ModelView& m, int mode) {
+static int recon_bf(const ModelView& m, int mode, int var = 0) {
+  if (var == 1) return Cfg<half_t, TL_CACHE_H_F16, 64, 1>::BF;
+  if (var == 2) return Cfg<half_t, TL_CACHE_H_F16, 64, 2>::BF;
   if (m.dtype == TL_DTYPE_F32) return Cfg<float, TL_CACHE_H_F32, 32>::BF;
   if (mode == TL_CACHE_H_INT4 && m.dh == 64) return Cfg<half_t, TL_CACHE_H_INT4, 64>::BF;
   static_assert(Cfg<half_t, TL_CACHE_H_INT4, 128>::BF == 256 && Cfg<half_t, TL_CACHE_H_INT8, 64>::BF == 256 &&
@@ -1228,7 +1252,8 @@ static int recon_bf(const ModelView& m, int mode) {
                 "other fp16 configurations");
   return 256;
 }
-static int recon_bj(const ModelView& m, int mode) {
+static int recon_bj(const ModelView& m, int mode, int var = 0) {
+  if (var == 2) return Cfg<half_t, TL_CACHE_H_F16, 64, 2>::BJ;
   if (m.dtype == TL_DTYPE_F32) return Cfg<float, TL_CACHE_H_F32, 32>::BJ;
   if (mode == TL_CACHE_H_INT4 && m.dh == 64) return Cfg<half_t, TL_CACHE_H_INT4, 64>::BJ;
   return Cfg<half_t, TL_CACHE_H_F16, 64>::BJ;
@@ -1241,8 +1266,19 @@ int recon_split_len(const ModelView& m, int mode) {
 
 hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t s) {
   if (r.tilecnt && (!r.o || !combined_splits(m, r.cache.mode))) return hipErrorInvalidValue;
-  const int BF = recon_bf(m, r.cache.mode);
-  const int BJ = recon_bj(m, r.cache.mode);
+  // fp16 h at 64-wide heads: the one-head configurations when the regular one
+  // would leave CUs without a workgroup (128-position tiles when 256-position
+  // ones still would)
+  int var = 0;
+  if (m.dtype == TL_DTYPE_F16 && r.cache.mode == TL_CACHE_H_F16 && m.dh == 64) {
+    auto wgs = [&](int v) {
+      const int bj = recon_bj(m, r.cache.mode, v);
+      return (long)((r.t_ub + bj - 1) / bj) * r.n_rows * (2 * m.D / recon_bf(m, r.cache.mode, v));
+    };
+    if (wgs(0) < kCUs) var = wgs(1) < kCUs ? 2 : 1;
+  }
+  const int BF = recon_bf(m, r.cache.mode, var);
+  const int BJ = recon_bj(m, r.cache.mode, var);
   KArgs k{};
   k.cache = r.cache;
   k.layer = r.layer;
@@ -1273,7 +1309,7 @@ hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t
   const long n_tiles = (long)k.n_ptiles * r.n_rows;
   const long grid = ((n_tiles + parts - 1) / parts) * parts * k.n_hg;
   if (grid <= 0 || grid > (1L << 30)) return hipErrorInvalidValue;
-  return dispatch(m, k, (int)grid, s, EPI_ATTN);
+  return dispatch(m, k, (int)grid, s, EPI_ATTN, var);
 }
 
 hipError_t launch_recon_store(const ModelView& m, const CacheView& c, int layer, int lane, int T,
