@@ -5,25 +5,24 @@
 // them for the causal prefill attention.
 //
 // One workgroup computes the product tile C[f, j] = sum_k W[f, k] h'[j, k] for
-// BF features (the K and V rows of whole heads) and BJ cached positions of one
-// lane, streaming d_model in BK = 64 deep stages. Four waves, 2 x 2, each own
-// a 128 x 128 tile (fp16: 4 x 4 v_mfma_f32_32x32x16_f16 blocks, 256
-// accumulators per lane); features run down the MFMA rows and positions along
-// its columns, so each lane ends up holding whole positions.
-//   * W rows (fp16, L2-resident: consecutive workgroups take different head
-//     groups, i.e. different XCDs, so each XCD streams one head group's rows)
-//     are loaded one stage ahead into registers and staged through LDS (double
-//     buffered, rows padded to 144 B: the 16-byte fragment reads of 16 lanes
-//     hit disjoint banks).
-//   * INT4 / INT8 h never goes through LDS: each lane loads the codes of its
-//     own positions for the next stages straight from the cache (the block
-//     rows are laid out so that one half-wave's k-run is contiguous) and
-//     dequantises them in registers into MFMA operands, fp16(q * s) exactly.
-//     That halves the LDS traffic per MFMA compared with staging both
-//     operands. fp16 / fp32 h (no dequantisation) is staged through LDS.
+// BF features (the K and V rows of whole heads, interleaved per head at
+// decode) and BJ cached positions of one lane, streaming d_model in BK = 64
+// deep stages on v_mfma_f32_32x32x16_f16 (fp32 accumulators). Features run
+// down the MFMA rows and positions along its columns, so each lane ends up
+// holding whole positions.
+//   * INT4 / INT8 h: the W tile, the h codes and the INT4 scales of a stage
+//     are copied by the memory unit straight into a three-buffer LDS ring
+//     (buffer loads to LDS); each of four waves owns all the tile's features
+//     for 64 positions and dequantises its codes in registers into the B
+//     operand, fp16(q * s) exactly, one k-step ahead of the MFMAs.
+//   * fp16 / fp32 h: both operands go through registers into a two-buffer
+//     LDS tile, one stage ahead; waves are laid out over features and
+//     positions.
 // The decode epilogue reads the scores q . K_j out of the accumulators,
-// applies a wave-level online softmax and reduces p_j V_j across lanes,
-// writing (max, sum, o) per (row, head, 128-position split).
+// applies a wave-level online softmax and reduces p_j V_j across lanes into
+// (max, sum, o) per (row, head, position tile); the last workgroup to finish
+// a (row, head group) merges that row's tiles itself. The prefill epilogue
+// stores the K | V rows for the causal attention kernel.
 #include <type_traits>
 
 #include "tl_device.h"
