@@ -8,8 +8,8 @@ iteration appends h, rebuilds K|V from the INT4 cache on MFMA, attends, runs
 W_o and the MLP, and checks the residual norm after every loop iteration.
 
 Prints one JSON line: decode tokens/s, the roofline of the dominant kernel
-(the reconstruction + attention kernel, timed with HIP events on the stream it
-runs on), and the CPU oracle timed on a bounded sample of the same workload.
+(the reconstruction + attention kernel, timed with HIP events attached to its
+launches on the stream it runs on), and the CPU oracle timed on a bounded sample of the same workload.
 Inputs are synthetic (seeded weights ~ N(0, 0.02), uniform prompt ids).
 """
 from __future__ import annotations
@@ -150,7 +150,8 @@ def cpu_baseline(shape, w, mode, context, loops, budget_s=12.0, max_steps=64):
 def measure_mode(torch, tl, model, wl, shape, mode, prompts, K, W, profile, order="explicit", repeats=1):
     """Prefill the workload's lanes in `mode`, time K decode steps after W
     warm-up steps (inputs resident in HBM), then, if `profile`, time the
-    attention kernel alone over another K steps with HIP events on its stream.
+    attention kernel alone over another K steps with HIP events attached to its
+    launches on its stream.
     `order`: the decode attention's evaluation order ("explicit" rebuilds K/V
     on MFMA; "absorbed" attends over h' with W_k^T q and applies W_v after).
     Returns (tok/s, wall s, roofline, extra, prefill s, cache bytes)."""

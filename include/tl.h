@@ -334,12 +334,15 @@ tl_status tl_cache_read(const tl_cache* c, int lane, int layer, int pos0, int n,
 tl_status tl_cache_reset_lane(tl_cache* c, int lane, void* stream);
 
 /* Kernel timing for measurement: between tl_profile_start and tl_profile_stop
- * every launch of the decode attention kernel (store-h reconstruction +
- * attention, or the stored-K/V streaming attention) made by tl_decode_step,
- * and of the causal attention kernel made by tl_prefill_chunk, is bracketed
- * with HIP events recorded on the call's stream. tl_profile_stop
- * waits for the last event and returns the summed kernel time in milliseconds
- * and the number of launches. Host-side events only; no device memory. */
+ * every launch of the decode attention kernel made by tl_decode_step (store-h
+ * reconstruction + attention, the absorbed-order attention, or the stored-K/V
+ * streaming attention) is timed by a pair of HIP events attached to that
+ * launch, which take its own start and end timestamps (hipExtLaunchKernel);
+ * the causal attention of tl_prefill_chunk (with its split merge, when the
+ * keys are split) is bracketed by events recorded on the call's stream
+ * before and after it. tl_profile_stop waits for the last event and returns
+ * the summed time in milliseconds and the number of timed launches.
+ * Host-side events only; no device memory. */
 tl_status tl_profile_start(tl_cache* c);
 tl_status tl_profile_stop(tl_cache* c, double* total_ms, int* n_launches);
 

@@ -459,7 +459,7 @@ hipError_t launch_absorb_q(const ModelView& m, int n_rows, const float* q, const
 hipError_t launch_absorbed_attn(const ModelView& m, const CacheView& c, int layer, int n_rows,
                                 const int32_t* row_lane, const int32_t* row_pos,
                                 const int32_t* status, const float* qt, float* part, int S,
-                                int split_len, hipStream_t s) {
+                                int split_len, hipStream_t s, const LaunchEvents& ev) {
   if (!absorbed_supported(m, c.mode) || n_rows < 1 || S < 1) return hipErrorInvalidValue;
   AbsArgs a{};
   a.cache = c; a.layer = layer; a.row_lane = row_lane; a.row_pos = row_pos; a.status = status;
@@ -467,14 +467,13 @@ hipError_t launch_absorbed_attn(const ModelView& m, const CacheView& c, int laye
   const int grid = n_rows * S;
 #define TL_ABS(D_)                                                                              \
   do {                                                                                          \
-    if (c.mode == TL_CACHE_H_INT4) absorbed_attn_kernel<TL_CACHE_H_INT4, D_><<<grid, 256, 0, s>>>(a); \
-    else if (c.mode == TL_CACHE_H_INT8) absorbed_attn_kernel<TL_CACHE_H_INT8, D_><<<grid, 256, 0, s>>>(a); \
-    else absorbed_attn_kernel<TL_CACHE_H_F16, D_><<<grid, 256, 0, s>>>(a);                     \
+    if (c.mode == TL_CACHE_H_INT4) return launch_timed(absorbed_attn_kernel<TL_CACHE_H_INT4, D_>, grid, 256, s, ev, a); \
+    if (c.mode == TL_CACHE_H_INT8) return launch_timed(absorbed_attn_kernel<TL_CACHE_H_INT8, D_>, grid, 256, s, ev, a); \
+    return launch_timed(absorbed_attn_kernel<TL_CACHE_H_F16, D_>, grid, 256, s, ev, a);          \
   } while (0)
   if (m.D == 1024) TL_ABS(1024);
   else TL_ABS(2048);
 #undef TL_ABS
-  return hipGetLastError();
 }
 
 hipError_t launch_absorbed_out(const ModelView& m, int n_rows, const int32_t* row_lane,

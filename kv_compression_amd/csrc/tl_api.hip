@@ -739,19 +739,22 @@ tl_status decode_enqueue(tl_cache* c, const Workspace& ws, int n, const int32_t*
     ra.part = ws.part; ra.S = ws.S;
     int split_len;
     if (c->prof_on) {
+      // profiling: a pair of events that take the attention kernel's own
+      // start and end (the launch gaps around it, and any merge launch
+      // after it, are not counted)
       while (c->prof_ev.size() < c->prof_used + 2) {
         hipEvent_t e;
         TL_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
         c->prof_ev.push_back(e);
       }
+      ra.ev.start = c->prof_ev[c->prof_used];
+      ra.ev.stop = c->prof_ev[c->prof_used + 1];
     }
-    // the profiling events bracket the attention kernel alone
     if (c->mode == TL_CACHE_KV) {
       GemmArgs g = gemm_args(W.w_qkv, D, ws.x, D, rows, 3 * D, D, EPI_QKV, ws.q, D);
       g.scale = qscale; g.q_is_t = 0;
       row_work(g);
       TL_HIP(launch_gemm(mv, g, s));
-      if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
       TL_HIP(launch_kv_attn(mv, ra, s));
       split_len = kKvSplit;
     } else {
@@ -770,13 +773,8 @@ tl_status decode_enqueue(tl_cache* c, const Workspace& ws, int n, const int32_t*
         TL_HIP(launch_absorb_q(mv, rows, ws.q, W.w_qkv, ws.qt, s));
         int sl = 0;
         const int S = absorbed_splits(rows, t_ub, ws.apair_cap, &sl);
-        if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
         TL_HIP(launch_absorbed_attn(mv, ra.cache, ra.layer, rows, ws.row_lane, ws.row_pos, ws.status,
-                                    ws.qt, ws.apart, S, sl, s));
-        if (c->prof_on) {
-          TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
-          c->prof_used += 2;
-        }
+                                    ws.qt, ws.apart, S, sl, s, ra.ev));
         // (the merged r reuses the qt rows, which the attention kernel has consumed)
         TL_HIP(launch_absorbed_out(mv, rows, ws.row_lane, ws.row_pos, ws.status, ws.apart, S, sl,
                                    W.w_qkv, ws.qt, ws.o, s));
@@ -788,20 +786,12 @@ tl_status decode_enqueue(tl_cache* c, const Workspace& ws, int n, const int32_t*
           ra.o = ws.o;
           ra.tilecnt = ws.tilecnt;
         }
-        if (c->prof_on) TL_HIP(hipEventRecord(c->prof_ev[c->prof_used], s));
         TL_HIP(launch_recon_attn(mv, ra, s));
         split_len = fused ? 0 : recon_split_len(mv, ra.cache.mode);
-        if (fused && c->prof_on) {
-          TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
-          c->prof_used += 2;
-        }
       }
     }
+    if (c->prof_on) c->prof_used += 2;   // the pair was taken by a launch
     if (split_len) {
-      if (c->prof_on) {
-        TL_HIP(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
-        c->prof_used += 2;
-      }
       TL_HIP(launch_attn_merge(mv, rows, ws.row_lane, ws.row_pos, ws.status, ws.part, ws.S, split_len,
                                ws.o, s));
     }

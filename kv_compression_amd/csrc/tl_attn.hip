@@ -561,18 +561,16 @@ hipError_t launch_kv_attn(const ModelView& m, const ReconArgs& a, hipStream_t s)
   const int grid = n_splits * a.n_rows;
   if (n_splits > a.S) return hipErrorInvalidValue;
   if (m.dtype == TL_DTYPE_F32 && m.D == 128 && m.dh == 32)
-    kv_attn_kernel<float, 128, 32, 256><<<grid, 256, 0, s>>>(m, a, n_splits);
+    return launch_timed(kv_attn_kernel<float, 128, 32, 256>, grid, 256, s, a.ev, m, a, n_splits);
   else if (m.dtype == TL_DTYPE_F16 && m.D == 1024 && m.dh == 64)
-    kv_attn_kernel<half_t, 1024, 64, 256><<<grid, 256, 0, s>>>(m, a, n_splits);
+    return launch_timed(kv_attn_kernel<half_t, 1024, 64, 256>, grid, 256, s, a.ev, m, a, n_splits);
   else if (m.dtype == TL_DTYPE_F16 && m.D == 2048 && m.dh == 128)
-    kv_attn_kernel<half_t, 2048, 128, 512><<<grid, 512, 0, s>>>(m, a, n_splits);
+    return launch_timed(kv_attn_kernel<half_t, 2048, 128, 512>, grid, 512, s, a.ev, m, a, n_splits);
   else if (m.dtype == TL_DTYPE_F16 && m.D == 2048 && m.dh == 64)
-    kv_attn_kernel<half_t, 2048, 64, 512><<<grid, 512, 0, s>>>(m, a, n_splits);
+    return launch_timed(kv_attn_kernel<half_t, 2048, 64, 512>, grid, 512, s, a.ev, m, a, n_splits);
   else if (m.dtype == TL_DTYPE_F16 && m.D == 1024 && m.dh == 128)
-    kv_attn_kernel<half_t, 1024, 128, 256><<<grid, 256, 0, s>>>(m, a, n_splits);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+    return launch_timed(kv_attn_kernel<half_t, 1024, 128, 256>, grid, 256, s, a.ev, m, a, n_splits);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_merge(const ModelView& m, int n_rows, const int32_t* row_lane,

@@ -2,6 +2,7 @@
 // translation units. Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -252,6 +253,18 @@ hipError_t launch_gemm(const ModelView& m, const GemmArgs& g, hipStream_t s);
 
 // Decode attention over the store-h cache: rebuild K|V of every position with
 // MFMA and fold them into per-split online-softmax partials.
+// Timing of one kernel: events that take that launch's own start and end
+// timestamps (hipExtLaunchKernel), so the time between them is the kernel's
+// execution without the launch gaps around it. Null: not timed.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+template <typename F, typename... A>
+hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, const LaunchEvents& ev, A... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  return hipGetLastError();
+}
+
 struct ReconArgs {
   CacheView cache;
   int layer;
@@ -268,6 +281,7 @@ struct ReconArgs {
   // each (row, head group) merges the tiles into o, and no split merge follows
   void* o;
   int32_t* tilecnt;          // [rows, 2 D / 128] zero before the first launch
+  LaunchEvents ev;           // timing of the attention kernel
 };
 hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& a, hipStream_t s);
 int recon_split_len(const ModelView& m, int mode);
@@ -346,7 +360,7 @@ hipError_t launch_absorb_q(const ModelView& m, int n_rows, const float* q, const
 hipError_t launch_absorbed_attn(const ModelView& m, const CacheView& c, int layer, int n_rows,
                                 const int32_t* row_lane, const int32_t* row_pos,
                                 const int32_t* status, const float* qt, float* part, int S,
-                                int split_len, hipStream_t s);
+                                int split_len, hipStream_t s, const LaunchEvents& ev = {});
 // merge the splits into rbuf [rows][H][D] (r / l, fp32), then
 // o[row][h d + j] = W_v,h r (model dtype)
 hipError_t launch_absorbed_out(const ModelView& m, int n_rows, const int32_t* row_lane,

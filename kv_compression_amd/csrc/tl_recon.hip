@@ -1198,28 +1198,30 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
 }
 
 template <typename T, int MODE, int DH, int VAR = 0>
-hipError_t launch_mode(const KArgs& k, int grid, hipStream_t s, int epi) {
-  if (epi == EPI_ATTN) recon_kernel<T, MODE, DH, EPI_ATTN, VAR><<<grid, Cfg<T, MODE, DH, VAR>::NT, 0, s>>>(k);
-  else recon_kernel<T, MODE, DH, EPI_KVSTORE, VAR><<<grid, Cfg<T, MODE, DH, VAR>::NT, 0, s>>>(k);
+hipError_t launch_mode(const KArgs& k, int grid, hipStream_t s, int epi, const LaunchEvents& ev) {
+  constexpr int NT = Cfg<T, MODE, DH, VAR>::NT;
+  if (epi == EPI_ATTN) return launch_timed(recon_kernel<T, MODE, DH, EPI_ATTN, VAR>, grid, NT, s, ev, k);
+  recon_kernel<T, MODE, DH, EPI_KVSTORE, VAR><<<grid, NT, 0, s>>>(k);
   return hipGetLastError();
 }
 
 // var 1, 2: the one-head fp16-h configurations (decode attention only)
-hipError_t dispatch(const ModelView& m, const KArgs& k, int grid, hipStream_t s, int epi, int var = 0) {
+hipError_t dispatch(const ModelView& m, const KArgs& k, int grid, hipStream_t s, int epi, int var = 0,
+                    const LaunchEvents& ev = {}) {
   if (var == 1 || var == 2) {
     if (!(m.dtype == TL_DTYPE_F16 && k.cache.mode == TL_CACHE_H_F16 && m.dh == 64 && epi == EPI_ATTN))
       return hipErrorInvalidValue;
-    return var == 1 ? launch_mode<half_t, TL_CACHE_H_F16, 64, 1>(k, grid, s, epi)
-                    : launch_mode<half_t, TL_CACHE_H_F16, 64, 2>(k, grid, s, epi);
+    return var == 1 ? launch_mode<half_t, TL_CACHE_H_F16, 64, 1>(k, grid, s, epi, ev)
+                    : launch_mode<half_t, TL_CACHE_H_F16, 64, 2>(k, grid, s, epi, ev);
   }
   if (m.dtype == TL_DTYPE_F32) {
     if (m.dh == 32 && k.cache.mode == TL_CACHE_H_F32)
-      return launch_mode<float, TL_CACHE_H_F32, 32>(k, grid, s, epi);
+      return launch_mode<float, TL_CACHE_H_F32, 32>(k, grid, s, epi, ev);
     return hipErrorInvalidValue;
   }
   const int mode = k.cache.mode;
 #define TL_RECON_CASE(MODE_, DH_) \
-  if (mode == MODE_ && m.dh == DH_) return launch_mode<half_t, MODE_, DH_>(k, grid, s, epi);
+  if (mode == MODE_ && m.dh == DH_) return launch_mode<half_t, MODE_, DH_>(k, grid, s, epi, ev);
   TL_RECON_CASE(TL_CACHE_H_INT4, 64)
   TL_RECON_CASE(TL_CACHE_H_INT4, 128)
   TL_RECON_CASE(TL_CACHE_H_INT8, 64)
@@ -1308,7 +1310,7 @@ hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t
   const long n_tiles = (long)k.n_ptiles * r.n_rows;
   const long grid = ((n_tiles + parts - 1) / parts) * parts * k.n_hg;
   if (grid <= 0 || grid > (1L << 30)) return hipErrorInvalidValue;
-  return dispatch(m, k, (int)grid, s, EPI_ATTN, var);
+  return dispatch(m, k, (int)grid, s, EPI_ATTN, var, r.ev);
 }
 
 hipError_t launch_recon_store(const ModelView& m, const CacheView& c, int layer, int lane, int T,
