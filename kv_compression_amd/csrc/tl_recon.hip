@@ -40,9 +40,10 @@ namespace {
 //   fp16 h (staged through LDS from registers): 8 waves, 2 per SIMD, 128 x 64.
 //   fp32: 4 waves of 64 x 64.
 // OCC: workgroups resident per CU (waves per SIMD), which sets the register
-// budget of a wave (512 / OCC, accumulators included).
+// budget of a wave (512 / OCC, accumulators included). NBUF: stage buffers of
+// the LDS ring of the copied-operand path.
 template <typename T, int MODE, int DH, int VAR = 0> struct Cfg {
-  static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1;
+  static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
 // fp16 h at 64-wide heads when a launch has too few rows and position tiles
@@ -50,17 +51,17 @@ template <typename T, int MODE, int DH, int VAR = 0> struct Cfg {
 // context of about a thousand: 40 workgroups): one head (its 64 K and 64 V
 // rows) per workgroup, so twice the workgroups with half the work each.
 template <> struct Cfg<half_t, TL_CACHE_H_F16, 64, 1> {
-  static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1;
+  static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
 // ... and with 128-position tiles when even that leaves CUs idle
 template <> struct Cfg<half_t, TL_CACHE_H_F16, 64, 2> {
-  static constexpr int BF = 128, BJ = 128, WF = 128, WJ = 64, BK = 64, OCC = 1;
+  static constexpr int BF = 128, BJ = 128, WF = 128, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
 // integer codes: every wave covers all BF features of its positions
 template <int MODE, int DH> struct CfgCodes {
-  static constexpr int BF = 256, BJ = 256, WF = 256, WJ = 64, BK = 64, OCC = 1;
+  static constexpr int BF = 256, BJ = 256, WF = 256, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
 template <int DH> struct Cfg<half_t, TL_CACHE_H_INT8, DH> : CfgCodes<TL_CACHE_H_INT8, DH> {};
@@ -72,11 +73,19 @@ template <int DH> struct Cfg<half_t, TL_CACHE_H_INT4, DH> : CfgCodes<TL_CACHE_H_
 // workgroup per CU, time the same at 4096 positions and lose a third
 // dispatch round just past it.)
 template <> struct Cfg<half_t, TL_CACHE_H_INT4, 64> {
-  static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 2;
+  static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 2, NBUF = 3;
+  static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+};
+// INT8 codes with 64-wide heads: the same shape, two workgroups per CU; a
+// stage's h codes are twice INT4's, so the ring has two stage buffers (a
+// stage's copies have one stage of MFMA work to land, which the other
+// workgroup's MFMAs lengthen)
+template <> struct Cfg<half_t, TL_CACHE_H_INT8, 64> {
+  static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 2, NBUF = 2;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
 template <int MODE, int DH> struct Cfg<float, MODE, DH> {
-  static constexpr int BF = 128, BJ = 128, WF = 64, WJ = 64, BK = 64, OCC = 1;
+  static constexpr int BF = 128, BJ = 128, WF = 64, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
 };
 // the fp16 configurations other than INT4 at 64-wide heads share BJ and WJ
@@ -283,7 +292,8 @@ __device__ __forceinline__ int w_swz(int R) { return ((R >> 1) ^ (R << 2)) & 7; 
 template <typename T, int MODE, int DH, int EPI, int VAR = 0>
 __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>::OCC)) void recon_kernel(KArgs a) {
   typedef Cfg<T, MODE, DH, VAR> C;
-  constexpr int BF = C::BF, BJ = C::BJ, WF = C::WF, WJ = C::WJ, BK = C::BK, NT = C::NT;
+  constexpr int BF = C::BF, BJ = C::BJ, WF = C::WF, WJ = C::WJ, BK = C::BK, NT = C::NT, NBUF = C::NBUF;
+  static_assert(NBUF == 2 || NBUF == 3, "ring depth");
   constexpr int WJN = BJ / WJ;                // waves along positions
   constexpr int ES = sizeof(T);
   constexpr int ROWB = BK * ES + 16;          // padded LDS row bytes
@@ -432,12 +442,13 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
 
   if constexpr (B_REG) {
     // ---- W rows and h codes copied by the memory unit straight into LDS -----
-    // A ring of three stage buffers, each one separate LDS array: stage st
-    // reads buffer st % 3 while the copies of stages st+1 and st+2 are in
-    // flight, so every load has two stages of MFMA work to land. Each wave
-    // issues exactly DMA_PER_STAGE copies per stage; waiting until only the
-    // newest stage's copies are outstanding (the counter drains in issue order)
-    // and then synchronising the workgroup publishes the next stage's buffer.
+    // A ring of NBUF stage buffers, each one separate LDS array: stage st
+    // reads buffer st % NBUF while the copies of the next NBUF - 1 stages are
+    // in flight, so every load has NBUF - 1 stages of MFMA work to land. Each
+    // wave issues exactly DMA_PER_STAGE copies per stage; waiting until only
+    // the copies after stage st+1 are outstanding (the counter drains in issue
+    // order) and then synchronising the workgroup publishes the next stage's
+    // buffer.
     //   W tile: BF rows x 128 bytes, 16-byte chunk c of row R at slot
     //     c ^ swz(R), so the fragment reads of 16 consecutive rows are spread
     //     over all banks without padding. One copy instruction fills 1 KB
@@ -458,7 +469,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     constexpr int DMA_PER_STAGE = W_IPW + H_IPW + (S_BYTES ? 1 : 0);
     static_assert(W_IPW * NW * 1024 == W_BYTES && H_IPW * NW * 1024 == H_BYTES, "copy split");
     static_assert(S_BYTES == 0 || S_BYTES == NW * 256, "one 4-byte copy per lane and wave for the scales");
-    static_assert(3 * (W_BYTES + H_BYTES + S_BYTES) <= 160 * 1024, "LDS ring");
+    static_assert(C::OCC * NBUF * (W_BYTES + H_BYTES + S_BYTES) <= 160 * 1024, "LDS ring");
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
     uint32_t woff[W_IPW];     // byte offset of the lane's W chunk (stage 0)
@@ -587,16 +598,17 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     // fragments of kk+1 are read and its B operands dequantised. Before the
     // last k-step the wave waits for the copies of stage st+1 and joins the
     // workgroup barrier: every wave is then done with buffer BUF, which takes
-    // the copies of stage st+3 (part A now, parts B and C during k-steps 0
-    // and 1 of stage st+1), and the operands of the next stage's first
-    // k-step are read and dequantised under the last k-step's MFMAs.
+    // the copies of stage st+NBUF (three buffers: part A now, parts B and C
+    // during k-steps 0 and 1 of stage st+1; two buffers: all of them now), and
+    // the operands of the next stage's first k-step are read and dequantised
+    // under the last k-step's MFMAs.
     // Every stage issues its copies and waits the same way, past the last
     // stage too (the copy index is clamped to the last stage), so all paths
     // through the loop leave the same copies in flight.
     auto stage = [&](auto buf_c, auto nb_c, int st, Frag (&ca)[RB], half8 (&fbc)[CB], R& raw) {
       constexpr int BUF = decltype(buf_c)::value;
       constexpr int NB = decltype(nb_c)::value;
-      constexpr int NXT = (BUF + 1) % 3;
+      constexpr int NXT = (BUF + 1) % NBUF;
       const char* rb = Ring<BUF, RING>::p();
       Frag na[RB];
       half8 fbn[CB];
@@ -612,12 +624,14 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
 #pragma unroll
         for (int j = 0; j < CB; ++j) fd[j] = fs[j];
       };
-      constexpr int PREV = (BUF + 2) % 3;   // buffer of stage st+2 (freed by the last barrier)
+      constexpr int PREV = (BUF + NBUF - 1) % NBUF;   // three buffers: stage st+2's (freed by the last barrier)
       const int st2 = min(st + 2, nst - 1);
 #pragma unroll
       for (int kk = 0; kk < BK / 16 - 1; ++kk) {
-        if (kk == 0) issue_ops(std::integral_constant<int, PREV>{}, IA1{}, IB1{}, st2);
-        if (kk == 1) issue_ops(std::integral_constant<int, PREV>{}, IB1{}, IC1{}, st2);
+        if constexpr (NBUF == 3) {
+          if (kk == 0) issue_ops(std::integral_constant<int, PREV>{}, IA1{}, IB1{}, st2);
+          if (kk == 1) issue_ops(std::integral_constant<int, PREV>{}, IB1{}, IC1{}, st2);
+        }
         if constexpr (NB > 0) {
           read_a3(rb, kk + 1, na);
 #pragma unroll
@@ -627,7 +641,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
 #pragma unroll
           for (int g = 0; g < RB; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            if (g < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // copy
+            if (NBUF == 3 && g < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // copy
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -637,10 +651,15 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (NB > 0) copy_ops(ca, na, fbc, fbn);
       }
-      // copies of stage st+1 landed once only stage st+2's remain; after the
-      // barrier no wave reads buffer BUF any more
-      dma_sync<DMA_PER_STAGE>();
-      issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IA1{}, min(st + 3, nst - 1));
+      // copies of stage st+1 landed once only stage st+2's remain (three
+      // buffers) or none (two); after the barrier no wave reads buffer BUF
+      if constexpr (NBUF == 3) {
+        dma_sync<DMA_PER_STAGE>();
+        issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IA1{}, min(st + 3, nst - 1));
+      } else {
+        dma_sync<0>();
+        issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IC1{}, min(st + 2, nst - 1));
+      }
       if constexpr (NB > 0) {
         // operands of the next stage's k-step 0 (its buffer has landed; past
         // the last stage it holds a clamped copy and the values go unused)
@@ -651,10 +670,11 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
         mfmas(ca, fbc);
         // copies first (they follow no read of this wave), then the code and
         // fragment reads, then the dequantisation
+        constexpr int CPG = NBUF == 3 ? 1 : (DMA_PER_STAGE + 3) / 4;   // copies per MFMA
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // copy
+          __builtin_amdgcn_sched_group_barrier(0x010, CPG, 0);     // copies
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * NB, 0);   // code reads
 #pragma unroll
@@ -676,14 +696,18 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     float qpre = 0.f;
     if constexpr (EPI == EPI_ATTN)
       if (tid < HPW_T * DH) qpre = a.q[(size_t)r * D + hg * HPW_T * DH + tid];
-    // stages 0 and 1 and part A of stage 2 are issued back to back; the loop
-    // starts once stage 0 has landed, with the rest in flight exactly as at
-    // the end of every stage (the counter drains in issue order, so the
-    // queries, issued first, have arrived too)
+    // stages 0 and 1 (and, with three buffers, part A of stage 2) are issued
+    // back to back; the loop starts once stage 0 has landed, with the rest in
+    // flight exactly as at the end of every stage (the counter drains in
+    // issue order, so the queries, issued first, have arrived too)
     issue(std::integral_constant<int, 0>{}, 0);
     issue(std::integral_constant<int, 1>{}, min(1, nst - 1));
-    issue_ops(std::integral_constant<int, 2>{}, IA0{}, IA1{}, min(2, nst - 1));   // parts B, C: stage 0
-    dma_sync<DMA_PER_STAGE + PA>();
+    if constexpr (NBUF == 3) {
+      issue_ops(std::integral_constant<int, 2>{}, IA0{}, IA1{}, min(2, nst - 1));   // parts B, C: stage 0
+      dma_sync<DMA_PER_STAGE + PA>();
+    } else {
+      dma_sync<DMA_PER_STAGE>();
+    }
     if constexpr (EPI == EPI_ATTN)
       if (tid < HPW_T * DH) q_lds[tid] = qpre;   // read after the loop's barriers
     auto loop = [&](auto nb_c) {
@@ -698,13 +722,21 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
         for (int j = 0; j < NB; ++j) fbc[j] = b_frag(raw, j, 0);
       }
       int st = 0;
-      for (; st + 3 <= nst; st += 3) {
-        stage(std::integral_constant<int, 0>{}, nb_c, st, ca, fbc, raw);
-        stage(std::integral_constant<int, 1>{}, nb_c, st + 1, ca, fbc, raw);
-        stage(std::integral_constant<int, 2>{}, nb_c, st + 2, ca, fbc, raw);
+      if constexpr (NBUF == 3) {
+        for (; st + 3 <= nst; st += 3) {
+          stage(std::integral_constant<int, 0>{}, nb_c, st, ca, fbc, raw);
+          stage(std::integral_constant<int, 1>{}, nb_c, st + 1, ca, fbc, raw);
+          stage(std::integral_constant<int, 2>{}, nb_c, st + 2, ca, fbc, raw);
+        }
+        if (st < nst) stage(std::integral_constant<int, 0>{}, nb_c, st, ca, fbc, raw);
+        if (st + 1 < nst) stage(std::integral_constant<int, 1>{}, nb_c, st + 1, ca, fbc, raw);
+      } else {
+        for (; st + 2 <= nst; st += 2) {
+          stage(std::integral_constant<int, 0>{}, nb_c, st, ca, fbc, raw);
+          stage(std::integral_constant<int, 1>{}, nb_c, st + 1, ca, fbc, raw);
+        }
+        if (st < nst) stage(std::integral_constant<int, 0>{}, nb_c, st, ca, fbc, raw);
       }
-      if (st < nst) stage(std::integral_constant<int, 0>{}, nb_c, st, ca, fbc, raw);
-      if (st + 1 < nst) stage(std::integral_constant<int, 1>{}, nb_c, st + 1, ca, fbc, raw);
       dma_sync<0>();   // no copy may still be writing LDS past this point
     };
     // A tile with at most one live 32-position block (the tile just past a
@@ -755,15 +787,17 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
       // the copies go out and are waited for exactly as in `stage`
       auto stage_t = [&](auto buf_c, int st, Frag (&ca)[RBT], half8& fbc, R& raw) {
         constexpr int BUF = decltype(buf_c)::value;
-        constexpr int NXT = (BUF + 1) % 3, PREV = (BUF + 2) % 3;
+        constexpr int NXT = (BUF + 1) % NBUF, PREV = (BUF + NBUF - 1) % NBUF;
         const char* rb = Ring<BUF, RING>::p();
         const int st2 = min(st + 2, nst - 1);
         Frag na[RBT];
         half8 fbn;
 #pragma unroll
         for (int kk = 0; kk < BK / 16 - 1; ++kk) {
-          if (kk == 0) issue_ops(std::integral_constant<int, PREV>{}, IA1{}, IB1{}, st2);
-          if (kk == 1) issue_ops(std::integral_constant<int, PREV>{}, IB1{}, IC1{}, st2);
+          if constexpr (NBUF == 3) {
+            if (kk == 0) issue_ops(std::integral_constant<int, PREV>{}, IA1{}, IB1{}, st2);
+            if (kk == 1) issue_ops(std::integral_constant<int, PREV>{}, IB1{}, IC1{}, st2);
+          }
           read_at(rb, kk + 1, na);
           fbn = b_fragt(raw, kk + 1);
           if (trows)
@@ -774,8 +808,13 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
           for (int i = 0; i < RBT; ++i) ca[i] = na[i];
           fbc = fbn;
         }
-        dma_sync<DMA_PER_STAGE>();
-        issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IA1{}, min(st + 3, nst - 1));
+        if constexpr (NBUF == 3) {
+          dma_sync<DMA_PER_STAGE>();
+          issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IA1{}, min(st + 3, nst - 1));
+        } else {
+          dma_sync<0>();
+          issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IC1{}, min(st + 2, nst - 1));
+        }
         read_rawt(Ring<NXT, RING>::p(), raw);
         read_at(Ring<NXT, RING>::p(), 0, na);
         fbn = b_fragt(raw, 0);
@@ -795,13 +834,21 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
         read_at(Ring<0, RING>::p(), 0, ca);
         fbc = b_fragt(raw, 0);
         int st = 0;
-        for (; st + 3 <= nst; st += 3) {
-          stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
-          stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
-          stage_t(std::integral_constant<int, 2>{}, st + 2, ca, fbc, raw);
+        if constexpr (NBUF == 3) {
+          for (; st + 3 <= nst; st += 3) {
+            stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+            stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
+            stage_t(std::integral_constant<int, 2>{}, st + 2, ca, fbc, raw);
+          }
+          if (st < nst) stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+          if (st + 1 < nst) stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
+        } else {
+          for (; st + 2 <= nst; st += 2) {
+            stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+            stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
+          }
+          if (st < nst) stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
         }
-        if (st < nst) stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
-        if (st + 1 < nst) stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
         dma_sync<0>();
       }
       // row blocks w*RBT .. w*RBT+RBT-1 of wave w -> wave 0, through ring
@@ -1247,7 +1294,8 @@ static int recon_bf(const ModelView& m, int mode, int var = 0) {
   if (var == 2) return Cfg<half_t, TL_CACHE_H_F16, 64, 2>::BF;
   if (m.dtype == TL_DTYPE_F32) return Cfg<float, TL_CACHE_H_F32, 32>::BF;
   if (mode == TL_CACHE_H_INT4 && m.dh == 64) return Cfg<half_t, TL_CACHE_H_INT4, 64>::BF;
-  static_assert(Cfg<half_t, TL_CACHE_H_INT4, 128>::BF == 256 && Cfg<half_t, TL_CACHE_H_INT8, 64>::BF == 256 &&
+  if (mode == TL_CACHE_H_INT8 && m.dh == 64) return Cfg<half_t, TL_CACHE_H_INT8, 64>::BF;
+  static_assert(Cfg<half_t, TL_CACHE_H_INT4, 128>::BF == 256 &&
                     Cfg<half_t, TL_CACHE_H_INT8, 128>::BF == 256 && Cfg<half_t, TL_CACHE_H_F16, 64>::BF == 256 &&
                     Cfg<half_t, TL_CACHE_H_F16, 128>::BF == 256,
                 "other fp16 configurations");

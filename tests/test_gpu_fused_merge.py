@@ -59,8 +59,9 @@ def test_rows_change_lanes_and_tile_counts(mode):
             toks[k] = int(t[i])
 
 
-def test_tail_tiles_across_tile_boundaries():
-    """INT4 at 64-wide heads: a last position tile of at most 32 positions is
+@pytest.mark.parametrize("mode", ["int4", "int8"])
+def test_tail_tiles_across_tile_boundaries(mode):
+    """INT4 and INT8 at 64-wide heads: a last position tile of at most 32 positions is
     computed with its row blocks dealt over the four waves (the tail split),
     one of 33 or more as an ordinary partial tile. One launch mixes rows on
     both sides of that boundary (prompts of 256, 287, 288 and 543 tokens:
@@ -70,7 +71,7 @@ def test_tail_tiles_across_tile_boundaries():
     lens = [256, 287, 288, 543]
     prompts = [synth.make_prompts(S407.vocab, 1, n, 40 + i)[0] for i, n in enumerate(lens)]
     loops = [2, 1, 3, 2]
-    orc, c, toks = _both(gm, w, "int4", prompts, loops, 560, 3)
+    orc, c, toks = _both(gm, w, mode, prompts, loops, 560, 3)
     for step, lanes in enumerate([[0, 1, 2, 3], [3, 1], [2, 0, 3], [1, 2, 3, 0]]):
         lp = [loops[k] for k in lanes]
         tin = [toks[k] for k in lanes]
@@ -78,13 +79,13 @@ def test_tail_tiles_across_tile_boundaries():
         for i, k in enumerate(lanes):
             assert st[i] == 0
             e = rel_err(lg[i], r["logits"][i])
-            record("tail_tiles", step=step, lane=k, T=int(orc.length[k]), rel=e)
+            record("tail_tiles", mode=mode, step=step, lane=k, T=int(orc.length[k]), rel=e)
             assert e <= REL_TOL, (step, k, e)
             assert token_ok(int(t[i]), r["logits"][i]), (step, k)
             toks[k] = int(t[i])
 
 
-@pytest.mark.parametrize("mode", ["int4", "f16"])
+@pytest.mark.parametrize("mode", ["int4", "int8", "f16"])
 def test_abort_mid_step_leaves_counters_clean(mode):
     w, gm = gpu_model(S407)
     L = 4
