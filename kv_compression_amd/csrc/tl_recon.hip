@@ -33,10 +33,11 @@ namespace {
 
 // Tile shapes (BF features x BJ positions per workgroup, WF x WJ per wave).
 //   INT4 / INT8 h (operands copied to LDS, h dequantised in registers): 4
-//   waves, one per SIMD, each owning all 256 features of the tile for 64
-//   positions (256 accumulators, held in AGPRs). Every dequantised h operand
-//   feeds 8 MFMAs, and the MFMAs of one k-step cover the dequantisation and
-//   LDS reads of the next.
+//   waves, one per SIMD, each owning all the tile's features for 64
+//   positions: 256 features (two heads of 64 or one of 128; 256 accumulators
+//   in AGPRs), or 128 (one head of 64, two workgroups per CU). Every
+//   dequantised h operand feeds 8 (or 4) MFMAs, and the MFMAs of one k-step
+//   cover the dequantisation and LDS reads of the next.
 //   fp16 h (staged through LDS from registers): 8 waves, 2 per SIMD, 128 x 64.
 //   fp32: 4 waves of 64 x 64.
 // OCC: workgroups resident per CU (waves per SIMD), which sets the register
