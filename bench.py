@@ -393,8 +393,8 @@ def decode_both_orders(torch, tl, wl, loops, steps, warmup, label, orders=("expl
     st = torch.empty_like(tin)
     start = ctx + wl.chunk
     t_values = [start + warmup + 1 + s for s in range(steps)]
-    for order in orders:
-        cache.tl_cache_set_attention(order)
+    def run(profile):
+        # warm-up and `steps` timed steps from the same start
         for k in range(wl.lanes):
             cache.tl_cache_set_length(k, start, sh.n_pre + loops[k])
         a, b = tin.clone(), tout
@@ -402,15 +402,22 @@ def decode_both_orders(torch, tl, wl, loops, steps, warmup, label, orders=("expl
             cache.tl_decode_step(lanes, loops, a, wl.threshold, b, None, st)
             a, b = b, a
         torch.cuda.synchronize()
-        cache.tl_profile_start()
+        if profile:
+            cache.tl_profile_start()
         t0 = time.perf_counter()
         for _ in range(steps):
             cache.tl_decode_step(lanes, loops, a, wl.threshold, b, None, st)
             a, b = b, a
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kern_ms, launches = cache.tl_profile_stop()
+        kern = cache.tl_profile_stop() if profile else None
         assert np.all(st.cpu().numpy() == 0)
+        return wall, kern
+
+    for order in orders:
+        cache.tl_cache_set_attention(order)
+        wall, _ = run(False)
+        _, (kern_ms, launches) = run(True)   # the attention kernel, same steps
         flops, _, n_launch = recon_flops_bytes(sh, eb, lanes, loops, t_values)
         assert n_launch == launches, (n_launch, launches)
         out[order] = {"decode_tok_s": round(wl.lanes * steps / wall, 1),
@@ -459,11 +466,13 @@ def measure_tiny(torch, tl, steps=256, warmup=8):
 
         run(warmup)
         torch.cuda.synchronize()
-        c.tl_profile_start()
         t0 = time.perf_counter()
         run(steps)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        # the attention kernel timed over the same steps again
+        c.tl_profile_start()
+        run(steps)
         kern_ms, launches = c.tl_profile_stop()
         assert int(st.cpu()[0]) == 0
         out[mode] = {"ms_per_step": round(wall * 1e3 / steps, 4), "tok_s": round(steps / wall, 1),
@@ -496,18 +505,27 @@ def measure_f16h_ctx1024(torch, tl, steps=128, warmup=2):
     for _ in range(warmup):
         c.tl_decode_step([0], [L], a, wl.threshold, b, None, st)
         a, b = b, a
-    c.tl_cache_set_length(0, ctx, sh.n_pre + L)
-    a.copy_(nxt)
-    torch.cuda.synchronize()
-    c.tl_profile_start()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        c.tl_decode_step([0], [L], a, wl.threshold, b, None, st)
-        a, b = b, a
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms, launches = c.tl_profile_stop()
-    assert int(st.cpu()[0]) == 0
+
+    def decode_steps(profile):
+        # `steps` greedy steps from the prompt's first token
+        nonlocal a, b
+        c.tl_cache_set_length(0, ctx, sh.n_pre + L)
+        a.copy_(nxt)
+        torch.cuda.synchronize()
+        if profile:
+            c.tl_profile_start()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            c.tl_decode_step([0], [L], a, wl.threshold, b, None, st)
+            a, b = b, a
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = c.tl_profile_stop() if profile else None
+        assert int(st.cpu()[0]) == 0
+        return wall, kern
+
+    wall, _ = decode_steps(False)
+    _, (kern_ms, launches) = decode_steps(True)   # the attention kernel, same steps
     eb = c.cache_bytes / ((sh.n_pre + L) * (ctx + steps + warmup + 1))
     flops, _, n_launch = recon_flops_bytes(sh, eb, [0], [L], [ctx + 1 + s for s in range(steps)])
     assert n_launch == launches, (n_launch, launches)
@@ -529,18 +547,8 @@ def measure_f16h_ctx1024(torch, tl, steps=128, warmup=2):
     for _ in range(warmup):
         c.tl_decode_step([0], [L], a, wl.threshold, b, None, st)
         a, b = b, a
-    c.tl_cache_set_length(0, ctx, sh.n_pre + L)
-    a.copy_(nxt)
-    torch.cuda.synchronize()
-    c.tl_profile_start()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        c.tl_decode_step([0], [L], a, wl.threshold, b, None, st)
-        a, b = b, a
-    torch.cuda.synchronize()
-    wall_a = time.perf_counter() - t0
-    kern_a, launches_a = c.tl_profile_stop()
-    assert int(st.cpu()[0]) == 0
+    wall_a, _ = decode_steps(False)
+    _, (kern_a, launches_a) = decode_steps(True)
     out["absorbed"] = {"decode_tok_s": round(steps / wall_a, 1), "ms_per_step": round(wall_a * 1e3 / steps, 4),
                        "attention_kernel": "absorbed_attn",
                        "attention_kernel_avg_us": round(kern_a * 1e3 / launches_a, 2),

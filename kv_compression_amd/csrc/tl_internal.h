@@ -261,7 +261,8 @@ struct LaunchEvents {
 };
 template <typename F, typename... A>
 hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, const LaunchEvents& ev, A... args) {
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  if (ev.start) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  else kernel<<<grid, block, 0, s>>>(args...);
   return hipGetLastError();
 }
 
