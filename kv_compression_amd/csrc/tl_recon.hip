@@ -46,6 +46,15 @@ namespace {
 template <typename T, int MODE, int DH, int VAR = 0> struct Cfg {
   static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+  static constexpr bool COPY16 = false;   // fp16 h through the copied-operand ring
+};
+// fp16 h at 64-wide heads: the W tile and the h tile (both 128-byte rows of
+// one stage) are copied into a two-buffer ring and the h fragments are read
+// from it as the MFMA B operand, 8 waves of one head x 64 positions
+template <> struct Cfg<half_t, TL_CACHE_H_F16, 64> {
+  static constexpr int BF = 256, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1, NBUF = 2;
+  static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+  static constexpr bool COPY16 = true;
 };
 // fp16 h at 64-wide heads when a launch has too few rows and position tiles
 // to give every CU a workgroup of the configuration above (one lane at a
@@ -54,16 +63,19 @@ template <typename T, int MODE, int DH, int VAR = 0> struct Cfg {
 template <> struct Cfg<half_t, TL_CACHE_H_F16, 64, 1> {
   static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+  static constexpr bool COPY16 = false;
 };
 // ... and with 128-position tiles when even that leaves CUs idle
 template <> struct Cfg<half_t, TL_CACHE_H_F16, 64, 2> {
   static constexpr int BF = 128, BJ = 128, WF = 128, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+  static constexpr bool COPY16 = false;
 };
 // integer codes: every wave covers all BF features of its positions
 template <int MODE, int DH> struct CfgCodes {
   static constexpr int BF = 256, BJ = 256, WF = 256, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+  static constexpr bool COPY16 = false;
 };
 template <int DH> struct Cfg<half_t, TL_CACHE_H_INT8, DH> : CfgCodes<TL_CACHE_H_INT8, DH> {};
 template <int DH> struct Cfg<half_t, TL_CACHE_H_INT4, DH> : CfgCodes<TL_CACHE_H_INT4, DH> {};
@@ -76,6 +88,7 @@ template <int DH> struct Cfg<half_t, TL_CACHE_H_INT4, DH> : CfgCodes<TL_CACHE_H_
 template <> struct Cfg<half_t, TL_CACHE_H_INT4, 64> {
   static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 2, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+  static constexpr bool COPY16 = false;
 };
 // INT8 codes with 64-wide heads: the same shape, two workgroups per CU; a
 // stage's h codes are twice INT4's, so the ring has two stage buffers (a
@@ -84,10 +97,12 @@ template <> struct Cfg<half_t, TL_CACHE_H_INT4, 64> {
 template <> struct Cfg<half_t, TL_CACHE_H_INT8, 64> {
   static constexpr int BF = 128, BJ = 256, WF = 128, WJ = 64, BK = 64, OCC = 2, NBUF = 2;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+  static constexpr bool COPY16 = false;
 };
 template <int MODE, int DH> struct Cfg<float, MODE, DH> {
   static constexpr int BF = 128, BJ = 128, WF = 64, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
+  static constexpr bool COPY16 = false;
 };
 // the fp16 configurations other than INT4 at 64-wide heads share BJ and WJ
 // (split length)
@@ -245,6 +260,10 @@ template <int CB> struct Raw<TL_CACHE_H_INT4, CB> {
 template <int CB> struct Raw<TL_CACHE_H_INT8, CB> {
   u32x4 w[CB][2];
 };
+// fp16 h read from the ring: the stage's buffer
+template <int CB> struct Raw<TL_CACHE_H_F16, CB> {
+  const char* rb;
+};
 
 #define TL_LDS __attribute__((address_space(3)))
 
@@ -301,22 +320,26 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
   constexpr int RB = WF / 32, CB = WJ / 32;   // MFMA blocks per wave
   constexpr int A_CPR = BK * ES / 16;         // 16-byte chunks per W row per stage
   constexpr int A_NCH = BF * A_CPR / NT;      // per thread
-  constexpr bool B_REG = MODE == TL_CACHE_H_INT4 || MODE == TL_CACHE_H_INT8;
+  constexpr bool B_REG = MODE == TL_CACHE_H_INT4 || MODE == TL_CACHE_H_INT8;   // codes dequantised in registers
+  constexpr bool H16C = C::COPY16;                    // fp16 h read from the ring
+  constexpr bool COPY = B_REG || H16C;                // operands copied into an LDS ring
+  static_assert(!H16C || (MODE == TL_CACHE_H_F16 && std::is_same<T, half_t>::value), "fp16 h");
   constexpr int B_NCH = B_REG ? HLoad<MODE>::NCH : BJ * HLoad<MODE>::CPP / NT;   // h chunks per thread
   constexpr int B_CPP = HLoad<MODE>::CPP;     // chunks per position
   static_assert(B_REG || BJ * B_CPP == NT * B_NCH, "h tile chunks");
-  static_assert(!B_REG || (std::is_same<T, half_t>::value && BK == kKBlock), "register h path");
-  constexpr int TILE_BYTES = (B_REG ? BF : BF + BJ) * ROWB;   // one LDS buffer (LDS-staged h)
-  __shared__ __attribute__((aligned(16))) char smem[B_REG ? 16 : 2 * TILE_BYTES];
+  static_assert(!COPY || (std::is_same<T, half_t>::value && BK == kKBlock), "copied-operand path");
+  constexpr int TILE_BYTES = (COPY ? BF : BF + BJ) * ROWB;   // one LDS buffer (LDS-staged h)
+  __shared__ __attribute__((aligned(16))) char smem[COPY ? 16 : 2 * TILE_BYTES];
   constexpr int HRB = block_row_bytes(MODE);
   // one LDS ring buffer of the copied path: W tile, h codes, INT4 scales
-  constexpr int RING = B_REG ? BF * BK * ES + BJ * HRB + (MODE == TL_CACHE_H_INT4 ? BJ * 4 : 0) : 16;
+  constexpr int RING = COPY ? BF * BK * ES + BJ * HRB + (MODE == TL_CACHE_H_INT4 ? BJ * 4 : 0) : 16;
   // per-wave attention partials of the copied-operand path, combined in LDS
   constexpr int NWV = NT / 64;
-  constexpr int HPW_T = 2 * DH > WF ? 1 : WF / (2 * DH);
-  __shared__ __attribute__((aligned(16))) float comb_lds[B_REG && EPI == EPI_ATTN ? NWV * HPW_T * (DH + 2) : 1];
+  constexpr int HPW_T = 2 * DH > WF ? 1 : WF / (2 * DH);   // heads per wave
+  constexpr int HGT = 2 * DH > BF ? 1 : BF / (2 * DH);     // heads per workgroup
+  __shared__ __attribute__((aligned(16))) float comb_lds[COPY && EPI == EPI_ATTN ? NWV * HPW_T * (DH + 2) : 1];
   // the queries of the workgroup's heads, staged at the start
-  __shared__ __attribute__((aligned(16))) float q_lds[B_REG && EPI == EPI_ATTN ? HPW_T * DH : 1];
+  __shared__ __attribute__((aligned(16))) float q_lds[COPY && EPI == EPI_ATTN ? HGT * DH : 1];
 
   const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
   const int wf = wave / WJN, wj = wave % WJN;
@@ -395,13 +418,13 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
   // (block j*WJN + wj), so a partial last tile spreads over all waves; the
   // LDS-staged path gives each wave WJ consecutive positions.
   auto pos_local = [&](int j) -> int {
-    return B_REG ? (j * WJN + wj) * 32 + (l & 31) : wj * WJ + j * 32 + (l & 31);
+    return COPY ? (j * WJN + wj) * 32 + (l & 31) : wj * WJ + j * 32 + (l & 31);
   };
   // blocks of this wave that hold positions < T (a prefix of j = 0, 1, ...);
   // the others are all zero, so their MFMAs are skipped while the wave keeps
   // loading and synchronising
   int ncb;
-  if constexpr (B_REG) {
+  if constexpr (COPY) {
     const int nbl = min(max((Tn - j0 + 31) / 32, 0), BJ / 32);
     ncb = 0;
 #pragma unroll
@@ -441,8 +464,8 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
       fa[i] = *(const Frag*)(As + (wf * WF + i * 32 + (l & 31)) * ROWB + kk * 16 * ES + koff);
   };
 
-  if constexpr (B_REG) {
-    // ---- W rows and h codes copied by the memory unit straight into LDS -----
+  if constexpr (COPY) {
+    // ---- W rows and h copied by the memory unit straight into LDS -----------
     // A ring of NBUF stage buffers, each one separate LDS array: stage st
     // reads buffer st % NBUF while the copies of the next NBUF - 1 stages are
     // in flight, so every load has NBUF - 1 stages of MFMA work to land. Each
@@ -458,9 +481,13 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     //   h codes: per 16 positions, the 16-byte runs of run index hq (half hb,
     //     part q of that half's k-run) sit side by side, so lanes 0..15 of a
     //     fragment read touch 16 consecutive slots.
+    //   fp16 h: BJ position rows of 128 bytes, laid out as the W tile (the
+    //     B fragments are read from it like the A fragments).
     //   INT4 scales: one 32-bit word (two fp16 group scales) per position.
-    // Positions past T copy the entry of position T-1 (always in bounds) and
-    // are zeroed through their scale when the operand is built.
+    // Positions past T copy the entry of position T-1 (always in bounds); the
+    // codes are zeroed through their scale when the operand is built, and
+    // fp16 rows are left as they are: their scores are masked, so their
+    // finite K and V rows weigh nothing.
     constexpr int NW = NT / 64;
     constexpr int NQ = HRB / 32;                         // 16-byte runs per half row
     constexpr int W_BYTES = BF * BK * ES;
@@ -485,9 +512,15 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
 #pragma unroll
     for (int i = 0; i < H_IPW; ++i) {
       const int S = (wave_u * H_IPW + i) * 64 + l;
-      const int pos = (S / (32 * NQ)) * 16 + S % 16;
-      const int hq = (S / 16) % (2 * NQ);
-      hoff[i] = (uint32_t)min(j0 + pos, Tn - 1) * HRB + hq * 16;
+      if constexpr (H16C) {
+        const int R = S >> 3;
+        const int c = (S & 7) ^ w_swz(R);
+        hoff[i] = (uint32_t)min(j0 + R, Tn - 1) * HRB + c * 16;
+      } else {
+        const int pos = (S / (32 * NQ)) * 16 + S % 16;
+        const int hq = (S / 16) % (2 * NQ);
+        hoff[i] = (uint32_t)min(j0 + pos, Tn - 1) * HRB + hq * 16;
+      }
     }
     const uint16_t* s4base = MODE == TL_CACHE_H_INT4 ? cv.int4_scale(a.layer, lane, 0, 0) : nullptr;
     // scale copy (LDS copies write one dword per lane): lane l of wave w
@@ -566,22 +599,30 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     };
     auto read_raw = [&](auto nb_c, const char* rb, R& raw) {
       constexpr int NB = decltype(nb_c)::value;
+      if constexpr (H16C) {
+        raw.rb = rb;
+      } else {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int pos = pos_local(j);
-        const char* hs = rb + W_BYTES + ((pos >> 4) * (32 * NQ) + hb * NQ * 16 + (pos & 15)) * 16;
-        if constexpr (MODE == TL_CACHE_H_INT4) {
-          raw.w[j] = *(const u32x4*)hs;
-          raw.s[j] = *(const uint32_t*)(rb + W_BYTES + H_BYTES + pos * 4);
-        } else {
-          raw.w[j][0] = *(const u32x4*)hs;
-          raw.w[j][1] = *(const u32x4*)(hs + 16 * 16);
+        for (int j = 0; j < NB; ++j) {
+          const int pos = pos_local(j);
+          const char* hs = rb + W_BYTES + ((pos >> 4) * (32 * NQ) + hb * NQ * 16 + (pos & 15)) * 16;
+          if constexpr (MODE == TL_CACHE_H_INT4) {
+            raw.w[j] = *(const u32x4*)hs;
+            raw.s[j] = *(const uint32_t*)(rb + W_BYTES + H_BYTES + pos * 4);
+          } else {
+            raw.w[j][0] = *(const u32x4*)hs;
+            raw.w[j][1] = *(const u32x4*)(hs + 16 * 16);
+          }
         }
       }
     };
-    // MFMA operand of block j, k-step kk: 8 fp16 = fp16(q * s)
+    // MFMA operand of block j, k-step kk: 8 fp16 = fp16(q * s), or the fp16
+    // h fragment (chunk kk*2 + hb of the block's position row)
     auto b_frag = [&](const R& raw, int j, int kk) -> half8 {
-      if constexpr (MODE == TL_CACHE_H_INT4) {
+      if constexpr (H16C) {
+        const int pos = pos_local(j);
+        return *(const half8*)(raw.rb + W_BYTES + pos * (BK * ES) + (((kk * 2 + hb) ^ w_swz(pos)) * 16));
+      } else if constexpr (MODE == TL_CACHE_H_INT4) {
         const uint32_t sv = ((vmask >> j) & 1) ? raw.s[j] : 0u;   // positions past T: scale 0
         const half_t sc = h_from_bits((uint16_t)(kk < 2 ? (sv & 0xFFFFu) : (sv >> 16)));
         return int4_dequant8(raw.w[j][kk], sc);
@@ -638,15 +679,24 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
 #pragma unroll
           for (int j = 0; j < NB; ++j) fbn[j] = b_frag(raw, j, kk + 1);
           mfmas(ca, fbc);
-          // 16 MFMAs, up to 4 copies, 8 fragment reads, ~40 dequantisation
+          if constexpr (H16C) {
+            // RB * NB MFMAs and RB + NB fragment reads
 #pragma unroll
-          for (int g = 0; g < RB; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            if (NBUF == 3 && g < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // copy
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            for (int g = 0; g < RB * NB; ++g) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+              if (g < RB + NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            }
+          } else {
+            // 16 MFMAs, up to 4 copies, 8 fragment reads, ~40 dequantisation
+#pragma unroll
+            for (int g = 0; g < RB; ++g) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+              if (NBUF == 3 && g < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // copy
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+              __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -677,16 +727,25 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
           __builtin_amdgcn_sched_group_barrier(0x010, CPG, 0);     // copies
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NB, 0);   // code reads
+        if constexpr (H16C) {
+          // the A and B fragment reads of the next stage's k-step 0
 #pragma unroll
-        for (int g = 0; g < RB / 2; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // A fragment reads
-        }
+          for (int g = 0; g < NB * RB - 4; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * NB, 0);   // code reads
 #pragma unroll
-        for (int g = 0; g < NB * RB - 4 - RB / 2; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          for (int g = 0; g < RB / 2; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // A fragment reads
+          }
+#pragma unroll
+          for (int g = 0; g < NB * RB - 4 - RB / 2; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         copy_ops(ca, na, fbc, fbn);
@@ -696,7 +755,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     // the workgroup's queries ride along with the first copies
     float qpre = 0.f;
     if constexpr (EPI == EPI_ATTN)
-      if (tid < HPW_T * DH) qpre = a.q[(size_t)r * D + hg * HPW_T * DH + tid];
+      if (tid < HGT * DH) qpre = a.q[(size_t)r * D + hg * HGT * DH + tid];
     // stages 0 and 1 (and, with three buffers, part A of stage 2) are issued
     // back to back; the loop starts once stage 0 has landed, with the rest in
     // flight exactly as at the end of every stage (the counter drains in
@@ -710,7 +769,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
       dma_sync<DMA_PER_STAGE>();
     }
     if constexpr (EPI == EPI_ATTN)
-      if (tid < HPW_T * DH) q_lds[tid] = qpre;   // read after the loop's barriers
+      if (tid < HGT * DH) q_lds[tid] = qpre;   // read after the loop's barriers
     auto loop = [&](auto nb_c) {
       constexpr int NB = decltype(nb_c)::value;
       Frag ca[RB];
@@ -746,61 +805,82 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     // over the same stages, and the waves then hand their rows to wave 0,
     // which runs the epilogue as if it had computed the block alone.
     // With more waves than row blocks the waves past the row blocks only copy.
-    constexpr int RBT = RB >= NW ? RB / NW : 1;
-    static_assert((RB >= NW ? RBT * NW == RB : NW % RB == 0) && RB * 16 * 64 * 4 <= RING, "tail split");
-    const bool tail = Tn - j0 <= 32;
-    if (tail) {
-      const bool trows = wave_u * RBT < RB;
-      const int trow = min(wave_u * RBT, RB - RBT) * 32 + (l & 31);
-      const uint32_t tmask = j0 + (l & 31) < Tn ? 1u : 0u;
-      auto read_at = [&](const char* rb, int kk, Frag (&fa)[RBT]) {
-        const char* base = rb + trow * (BK * ES) + (((kk * 2 + hb) ^ aswz) * 16);
+    // (tiles whose waves each hold all the tile's rows; the others run a
+    // partial last tile through the ordinary loop)
+    if constexpr (B_REG && WF == BF) {
+      constexpr int RBT = RB >= NW ? RB / NW : 1;
+      static_assert((RB >= NW ? RBT * NW == RB : NW % RB == 0) && RB * 16 * 64 * 4 <= RING, "tail split");
+      const bool tail = Tn - j0 <= 32;
+      if (tail) {
+        const bool trows = wave_u * RBT < RB;
+        const int trow = min(wave_u * RBT, RB - RBT) * 32 + (l & 31);
+        const uint32_t tmask = j0 + (l & 31) < Tn ? 1u : 0u;
+        auto read_at = [&](const char* rb, int kk, Frag (&fa)[RBT]) {
+          const char* base = rb + trow * (BK * ES) + (((kk * 2 + hb) ^ aswz) * 16);
 #pragma unroll
-        for (int i = 0; i < RBT; ++i) fa[i] = *(const Frag*)(base + i * 32 * (BK * ES));
-      };
-      // block 0 of the tile: position l % 32, the same for every wave
-      auto read_rawt = [&](const char* rb, R& raw) {
-        const int pos = l & 31;
-        const char* hs = rb + W_BYTES + ((pos >> 4) * (32 * NQ) + hb * NQ * 16 + (pos & 15)) * 16;
-        if constexpr (MODE == TL_CACHE_H_INT4) {
-          raw.w[0] = *(const u32x4*)hs;
-          raw.s[0] = *(const uint32_t*)(rb + W_BYTES + H_BYTES + pos * 4);
-        } else {
-          raw.w[0][0] = *(const u32x4*)hs;
-          raw.w[0][1] = *(const u32x4*)(hs + 16 * 16);
-        }
-      };
-      half_t s8t = (half_t)0.f;
-      if constexpr (MODE == TL_CACHE_H_INT8)
-        s8t = tmask ? h_from_bits(*cv.int8_scale(a.layer, lane, j0 + (l & 31))) : (half_t)0.f;
-      auto b_fragt = [&](const R& raw, int kk) -> half8 {
-        if constexpr (MODE == TL_CACHE_H_INT4) {
-          const uint32_t sv = tmask ? raw.s[0] : 0u;
-          const half_t sc = h_from_bits((uint16_t)(kk < 2 ? (sv & 0xFFFFu) : (sv >> 16)));
-          return int4_dequant8(raw.w[0][kk], sc);
-        } else {
-          const u32x4& w = raw.w[0][kk >> 1];
-          const half4 lo = int8_dequant4(w[(kk & 1) * 2], s8t);
-          const half4 hi = int8_dequant4(w[(kk & 1) * 2 + 1], s8t);
-          return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-      };
-      // the copies go out and are waited for exactly as in `stage`
-      auto stage_t = [&](auto buf_c, int st, Frag (&ca)[RBT], half8& fbc, R& raw) {
-        constexpr int BUF = decltype(buf_c)::value;
-        constexpr int NXT = (BUF + 1) % NBUF, PREV = (BUF + NBUF - 1) % NBUF;
-        const char* rb = Ring<BUF, RING>::p();
-        const int st2 = min(st + 2, nst - 1);
-        Frag na[RBT];
-        half8 fbn;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16 - 1; ++kk) {
-          if constexpr (NBUF == 3) {
-            if (kk == 0) issue_ops(std::integral_constant<int, PREV>{}, IA1{}, IB1{}, st2);
-            if (kk == 1) issue_ops(std::integral_constant<int, PREV>{}, IB1{}, IC1{}, st2);
+          for (int i = 0; i < RBT; ++i) fa[i] = *(const Frag*)(base + i * 32 * (BK * ES));
+        };
+        // block 0 of the tile: position l % 32, the same for every wave
+        auto read_rawt = [&](const char* rb, R& raw) {
+          const int pos = l & 31;
+          const char* hs = rb + W_BYTES + ((pos >> 4) * (32 * NQ) + hb * NQ * 16 + (pos & 15)) * 16;
+          if constexpr (MODE == TL_CACHE_H_INT4) {
+            raw.w[0] = *(const u32x4*)hs;
+            raw.s[0] = *(const uint32_t*)(rb + W_BYTES + H_BYTES + pos * 4);
+          } else {
+            raw.w[0][0] = *(const u32x4*)hs;
+            raw.w[0][1] = *(const u32x4*)(hs + 16 * 16);
           }
-          read_at(rb, kk + 1, na);
-          fbn = b_fragt(raw, kk + 1);
+        };
+        half_t s8t = (half_t)0.f;
+        if constexpr (MODE == TL_CACHE_H_INT8)
+          s8t = tmask ? h_from_bits(*cv.int8_scale(a.layer, lane, j0 + (l & 31))) : (half_t)0.f;
+        auto b_fragt = [&](const R& raw, int kk) -> half8 {
+          if constexpr (MODE == TL_CACHE_H_INT4) {
+            const uint32_t sv = tmask ? raw.s[0] : 0u;
+            const half_t sc = h_from_bits((uint16_t)(kk < 2 ? (sv & 0xFFFFu) : (sv >> 16)));
+            return int4_dequant8(raw.w[0][kk], sc);
+          } else {
+            const u32x4& w = raw.w[0][kk >> 1];
+            const half4 lo = int8_dequant4(w[(kk & 1) * 2], s8t);
+            const half4 hi = int8_dequant4(w[(kk & 1) * 2 + 1], s8t);
+            return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        };
+        // the copies go out and are waited for exactly as in `stage`
+        auto stage_t = [&](auto buf_c, int st, Frag (&ca)[RBT], half8& fbc, R& raw) {
+          constexpr int BUF = decltype(buf_c)::value;
+          constexpr int NXT = (BUF + 1) % NBUF, PREV = (BUF + NBUF - 1) % NBUF;
+          const char* rb = Ring<BUF, RING>::p();
+          const int st2 = min(st + 2, nst - 1);
+          Frag na[RBT];
+          half8 fbn;
+#pragma unroll
+          for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+            if constexpr (NBUF == 3) {
+              if (kk == 0) issue_ops(std::integral_constant<int, PREV>{}, IA1{}, IB1{}, st2);
+              if (kk == 1) issue_ops(std::integral_constant<int, PREV>{}, IB1{}, IC1{}, st2);
+            }
+            read_at(rb, kk + 1, na);
+            fbn = b_fragt(raw, kk + 1);
+            if (trows)
+#pragma unroll
+              for (int i = 0; i < RBT; ++i) acc[i][0] = Mma<T>::mma(ca[i], fbc, acc[i][0]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < RBT; ++i) ca[i] = na[i];
+            fbc = fbn;
+          }
+          if constexpr (NBUF == 3) {
+            dma_sync<DMA_PER_STAGE>();
+            issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IA1{}, min(st + 3, nst - 1));
+          } else {
+            dma_sync<0>();
+            issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IC1{}, min(st + 2, nst - 1));
+          }
+          read_rawt(Ring<NXT, RING>::p(), raw);
+          read_at(Ring<NXT, RING>::p(), 0, na);
+          fbn = b_fragt(raw, 0);
           if (trows)
 #pragma unroll
             for (int i = 0; i < RBT; ++i) acc[i][0] = Mma<T>::mma(ca[i], fbc, acc[i][0]);
@@ -808,67 +888,52 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
 #pragma unroll
           for (int i = 0; i < RBT; ++i) ca[i] = na[i];
           fbc = fbn;
-        }
-        if constexpr (NBUF == 3) {
-          dma_sync<DMA_PER_STAGE>();
-          issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IA1{}, min(st + 3, nst - 1));
-        } else {
+        };
+        {
+          Frag ca[RBT];
+          half8 fbc;
+          R raw;
+          read_rawt(Ring<0, RING>::p(), raw);
+          read_at(Ring<0, RING>::p(), 0, ca);
+          fbc = b_fragt(raw, 0);
+          int st = 0;
+          if constexpr (NBUF == 3) {
+            for (; st + 3 <= nst; st += 3) {
+              stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+              stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
+              stage_t(std::integral_constant<int, 2>{}, st + 2, ca, fbc, raw);
+            }
+            if (st < nst) stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+            if (st + 1 < nst) stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
+          } else {
+            for (; st + 2 <= nst; st += 2) {
+              stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+              stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
+            }
+            if (st < nst) stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+          }
           dma_sync<0>();
-          issue_ops(std::integral_constant<int, BUF>{}, IA0{}, IC1{}, min(st + 2, nst - 1));
         }
-        read_rawt(Ring<NXT, RING>::p(), raw);
-        read_at(Ring<NXT, RING>::p(), 0, na);
-        fbn = b_fragt(raw, 0);
-        if (trows)
+        // row blocks w*RBT .. w*RBT+RBT-1 of wave w -> wave 0, through ring
+        // buffer 0 (no copy is in flight any more): [row block][element][lane]
+        float* xch = (float*)Ring<0, RING>::p();
+        if (wave_u > 0 && trows) {
 #pragma unroll
-          for (int i = 0; i < RBT; ++i) acc[i][0] = Mma<T>::mma(ca[i], fbc, acc[i][0]);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int i = 0; i < RBT; ++i)
 #pragma unroll
-        for (int i = 0; i < RBT; ++i) ca[i] = na[i];
-        fbc = fbn;
-      };
-      {
-        Frag ca[RBT];
-        half8 fbc;
-        R raw;
-        read_rawt(Ring<0, RING>::p(), raw);
-        read_at(Ring<0, RING>::p(), 0, ca);
-        fbc = b_fragt(raw, 0);
-        int st = 0;
-        if constexpr (NBUF == 3) {
-          for (; st + 3 <= nst; st += 3) {
-            stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
-            stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
-            stage_t(std::integral_constant<int, 2>{}, st + 2, ca, fbc, raw);
-          }
-          if (st < nst) stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
-          if (st + 1 < nst) stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
-        } else {
-          for (; st + 2 <= nst; st += 2) {
-            stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
-            stage_t(std::integral_constant<int, 1>{}, st + 1, ca, fbc, raw);
-          }
-          if (st < nst) stage_t(std::integral_constant<int, 0>{}, st, ca, fbc, raw);
+            for (int e = 0; e < 16; ++e) xch[((wave_u * RBT + i) * 16 + e) * 64 + l] = acc[i][0][e];
         }
-        dma_sync<0>();
+        lds_sync();
+        if (wave_u == 0) {
+#pragma unroll
+          for (int i = RBT; i < RB; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][0][e] = xch[(i * 16 + e) * 64 + l];
+        }
+        __syncthreads();   // the exchange is read before the epilogue reuses LDS
+      } else {
+        dispatch_nb<CB>(ncb, loop);
       }
-      // row blocks w*RBT .. w*RBT+RBT-1 of wave w -> wave 0, through ring
-      // buffer 0 (no copy is in flight any more): [row block][element][lane]
-      float* xch = (float*)Ring<0, RING>::p();
-      if (wave_u > 0 && trows) {
-#pragma unroll
-        for (int i = 0; i < RBT; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) xch[((wave_u * RBT + i) * 16 + e) * 64 + l] = acc[i][0][e];
-      }
-      lds_sync();
-      if (wave_u == 0) {
-#pragma unroll
-        for (int i = RBT; i < RB; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][0][e] = xch[(i * 16 + e) * 64 + l];
-      }
-      __syncthreads();   // the exchange is read before the epilogue reuses LDS
     } else {
       dispatch_nb<CB>(ncb, loop);
     }
@@ -1098,20 +1163,21 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
                                     scratch + NT, scratch + NT + NT / DH);
     }
   };
-  if constexpr (B_REG) {
-    // Every wave holds all heads of the tile for its positions: each writes
-    // its (max, sum, o) per head to LDS (a wave with no position < T writes
-    // the neutral partial), and one partial per (row, head, tile) is formed by
-    // combining the waves in order w = 0, 1, ...
+  if constexpr (COPY) {
+    // Every wave holds whole heads (HPW of them, the workgroup's rows split
+    // over BF / WF feature waves) for its positions: each writes its (max,
+    // sum, o) per head to LDS (a wave with no position < T writes the neutral
+    // partial), and one partial per (row, head, tile) is formed by combining,
+    // in order, the WJN waves that hold the head (w = wf * WJN + 0, 1, ...).
     static_assert(!kCross, "copied-operand tiles hold whole heads");
-    static_assert(HPW == HG, "a wave covers the workgroup's heads");
+    static_assert(HPW * (BF / WF) == HG && WJN * (BF / WF) == NWV, "waves cover the workgroup's heads");
     float* comb = (float*)comb_lds;   // [NWV][HPW][DH + 2]
 #pragma unroll
     for (int g = 0; g < HPW; ++g) {
       float* dst = comb + (wave * HPW + g) * (DH + 2);
       if (wave_live) {
         float s[CB], m, lsum;
-        scores(g * 2 * KB, q_lds + g * DH, s);
+        scores(g * 2 * KB, q_lds + (wf * HPW + g) * DH, s);
         softmax(s, m, lsum);
         values(g * 2 * KB + KB, dst, s, m, lsum);
       } else {
@@ -1119,20 +1185,20 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
       }
     }
     lds_sync();
-    if (tid < HPW * DH) {
-      const int g = tid / DH, dim = tid % DH;
-      float M = comb[g * (DH + 2)];
+    if (tid < HG * DH) {
+      const int gg = tid / DH, dim = tid % DH, g = gg % HPW, w0 = (gg / HPW) * WJN;
+      float M = comb[(w0 * HPW + g) * (DH + 2)];
 #pragma unroll
-      for (int w = 1; w < NWV; ++w) M = fmaxf(M, comb[(w * HPW + g) * (DH + 2)]);
+      for (int w = 1; w < WJN; ++w) M = fmaxf(M, comb[((w0 + w) * HPW + g) * (DH + 2)]);
       float L = 0.f, O = 0.f;
 #pragma unroll
-      for (int w = 0; w < NWV; ++w) {
-        const float* c = comb + (w * HPW + g) * (DH + 2);
+      for (int w = 0; w < WJN; ++w) {
+        const float* c = comb + ((w0 + w) * HPW + g) * (DH + 2);
         const float e = c[0] == -__builtin_inff() ? 0.f : exp2f((c[0] - M) * kLog2e);
         L = fmaf(c[1], e, L);
         O = fmaf(c[2 + dim], e, O);
       }
-      store_partial(g, dim, M, L, O);
+      store_partial(gg, dim, M, L, O);
     }
     if (a.tilecnt) {
       static_assert(NWV * HPW_T * (DH + 2) >= NT + NT / DH + NT / 64, "merge scratch within comb_lds");
@@ -1221,7 +1287,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     // K rows live in wave wf = 0, V rows in wf = 1 (same positions): pass the
     // weights p through LDS.
     char* ex_base;
-    if constexpr (B_REG) ex_base = Ring<0, RING>::p();
+    if constexpr (COPY) ex_base = Ring<0, RING>::p();
     else ex_base = smem;
     float* ex = (float*)ex_base;            // [WJN][WJ] p, then [WJN][2] (m, l)
     const int head = hg;

@@ -125,3 +125,36 @@ def test_abort_mid_step_leaves_counters_clean(mode):
         assert st[lo] == 0 and e <= REL_TOL, (step, e)
         assert token_ok(int(t[lo]), r["logits"][lo])
         tok = int(t[lo])
+
+
+@pytest.mark.parametrize("mode", ["f16", "delta8"])
+def test_fp16_h_tiles_at_mixed_lengths(mode):
+    """fp16 h (and the delta mode's fp16 view) with enough rows and position
+    tiles for the regular configuration (8 waves, the W and h tiles copied
+    into the LDS ring): 4 lanes at contexts 2049, 2100, 2280 and 2304 (a last
+    tile of 1, 52 and 232 positions, and none), every lane against the oracle
+    over two steps."""
+    w, gm = gpu_model(S407)
+    L, seed = 3, 77
+    n_layers = S407.n_pre + L
+    ctxs = [2049, 2100, 2280, 2304]
+    c = gm.cache(mode, 4, 2312, L)
+    orc = oracle.LoopedOracle(S407, w, mode, 4, 2312, L)
+    for k, n in enumerate(ctxs):
+        for layer in range(n_layers):
+            c.tl_cache_fill_synthetic(k, layer, 0, n, seed)
+        c.tl_cache_set_length(k, n, n_layers)
+        orc.prime_synthetic(k, range(n_layers), n,
+                            lambda layer, k=k, n=n: synth.prior_h(seed, layer, k, np.arange(n), S407.d_model))
+    toks = [int(x) for x in synth.make_prompts(S407.vocab, 4, 1, 9)[:, 0]]
+    for step in range(2):
+        t, lg, st = decode(c, [0, 1, 2, 3], [L] * 4, toks)
+        r = orc.decode_step([0, 1, 2, 3], [L] * 4, toks)
+        for k in range(4):
+            assert st[k] == 0
+            e = rel_err(lg[k], r["logits"][k])
+            record("fp16_h_mixed_lengths", mode=mode, step=step, lane=k, rel=e)
+            assert e <= REL_TOL, (mode, step, k, e)
+            assert token_ok(int(t[k]), r["logits"][k]), (mode, step, k)
+            assert rel_err(c.tl_residual_norms(k)[:L], orc.norms[k][:L]) <= REL_TOL
+        toks = [int(x) for x in t]
