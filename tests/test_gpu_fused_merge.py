@@ -158,3 +158,33 @@ def test_fp16_h_tiles_at_mixed_lengths(mode):
             assert token_ok(int(t[k]), r["logits"][k]), (mode, step, k)
             assert rel_err(c.tl_residual_norms(k)[:L], orc.norms[k][:L]) <= REL_TOL
         toks = [int(x) for x in t]
+
+
+def test_fp16_h_many_short_lanes():
+    """fp16 h with many rows at short contexts, so the regular configuration
+    runs (rows x tiles x head groups fill the CUs) with every tile partial and
+    most waves holding no position: 32 lanes at contexts 1 .. 32 (decoding
+    at 2 .. 33, one or two tiles of 256), every lane against the oracle."""
+    w, gm = gpu_model(S407)
+    L, seed, lanes = 2, 91, 32
+    n_layers = S407.n_pre + L
+    c = gm.cache("f16", lanes, 40, L)
+    orc = oracle.LoopedOracle(S407, w, "f16", lanes, 40, L)
+    for k in range(lanes):
+        n = k + 1
+        for layer in range(n_layers):
+            c.tl_cache_fill_synthetic(k, layer, 0, n, seed)
+        c.tl_cache_set_length(k, n, n_layers)
+        orc.prime_synthetic(k, range(n_layers), n,
+                            lambda layer, k=k, n=n: synth.prior_h(seed, layer, k, np.arange(n), S407.d_model))
+    toks = [int(x) for x in synth.make_prompts(S407.vocab, lanes, 1, 5)[:, 0]]
+    for step in range(2):
+        t, lg, st = decode(c, list(range(lanes)), [L] * lanes, toks)
+        r = orc.decode_step(list(range(lanes)), [L] * lanes, toks)
+        for k in range(lanes):
+            assert st[k] == 0
+            e = rel_err(lg[k], r["logits"][k])
+            record("fp16_h_short_lanes", step=step, lane=k, rel=e)
+            assert e <= REL_TOL, (step, k, e)
+            assert token_ok(int(t[k]), r["logits"][k]), (step, k)
+        toks = [int(x) for x in t]
