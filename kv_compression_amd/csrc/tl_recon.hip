@@ -260,9 +260,8 @@ template <int CB> struct Raw<TL_CACHE_H_INT4, CB> {
 template <int CB> struct Raw<TL_CACHE_H_INT8, CB> {
   u32x4 w[CB][2];
 };
-// fp16 h read from the ring: the stage's buffer
+// fp16 h is read from the ring as the operand is needed: nothing to hold
 template <int CB> struct Raw<TL_CACHE_H_F16, CB> {
-  const char* rb;
 };
 
 #define TL_LDS __attribute__((address_space(3)))
@@ -600,7 +599,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     auto read_raw = [&](auto nb_c, const char* rb, R& raw) {
       constexpr int NB = decltype(nb_c)::value;
       if constexpr (H16C) {
-        raw.rb = rb;
+        (void)rb;
       } else {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -617,11 +616,20 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
       }
     };
     // MFMA operand of block j, k-step kk: 8 fp16 = fp16(q * s), or the fp16
-    // h fragment (chunk kk*2 + hb of the block's position row)
-    auto b_frag = [&](const R& raw, int j, int kk) -> half8 {
+    // h fragment (chunk kk*2 + hb of the block's position row) of ring
+    // buffer rb.
+    auto b_frag = [&](const R& raw, const char* rb, int j, int kk) -> half8 {
       if constexpr (H16C) {
-        const int pos = pos_local(j);
-        return *(const half8*)(raw.rb + W_BYTES + pos * (BK * ES) + (((kk * 2 + hb) ^ w_swz(pos)) * 16));
+        const uint32_t pos = (uint32_t)pos_local(j);
+        uint32_t off = W_BYTES + pos * (BK * ES) + (((uint32_t)(kk * 2 + hb) ^ (uint32_t)w_swz(pos)) << 4);
+        // The address is kept one offset away from the ring's LDS array (the
+        // empty asm stops the offset being split into a chain of steps): the
+        // compiler tells which copies in flight a read may depend on only by
+        // tracing its address back to the array within a few steps, and
+        // otherwise waits for all of them (here: the next stage's copies, at
+        // every stage).
+        __asm__("" : "+v"(off));
+        return *(const half8*)(rb + off);
       } else if constexpr (MODE == TL_CACHE_H_INT4) {
         const uint32_t sv = ((vmask >> j) & 1) ? raw.s[j] : 0u;   // positions past T: scale 0
         const half_t sc = h_from_bits((uint16_t)(kk < 2 ? (sv & 0xFFFFu) : (sv >> 16)));
@@ -677,7 +685,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
         if constexpr (NB > 0) {
           read_a3(rb, kk + 1, na);
 #pragma unroll
-          for (int j = 0; j < NB; ++j) fbn[j] = b_frag(raw, j, kk + 1);
+          for (int j = 0; j < NB; ++j) fbn[j] = b_frag(raw, rb, j, kk + 1);
           mfmas(ca, fbc);
           if constexpr (H16C) {
             // RB * NB MFMAs and RB + NB fragment reads
@@ -717,7 +725,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
         read_raw(nb_c, Ring<NXT, RING>::p(), raw);
         read_a3(Ring<NXT, RING>::p(), 0, na);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) fbn[j] = b_frag(raw, j, 0);
+        for (int j = 0; j < NB; ++j) fbn[j] = b_frag(raw, Ring<NXT, RING>::p(), j, 0);
         mfmas(ca, fbc);
         // copies first (they follow no read of this wave), then the code and
         // fragment reads, then the dequantisation
@@ -779,7 +787,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
         read_raw(nb_c, Ring<0, RING>::p(), raw);
         read_a3(Ring<0, RING>::p(), 0, ca);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) fbc[j] = b_frag(raw, j, 0);
+        for (int j = 0; j < NB; ++j) fbc[j] = b_frag(raw, Ring<0, RING>::p(), j, 0);
       }
       int st = 0;
       if constexpr (NBUF == 3) {
