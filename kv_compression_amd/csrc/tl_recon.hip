@@ -65,9 +65,11 @@ template <> struct Cfg<half_t, TL_CACHE_H_F16, 64, 1> {
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
   static constexpr bool COPY16 = false;
 };
-// ... and with 128-position tiles when even that leaves CUs idle
+// ... and with 128-position tiles, four waves of 32 positions, when even that
+// leaves CUs idle (all four SIMDs of a CU busy: 19.8 against 24.4 us for two
+// waves of 64 at one lane and context 1030-1150)
 template <> struct Cfg<half_t, TL_CACHE_H_F16, 64, 2> {
-  static constexpr int BF = 128, BJ = 128, WF = 128, WJ = 64, BK = 64, OCC = 1, NBUF = 3;
+  static constexpr int BF = 128, BJ = 128, WF = 128, WJ = 32, BK = 64, OCC = 1, NBUF = 3;
   static constexpr int NT = 64 * (BF / WF) * (BJ / WJ);
   static constexpr bool COPY16 = false;
 };
@@ -105,10 +107,10 @@ template <int MODE, int DH> struct Cfg<float, MODE, DH> {
   static constexpr bool COPY16 = false;
 };
 // the fp16 configurations other than INT4 at 64-wide heads share BJ and WJ
-// (split length)
+// (split length); the one-head fp16 ones run only with the tile merge in the
+// launch, whose partials are per tile
 static_assert(Cfg<half_t, TL_CACHE_H_INT4, 128>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
               Cfg<half_t, TL_CACHE_H_F16, 64, 1>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
-              Cfg<half_t, TL_CACHE_H_F16, 64, 2>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ &&
               Cfg<half_t, TL_CACHE_H_INT8, 64>::BJ == Cfg<half_t, TL_CACHE_H_F16, 64>::BJ &&
               Cfg<half_t, TL_CACHE_H_INT4, 64>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ &&
               Cfg<half_t, TL_CACHE_H_INT8, 64>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ, "fp16 tiles");
@@ -241,11 +243,13 @@ __device__ __forceinline__ void dispatch_nb(int n, F&& f) {
     else if (n == 2) f(std::integral_constant<int, 2>{});
     else if (n == 1) f(std::integral_constant<int, 1>{});
     else f(std::integral_constant<int, 0>{});
-  } else {
-    static_assert(CB == 2, "2 or 4 position blocks per wave");
-    (void)0;
+  } else if constexpr (CB == 2) {
     if (n >= 2) f(std::integral_constant<int, 2>{});
     else if (n == 1) f(std::integral_constant<int, 1>{});
+    else f(std::integral_constant<int, 0>{});
+  } else {
+    static_assert(CB == 1, "1, 2 or 4 position blocks per wave");
+    if (n >= 1) f(std::integral_constant<int, 1>{});
     else f(std::integral_constant<int, 0>{});
   }
 }
@@ -1394,7 +1398,7 @@ hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t
   // would leave CUs without a workgroup (128-position tiles when 256-position
   // ones still would)
   int var = 0;
-  if (m.dtype == TL_DTYPE_F16 && r.cache.mode == TL_CACHE_H_F16 && m.dh == 64) {
+  if (m.dtype == TL_DTYPE_F16 && r.cache.mode == TL_CACHE_H_F16 && m.dh == 64 && r.tilecnt) {
     auto wgs = [&](int v) {
       const int bj = recon_bj(m, r.cache.mode, v);
       return (long)((r.t_ub + bj - 1) / bj) * r.n_rows * (2 * m.D / recon_bf(m, r.cache.mode, v));
