@@ -11,13 +11,16 @@
 // down the MFMA rows and positions along its columns, so each lane ends up
 // holding whole positions.
 //   * INT4 / INT8 h: the W tile, the h codes and the INT4 scales of a stage
-//     are copied by the memory unit straight into a three-buffer LDS ring
-//     (buffer loads to LDS); each of four waves owns all the tile's features
-//     for 64 positions and dequantises its codes in registers into the B
-//     operand, fp16(q * s) exactly, one k-step ahead of the MFMAs.
-//   * fp16 / fp32 h: both operands go through registers into a two-buffer
-//     LDS tile, one stage ahead; waves are laid out over features and
-//     positions.
+//     are copied by the memory unit straight into an LDS ring of two or
+//     three stage buffers (buffer loads to LDS); each of four waves owns all
+//     the tile's features for 64 positions and dequantises its codes in
+//     registers into the B operand, fp16(q * s) exactly, one k-step ahead of
+//     the MFMAs.
+//   * fp16 h at 64-wide heads: the W and h tiles are copied into the ring
+//     the same way and the h fragments are read from it as the B operand.
+//   * other fp16 configurations and fp32 h: both operands go through
+//     registers into a two-buffer LDS tile, one stage ahead; waves are laid
+//     out over features and positions.
 // The decode epilogue reads the scores q . K_j out of the accumulators,
 // applies a wave-level online softmax and reduces p_j V_j across lanes into
 // (max, sum, o) per (row, head, position tile); the last workgroup to finish
