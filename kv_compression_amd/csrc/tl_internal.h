@@ -251,8 +251,6 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const ModelView& m, const GemmArgs& g, hipStream_t s);
 
-// Decode attention over the store-h cache: rebuild K|V of every position with
-// MFMA and fold them into per-split online-softmax partials.
 // Timing of one kernel: events that take that launch's own start and end
 // timestamps (hipExtLaunchKernel), so the time between them is the kernel's
 // execution without the launch gaps around it. Null: not timed.
@@ -266,6 +264,8 @@ hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, const La
   return hipGetLastError();
 }
 
+// Decode attention over the store-h cache: rebuild K|V of every position with
+// MFMA and fold them into per-split online-softmax partials.
 struct ReconArgs {
   CacheView cache;
   int layer;
