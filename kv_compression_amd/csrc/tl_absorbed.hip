@@ -32,7 +32,9 @@ constexpr int kAbsTP = 32;    // positions per tile of the attention kernel
 // registers (all loads in flight together) and sums them against each row's
 // q, staged 64 rows at a time in LDS. The sum runs over j in order. The
 // result is written in the attention kernel's operand order (16 heads): per
-// row 4 waves x D / 128 k-steps x 64 lanes x (8 high, 8 low) halves.
+// row 4 waves x D / 128 k-steps x 64 lanes x (8 high, 8 low) halves, which
+// is also the order of 8 waves x D / 256 k-steps (the k-steps of wave w of 8
+// are k-steps 4 (w % 2) .. of wave w / 2 of 4).
 template <int DH>
 __global__ __launch_bounds__(64) void absorb_q_kernel(int D, int n_rows, const float* q,
                                                       const half_t* wk, float* qt) {
@@ -131,14 +133,16 @@ struct AbsArgs {
   int S, split_len;
 };
 
-// One workgroup per (row, key split), 4 waves; wave w owns d_model columns
-// w D / 4 .. (w + 1) D / 4 - 1 (D = 1024 or 2048) of both products. Per tile of 32 positions:
+// One workgroup per (row, key split) of NW waves (8 at D = 1024, two per
+// SIMD, so one wave's LDS and memory waits run under the other's MFMAs; 4 at
+// D = 2048, whose staged tile and sums leave room for no more); wave w owns
+// d_model columns w D / NW .. (w + 1) D / NW - 1 of both products. Per tile of 32 positions:
 //   S^T[pos][head] = h'[pos][:] . qt[head][:] on v_mfma_f32_16x16x32_f16, in
 //     two blocks of 16 positions: row m of block b is position
 //     8 (m / 4) + 4 b + m % 4, so that lane l's accumulators hold positions
 //     8 (l / 16) + j (j = 4 b + i) of head l % 16. A = h' rows from LDS; B =
 //     qt held in registers as fp16 high and low halves (fp32 accuracy). The
-//     four waves' partial sums over their columns are added in LDS in wave
+//     waves' partial sums over their columns are added in LDS in wave
 //     order;
 //   online softmax per head;
 //   R[head][d] += P[head][pos] h'[pos][d]: the lane's eight weights are exactly
@@ -149,12 +153,13 @@ struct AbsArgs {
 // sum's strided B reads (rows 8 (l / 16) + j) on distinct banks, the block
 // padding the staging writes (one block per lane), and every 8-element run
 // stays 16-byte aligned.
-template <int MODE, int D>
-__global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
-  constexpr int H = 16, TP = 32, BS = 72, LDR = D / 64 * BS + 32, WC = D / 4, KS = WC / 32, NB = WC / 16;
-  static_assert(D == 1024 || D == 2048, "a quarter of d_model per wave");
+template <int MODE, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void absorbed_attn_kernel(AbsArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int H = 16, TP = 32, BS = 72, LDR = D / 64 * BS + 32, WC = D / NW, KS = WC / 32, NB = WC / 16;
+  static_assert((D == 1024 || D == 2048) && (NW == 4 || NW == 8), "d_model / NW columns per wave");
   __shared__ __attribute__((aligned(16))) half_t hs[TP * LDR];
-  __shared__ float sp[4][512];
+  __shared__ float sp[NW][512];
   auto row_of = [](int p) { return p * LDR + 8 * ((p >> 3) & 3); };
   auto col_of = [](int k) { return (k >> 6) * BS + (k & 63); };
   const int row = blockIdx.x / a.S, split = blockIdx.x % a.S;
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
   // stored in this order by absorb_q_kernel (one contiguous 32 bytes per lane)
   half8 qh[KS], ql[KS];
   {
-    const half8* qp = (const half8*)a.qt + (((size_t)row * 4 + w) * KS * 64 + l) * 2;
+    const half8* qp = (const half8*)a.qt + (((size_t)row * NW + w) * KS * 64 + l) * 2;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       qh[s] = qp[s * 128];
@@ -181,13 +186,16 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
   for (int n = 0; n < NB; ++n) R[n] = float4v{0.f, 0.f, 0.f, 0.f};
   float mx = -__builtin_inff(), lsum = 0.f;   // head lq
   // staging: thread t dequantises blocks t % 16 + 16 b (b < D / 1024) of
-  // positions t / 16 and t / 16 + 16; staged block s is position
-  // spos + 16 (s % 2), block skb + 16 (s / 2)
-  constexpr int NS = 2 * (D / 1024);
+  // positions t / 16 + PPP i (i < NPP: PPP = NT / 16 positions per pass);
+  // staged block s is position spos + PPP (s % NPP), block skb + 16 (s / NPP)
+  constexpr int PPP = NT / 16, NPP = TP / PPP;
+  constexpr int NS = NPP * (D / 1024);
   const int spos = t >> 4, skb = t & 15;
+  auto s_pos = [&](int q) { return PPP * (q % NPP) + spos; };
+  auto s_blk = [&](int q) { return skb + 16 * (q / NPP); };
   half_t* sdst[NS];
 #pragma unroll
-  for (int q = 0; q < NS; ++q) sdst[q] = hs + row_of(spos + 16 * (q & 1)) + (skb + 16 * (q >> 1)) * BS;
+  for (int q = 0; q < NS; ++q) sdst[q] = hs + row_of(s_pos(q)) + s_blk(q) * BS;
   // the thread's blocks of the next PF tiles are loaded while the current
   // one is multiplied (positions past p_hi are clamped in and staged as zeros)
   // (at D = 2048 the INT8 and fp16 blocks are loaded right before they are
@@ -200,8 +208,7 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
     for (int u = 0; u < PF; ++u)
 #pragma unroll
       for (int q = 0; q < NS; ++q)
-        ring[u][q] = load_block<MODE>(a.cache, a.layer, lane, skb + 16 * (q >> 1),
-                                      min(p_lo + u * TP + 16 * (q & 1) + spos, p_hi - 1));
+        ring[u][q] = load_block<MODE>(a.cache, a.layer, lane, s_blk(q), min(p_lo + u * TP + s_pos(q), p_hi - 1));
   }
   for (int pr = p_lo; pr < p_hi; pr += PF * TP) {
 #pragma unroll
@@ -212,9 +219,8 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
       __syncthreads();   // the previous tile is no longer read
 #pragma unroll
       for (int q = 0; q < NS; ++q) {
-        const BlockRaw<MODE> b1 = load_block<MODE>(a.cache, a.layer, lane, skb + 16 * (q >> 1),
-                                                   min(p0 + 16 * (q & 1) + spos, p_hi - 1));
-        store_block<MODE>(b1, p0 + 16 * (q & 1) + spos < p_hi, sdst[q]);
+        const BlockRaw<MODE> b1 = load_block<MODE>(a.cache, a.layer, lane, s_blk(q), min(p0 + s_pos(q), p_hi - 1));
+        store_block<MODE>(b1, p0 + s_pos(q) < p_hi, sdst[q]);
       }
     } else {
       BlockRaw<MODE> cur[NS];
@@ -223,12 +229,11 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
       if (p0 + PF * TP < p_hi) {
 #pragma unroll
         for (int q = 0; q < NS; ++q)
-          ring[u][q] = load_block<MODE>(a.cache, a.layer, lane, skb + 16 * (q >> 1),
-                                        min(p0 + PF * TP + 16 * (q & 1) + spos, p_hi - 1));
+          ring[u][q] = load_block<MODE>(a.cache, a.layer, lane, s_blk(q), min(p0 + PF * TP + s_pos(q), p_hi - 1));
       }
       __syncthreads();   // the previous tile is no longer read
 #pragma unroll
-      for (int q = 0; q < NS; ++q) store_block<MODE>(cur[q], p0 + 16 * (q & 1) + spos < p_hi, sdst[q]);
+      for (int q = 0; q < NS; ++q) store_block<MODE>(cur[q], p0 + s_pos(q) < p_hi, sdst[q]);
     }
     __syncthreads();
     // partial scores over this wave's columns: block b in two chains
@@ -258,11 +263,13 @@ __global__ __launch_bounds__(256) void absorbed_attn_kernel(AbsArgs a) {
     float sc[8];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const float4v s0 = *(const float4v*)&sp[0][256 * b + 4 * l], s1 = *(const float4v*)&sp[1][256 * b + 4 * l];
-      const float4v s2 = *(const float4v*)&sp[2][256 * b + 4 * l], s3 = *(const float4v*)&sp[3][256 * b + 4 * l];
+      // the waves' column sums added in wave order
+      float4v sv = *(const float4v*)&sp[0][256 * b + 4 * l];
+#pragma unroll
+      for (int u = 1; u < NW; ++u) sv += *(const float4v*)&sp[u][256 * b + 4 * l];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = ((s0[i] + s1[i]) + s2[i]) + s3[i];
+        float v = sv[i];
         if (p0 + 8 * lg + 4 * b + i >= p_hi) v = -__builtin_inff();
         sc[4 * b + i] = v;
       }
@@ -428,21 +435,24 @@ bool absorbed_supported(const ModelView& m, int view_mode) {
 }
 
 int absorbed_splits(int n_rows, int t_ub, int pair_cap, int* split_len) {
-  // about 512 workgroups, at least 64 positions a split, the partials within
-  // their buffer; rows long enough that one workgroup per CU still gives every
-  // split 512 positions or more take that (each split writes H x D partial
-  // floats, and at that length fewer, longer splits measure faster: 8 rows of
-  // 33000 positions at d_model 2048 3.39 against 3.60 ms a step, while 48
-  // rows of 2048 positions keep 512 workgroups, 3.04 against 3.19 ms)
-  int S = (512 + n_rows - 1) / n_rows;
-  const int S1 = (256 + n_rows - 1) / n_rows;
-  if ((t_ub + S1 - 1) / S1 >= 512) S = S1;
-  S = std::min(S, std::max(1, (t_ub + 63) / 64));
-  S = std::min(S, std::max(1, pair_cap / n_rows));
-  int len = (t_ub + S - 1) / S;
-  len = (len + kAbsTP - 1) / kAbsTP * kAbsTP;
-  *split_len = len;
-  return (t_ub + len - 1) / len;
+  // The staged tile takes more than half of a CU's LDS, so one workgroup runs
+  // per CU: the splits of all rows are sized to fit one dispatch round of
+  // kCUs workgroups, each covering a whole number of 32-position tiles, at
+  // least two (a split pays a fixed cost: its qt operands and an H x D
+  // partial). Splits of 64 positions at four rows of ~4100 (the rule that
+  // aimed at two rounds of two-per-CU workgroups) made 260 workgroups, two
+  // rounds of one per CU.
+  const int tiles = (t_ub + kAbsTP - 1) / kAbsTP;
+  const int per_row = std::max(1, kCUs / n_rows);
+  int tps = std::max(2, (tiles + per_row - 1) / per_row);
+  int S = (tiles + tps - 1) / tps;
+  const int cap = std::max(1, pair_cap / n_rows);
+  if (S > cap) {
+    tps = (tiles + cap - 1) / cap;
+    S = (tiles + tps - 1) / tps;
+  }
+  *split_len = tps * kAbsTP;
+  return std::max(1, (t_ub + *split_len - 1) / *split_len);
 }
 
 hipError_t launch_absorb_q(const ModelView& m, int n_rows, const float* q, const void* w_qkv,
@@ -467,9 +477,10 @@ hipError_t launch_absorbed_attn(const ModelView& m, const CacheView& c, int laye
   const int grid = n_rows * S;
 #define TL_ABS(D_)                                                                              \
   do {                                                                                          \
-    if (c.mode == TL_CACHE_H_INT4) return launch_timed(absorbed_attn_kernel<TL_CACHE_H_INT4, D_>, grid, 256, s, ev, a); \
-    if (c.mode == TL_CACHE_H_INT8) return launch_timed(absorbed_attn_kernel<TL_CACHE_H_INT8, D_>, grid, 256, s, ev, a); \
-    return launch_timed(absorbed_attn_kernel<TL_CACHE_H_F16, D_>, grid, 256, s, ev, a);          \
+    constexpr int NW_ = D_ == 1024 ? 8 : 4;                                                    \
+    if (c.mode == TL_CACHE_H_INT4) return launch_timed(absorbed_attn_kernel<TL_CACHE_H_INT4, D_, NW_>, grid, NW_ * 64, s, ev, a); \
+    if (c.mode == TL_CACHE_H_INT8) return launch_timed(absorbed_attn_kernel<TL_CACHE_H_INT8, D_, NW_>, grid, NW_ * 64, s, ev, a); \
+    return launch_timed(absorbed_attn_kernel<TL_CACHE_H_F16, D_, NW_>, grid, NW_ * 64, s, ev, a);          \
   } while (0)
   if (m.D == 1024) TL_ABS(1024);
   else TL_ABS(2048);
