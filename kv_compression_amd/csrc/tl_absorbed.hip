@@ -439,9 +439,8 @@ int absorbed_splits(int n_rows, int t_ub, int pair_cap, int* split_len) {
   // per CU: the splits of all rows are sized to fit one dispatch round of
   // kCUs workgroups, each covering a whole number of 32-position tiles, at
   // least two (a split pays a fixed cost: its qt operands and an H x D
-  // partial). Splits of 64 positions at four rows of ~4100 (the rule that
-  // aimed at two rounds of two-per-CU workgroups) made 260 workgroups, two
-  // rounds of one per CU.
+  // partial). (A rule aiming at about 512 workgroups gave 528, three rounds,
+  // for 48 rows of 2049 positions.)
   const int tiles = (t_ub + kAbsTP - 1) / kAbsTP;
   const int per_row = std::max(1, kCUs / n_rows);
   int tps = std::max(2, (tiles + per_row - 1) / per_row);
