@@ -162,16 +162,17 @@ __global__ __launch_bounds__(NW * 64) void absorbed_attn_kernel(AbsArgs a) {
   __shared__ float sp[NW][512];
   auto row_of = [](int p) { return p * LDR + 8 * ((p >> 3) & 3); };
   auto col_of = [](int k) { return (k >> 6) * BS + (k & 63); };
+  // the kernel arguments the prologue uses, fetched in one batch at the start
+  __asm__ volatile("" ::"s"(a.cache.base), "s"(a.cache.scales), "s"(a.cache.mode), "s"(a.cache.max_seq),
+                   "s"(a.cache.n_lanes), "s"(a.layer), "s"(a.row_lane), "s"(a.row_pos), "s"(a.status),
+                   "s"(a.qt), "s"(a.S), "s"(a.split_len));
   const int row = blockIdx.x / a.S, split = blockIdx.x % a.S;
-  const int lane = a.row_lane[row];
-  if (a.status[lane] == TL_LANE_ABORTED || a.row_pos[row] < 0) return;
-  const int T = a.row_pos[row] + 1;
-  const int p_lo = split * a.split_len, p_hi = min(T, p_lo + a.split_len);
-  if (p_lo >= p_hi) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lq = l & 15, lg = l >> 4;
   const int c0 = w * WC;
   // qt as B operand: k-step s holds columns c0 + 32 s + 8 lg + j of head lq,
-  // stored in this order by absorb_q_kernel (one contiguous 32 bytes per lane)
+  // stored in this order by absorb_q_kernel (one contiguous 32 bytes per lane);
+  // its loads (they depend on the row only) go out with the row's lookups,
+  // and the lane's status is read once the first tiles' loads are in flight
   half8 qh[KS], ql[KS];
   {
     const half8* qp = (const half8*)a.qt + (((size_t)row * NW + w) * KS * 64 + l) * 2;
@@ -181,6 +182,13 @@ __global__ __launch_bounds__(NW * 64) void absorbed_attn_kernel(AbsArgs a) {
       ql[s] = qp[s * 128 + 1];
     }
   }
+  const int lane = a.row_lane[row];
+  const int rpos = a.row_pos[row];
+  __asm__ volatile("" ::"s"(lane), "s"(rpos));   // both lookups in flight together
+  if (rpos < 0) return;
+  const int T = rpos + 1;
+  const int p_lo = split * a.split_len, p_hi = min(T, p_lo + a.split_len);
+  if (p_lo >= p_hi) return;
   float4v R[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) R[n] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -210,6 +218,7 @@ __global__ __launch_bounds__(NW * 64) void absorbed_attn_kernel(AbsArgs a) {
       for (int q = 0; q < NS; ++q)
         ring[u][q] = load_block<MODE>(a.cache, a.layer, lane, s_blk(q), min(p_lo + u * TP + s_pos(q), p_hi - 1));
   }
+  if (a.status[lane] == TL_LANE_ABORTED) return;   // (loads into registers only so far)
   for (int pr = p_lo; pr < p_hi; pr += PF * TP) {
 #pragma unroll
   for (int u = 0; u < PF; ++u) {

@@ -351,6 +351,13 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
   const int wf = wave / WJN, wj = wave % WJN;
   const int D = a.D;
 
+  // the kernel arguments the prologue uses, fetched in one batch at the start
+  // (otherwise each is loaded where it is first needed, one scalar round trip
+  // after another ahead of the first copy)
+  __asm__ volatile("" ::"s"(a.cache.base), "s"(a.cache.scales), "s"(a.cache.mode), "s"(a.cache.max_seq),
+                   "s"(a.cache.n_lanes),
+                   "s"(a.layer), "s"(a.w_qkv), "s"(a.D), "s"(a.n_hg), "s"(a.hpx), "s"(a.n_rows),
+                   "s"(a.n_ptiles), "s"(a.row_lane), "s"(a.row_pos), "s"(a.status), "s"(a.q));
   int hg, ptile, r = 0, lane, Tn;
   if (EPI == EPI_ATTN) {
     // head group fastest (consecutive workgroups land on different XCDs, each
@@ -368,9 +375,15 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     r = tile % a.n_rows;
     ptile = tile / a.n_rows;
     if (ptile >= a.n_ptiles) return;
+    // the row's lane and length load together; with the copied operands the
+    // lane's status is read after the first stages' copies have gone out (a
+    // stopped lane's workgroup then waits for them and leaves), so the
+    // prologue takes two dependent lookups instead of three
     lane = a.row_lane[r];
-    if (a.status[lane] == TL_LANE_ABORTED) return;
     Tn = a.row_pos[r] + 1;
+    __asm__ volatile("" ::"s"(lane), "s"(Tn));   // both loads in flight together
+    if constexpr (!COPY)
+      if (a.status[lane] == TL_LANE_ABORTED) return;
   } else {
     hg = blockIdx.x % a.n_hg;
     ptile = blockIdx.x / a.n_hg;
@@ -777,8 +790,16 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     // issue order, so the queries, issued first, have arrived too)
     issue(std::integral_constant<int, 0>{}, 0);
     issue(std::integral_constant<int, 1>{}, min(1, nst - 1));
-    if constexpr (NBUF == 3) {
+    if constexpr (NBUF == 3)
       issue_ops(std::integral_constant<int, 2>{}, IA0{}, IA1{}, min(2, nst - 1));   // parts B, C: stage 0
+    if constexpr (EPI == EPI_ATTN) {
+      // (uniform over the workgroup: every wave leaves, after its copies have landed)
+      if (a.status[lane] == TL_LANE_ABORTED) {
+        dma_sync<0>();
+        return;
+      }
+    }
+    if constexpr (NBUF == 3) {
       dma_sync<DMA_PER_STAGE + PA>();
     } else {
       dma_sync<DMA_PER_STAGE>();
