@@ -31,14 +31,18 @@ def _nan_weights():
     return w
 
 
-@pytest.mark.parametrize("mode", ["int4", "f16", "kv"])
-def test_nan_residual_aborts_lane(mode):
+@pytest.mark.parametrize("mode,order", [("int4", "explicit"), ("f16", "explicit"), ("kv", "explicit"),
+                                        ("int4", "absorbed")])
+def test_nan_residual_aborts_lane(mode, order):
     torch = torch_gpu()
     w = _nan_weights()
     gm = GpuModel(S407, w)
     L = 3
     prompts = synth.make_prompts(S407.vocab, 2, 260, 31)
     c = gm.cache(mode, 2, 300, L)
+    if order != "explicit":
+        # the stopped lane's rows leave the absorbed kernels early, its batch mate is unaffected
+        c.tl_cache_set_attention(order)
     o = oracle.LoopedOracle(S407, w, mode, 2, 300, L)
     first = []
     for k in range(2):
