@@ -606,6 +606,48 @@ def measure_hbm_read(mib=(10, 64, 256, 1024)):
     return res
 
 
+def measure_mfma_reference(torch, shape):
+    """The MFMA-rate reference (kv_compression_amd/probe/mfma_rate, built with
+    the library): the fp16 rate this GPU's matrix cores sustain on MFMAs alone,
+    at two workgroups of four waves per CU, and the shader clock the waves
+    count; beside it the vendor fp16 GEMM (torch.matmul) on the decode
+    reconstruction's product shape (4 lanes x [2D x D] x [D x 4096]) and on
+    8192^3. A child process for the probe."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kv_compression_amd", "probe", "mfma_rate")
+    if not os.path.exists(exe):
+        raise RuntimeError("%s is missing: build the package first" % exe)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        raise RuntimeError("mfma_rate failed: " + r.stderr[-2000:])
+    probe = [json.loads(line) for line in r.stdout.splitlines() if line.startswith("{")][-1]
+
+    def gemm(a_shape, b_shape, reps=10):
+        g = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn(*a_shape, dtype=torch.float16, device="cuda", generator=g)
+        b = torch.randn(*b_shape, dtype=torch.float16, device="cuda", generator=g).contiguous()
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = 2.0 * a.numel() * b_shape[-1]
+        return round(flops / (ms * 1e-3) / 1e12, 1)
+
+    D = shape.d_model
+    out = {"probe": probe, "probe_frac_of_peak": round(probe["tflops"] / PEAK_FP16_TFLOPS, 4),
+           "vendor_gemm_recon_shape_tflops": gemm((4, 2 * D, D), (4, D, 4096)),
+           "vendor_gemm_8192_tflops": gemm((8192, 8192), (8192, 8192))}
+    log("mfma reference: probe %.0f TFLOP/s at %.2f GHz; vendor fp16 GEMM %.0f (recon shape), %.0f (8192^3) TFLOP/s"
+        % (probe["tflops"], probe["shader_ghz"], out["vendor_gemm_recon_shape_tflops"], out["vendor_gemm_8192_tflops"]))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -619,7 +661,8 @@ def main():
     ap.add_argument("--no-profile-pass", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="measure only --mode (skip the workload's other cache modes)")
-    ap.add_argument("--leg", choices=["laware_2b", "long_context_2b", "tiny_f32", "f16h_ctx1024", "hbm_read"],
+    ap.add_argument("--leg", choices=["laware_2b", "long_context_2b", "tiny_f32", "f16h_ctx1024", "hbm_read",
+                                      "mfma_rate"],
                     help="run only this 2B measurement and print its JSON object (for profiling it)")
     ap.add_argument("--leg-orders", default="both", choices=["both", "explicit"],
                     help="attention orders a 2B leg decodes in (explicit: the reconstruction kernel alone)")
@@ -644,6 +687,8 @@ def main():
               "f16h_ctx1024": measure_f16h_ctx1024}.get(args.leg)
         if args.leg == "hbm_read":
             res = measure_hbm_read((8, 10, 16, 32, 64, 128, 256, 512, 1024))
+        elif args.leg == "mfma_rate":
+            res = measure_mfma_reference(torch, synth.workload(args.workload).shape)
         elif args.leg in ("laware_2b", "long_context_2b") and args.leg_orders == "explicit":
             res = fn(torch, tl, orders=("explicit",))
         else:
@@ -729,9 +774,11 @@ def main():
     # what a kernel that only streams cold data reaches at the HBM-bound
     # kernels' sizes (the stored-K/V and absorbed attention launches move
     # about 64 and 10 MiB at this workload)
-    hbm_ref = None
+    hbm_ref = mfma_ref = None
     if not args.headline_only:
         hbm_ref = measure_hbm_read()
+        # what MFMAs alone sustain on this GPU, and the vendor GEMM beside them
+        mfma_ref = measure_mfma_reference(torch, shape)
         if "kv" in modes and modes["kv"]["roofline"]:
             ref = min(hbm_ref, key=lambda x: abs(x["bytes"] - 64 * 2 ** 20))
             modes["kv"]["vs_stream_read"] = round(modes["kv"]["roofline"]["achieved"] / ref["GBs_back_to_back"], 3)
@@ -775,6 +822,7 @@ def main():
         "warm_start": resume,
         "speculative": spec,
         "hbm_read_reference": hbm_ref,
+        "mfma_reference": mfma_ref,
     }
     print(json.dumps(out), flush=True)
 

@@ -1,8 +1,9 @@
 """Build libtl.so (the HIP library behind include/tl.h) for gfx950, in-tree.
 
 Each .hip source under csrc/ is compiled to an object with hipcc in parallel,
-then linked into kv_compression_amd/libtl.so; probe/hbm_read.hip, the
-streaming-read reference program, is built beside it as probe/hbm_read.
+then linked into kv_compression_amd/libtl.so; probe/hbm_read.hip and
+probe/mfma_rate.hip, the streaming-read and MFMA-rate reference programs, are
+built beside it as probe/hbm_read and probe/mfma_rate.
 Run: python -m kv_compression_amd.build
 """
 from __future__ import annotations
@@ -18,9 +19,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtl.so")
-# the streaming-read reference program (no part of the library)
-PROBE_SRC = os.path.join(HERE, "probe", "hbm_read.hip")
-PROBE = os.path.join(HERE, "probe", "hbm_read")
+# the streaming-read and MFMA-rate reference programs (no part of the library)
+PROBES = [(os.path.join(HERE, "probe", name + ".hip"), os.path.join(HERE, "probe", name))
+          for name in ("hbm_read", "mfma_rate")]
 ARCH = os.environ.get("TL_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -61,13 +62,14 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr[-4000:])
     os.replace(tmp, LIB)
-    ptmp = PROBE + ".tmp"
-    r = subprocess.run([HIPCC, *CFLAGS, "-o", ptmp, PROBE_SRC], capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed for %s:\n%s" % (PROBE_SRC, r.stderr[-4000:]))
-    os.replace(ptmp, PROBE)
+    for src, exe in PROBES:
+        ptmp = exe + ".tmp"
+        r = subprocess.run([HIPCC, *CFLAGS, "-o", ptmp, src], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr[-4000:]))
+        os.replace(ptmp, exe)
     if verbose:
-        print("built", LIB, "from", len(srcs), "sources, and", PROBE)
+        print("built", LIB, "from", len(srcs), "sources, and", ", ".join(exe for _, exe in PROBES))
     return LIB
 
 
