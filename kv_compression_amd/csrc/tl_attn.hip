@@ -57,9 +57,11 @@ __global__ __launch_bounds__(NT) void kv_attn_kernel(ModelView m, ReconArgs a, i
   typedef T vec_t __attribute__((ext_vector_type(EPT)));
   __shared__ float comb[PPS][TPR][EPT + 2];
   const int r = blockIdx.x / n_splits, split = blockIdx.x % n_splits;
+  // the row's lane and length load together; the lane's status is read once
+  // the split's loads (into registers) are in flight
   const int lane = a.row_lane[r];
-  if (a.status[lane] == TL_LANE_ABORTED) return;
   const int Tn = a.row_pos[r] + 1;
+  __asm__ volatile("" ::"s"(lane), "s"(Tn));
   const int j0 = split * kKvSplit;
   if (j0 >= Tn) return;
   const int t = threadIdx.x, g = t / TPR, c = t % TPR, e0 = c * EPT, head = e0 / DH;
@@ -74,6 +76,7 @@ __global__ __launch_bounds__(NT) void kv_attn_kernel(ModelView m, ReconArgs a, i
     vr[i] = *(const vec_t*)(row + D);
   }
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first use
+  if (a.status[lane] == TL_LANE_ABORTED) return;
   float q[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) q[e] = a.q[(size_t)r * D + e0 + e];
