@@ -119,6 +119,9 @@ static_assert(Cfg<half_t, TL_CACHE_H_INT4, 128>::BJ == Cfg<half_t, TL_CACHE_H_F1
               Cfg<half_t, TL_CACHE_H_INT8, 64>::WJ == Cfg<half_t, TL_CACHE_H_F16, 64>::WJ, "fp16 tiles");
 
 enum { EPI_ATTN = 0, EPI_KVSTORE = 1 };
+// position tiles a decode workgroup of the INT4 / INT8 configurations at
+// 64-wide heads takes, one after the other
+constexpr int kMaxTilesPerWorkgroup = 2;
 
 template <typename T> struct Mma;
 template <> struct Mma<half_t> {
@@ -152,7 +155,8 @@ struct KArgs {
   float* part;
   int S;
   void* o;                   // with tilecnt: merged output [rows, D]
-  int32_t* tilecnt;          // [rows, n_hg] tiles done, zero between launches
+  int32_t* tilecnt;          // [rows, n_hg] workgroups done, zero between launches
+  int tpw;                   // decode, INT4 / INT8 tiles: position tiles per workgroup (1 or 2)
   // prefill store
   int lane, T;
   void* kvbuf;
@@ -391,8 +395,35 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
     if (a.status && a.status[lane] == TL_LANE_ABORTED) return;
     Tn = a.T;
   }
+  // A decode workgroup of the INT4 / INT8 configurations takes TPW
+  // consecutive position tiles of its (row, head group), one after the other
+  // (each writes its own partial, as a workgroup per tile would), and counts
+  // itself once for the tile merge: one prologue's lookups and one handoff
+  // per TPW tiles.
+  // (INT4 / INT8 codes at 64-wide heads only: at 128 the loop leaves the
+  // register allocation no room and spills)
+  constexpr int TPW_MAX = EPI == EPI_ATTN && B_REG && DH == 64 ? kMaxTilesPerWorkgroup : 1;
+  const int TPW = TPW_MAX > 1 ? min(max(a.tpw, 1), TPW_MAX) : 1;
+  const int wtile = ptile;
+#pragma nounroll
+  for (int sub = 0; sub < TPW_MAX; ++sub) {
+  if (sub >= TPW) break;
+  // the row and head group are opaque to the compiler here, so what the tile
+  // derives from them is recomputed per tile rather than held in registers
+  // across the loop
+  hg = __builtin_amdgcn_readfirstlane(hg);
+  r = __builtin_amdgcn_readfirstlane(r);
+  lane = __builtin_amdgcn_readfirstlane(lane);
+  Tn = __builtin_amdgcn_readfirstlane(Tn);
+  __asm__ volatile("" : "+s"(hg), "+s"(r), "+s"(lane), "+s"(Tn));
+  ptile = wtile * TPW + sub;
   const int j0 = ptile * BJ;
-  if (j0 >= Tn) return;
+  if (j0 >= Tn) {
+    if (sub == 0) return;
+    break;
+  }
+  // the workgroup's last tile (it then counts itself)
+  const bool last_sub = sub + 1 == TPW || j0 + BJ >= Tn;
 
   // ---- W rows of this workgroup's BF features ------------------------------
   // Thread t loads 16-byte chunk `part` of A-tile rows f = f0 + F0STEP * i
@@ -794,7 +825,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
       issue_ops(std::integral_constant<int, 2>{}, IA0{}, IA1{}, min(2, nst - 1));   // parts B, C: stage 0
     if constexpr (EPI == EPI_ATTN) {
       // (uniform over the workgroup: every wave leaves, after its copies have landed)
-      if (a.status[lane] == TL_LANE_ABORTED) {
+      if (sub == 0 && a.status[lane] == TL_LANE_ABORTED) {
         dma_sync<0>();
         return;
       }
@@ -1181,14 +1212,15 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
   // next launch. scratch: NT + NT / DH + NT / 64 floats of LDS.
   auto count_and_merge = [&](float* scratch) {
     __shared__ int last_tile;
-    const int n_t = (Tn + BJ - 1) / BJ;
+    const int n_t = (Tn + BJ - 1) / BJ;      // the row's tiles (partials)
+    const int n_w = (n_t + TPW - 1) / TPW;   // the workgroups that count
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
       int* cnt = a.tilecnt + r * a.n_hg + hg;
       const int done = atomicAdd(cnt, 1) + 1;
-      last_tile = done == n_t;
-      if (done == n_t) atomicExch(cnt, 0);
+      last_tile = done == n_w;
+      if (done == n_w) atomicExch(cnt, 0);
     }
     __syncthreads();
     if (!last_tile) return;
@@ -1236,7 +1268,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
       }
       store_partial(gg, dim, M, L, O);
     }
-    if (a.tilecnt) {
+    if (a.tilecnt && last_sub) {
       static_assert(NWV * HPW_T * (DH + 2) >= NT + NT / DH + NT / 64, "merge scratch within comb_lds");
       count_and_merge(comb);
     }
@@ -1345,6 +1377,7 @@ __global__ __launch_bounds__((Cfg<T, MODE, DH, VAR>::NT), (Cfg<T, MODE, DH, VAR>
       values(0, part_of(head, split), p, ex[WJN * WJ + 2 * wj], ex[WJN * WJ + 2 * wj + 1]);
     }
   }
+  }   // position tiles of the workgroup
 }
 
 template <typename T, int MODE, int DH, int VAR = 0>
@@ -1438,7 +1471,18 @@ hipError_t launch_recon_attn(const ModelView& m, const ReconArgs& r, hipStream_t
   k.D = m.D;
   k.H = m.H;
   k.n_hg = 2 * m.D / BF;
-  k.n_ptiles = (r.t_ub + BJ - 1) / BJ;
+  // two position tiles per workgroup where the launch still has two
+  // workgroups per CU with them: INT4 / INT8 h at 64-wide heads (measured on
+  // one GPU: 64.9 -> 64.0 us per launch for INT4, 69.8 -> 67.5 us for INT8 at
+  // 4 lanes and T = 4097..4121; the fp16-h copied ring, one workgroup per
+  // CU, measured no gain and takes one)
+  const int tiles = (r.t_ub + BJ - 1) / BJ;
+  k.tpw = var == 0 && m.dh == 64 && combined_splits(m, r.cache.mode) &&
+                  (r.cache.mode == TL_CACHE_H_INT4 || r.cache.mode == TL_CACHE_H_INT8) &&
+                  (long)((tiles + 1) / 2) * r.n_rows * k.n_hg >= 2L * kCUs
+              ? kMaxTilesPerWorkgroup
+              : 1;
+  k.n_ptiles = (tiles + k.tpw - 1) / k.tpw;
   k.n_rows = r.n_rows;
   k.row_lane = r.row_lane;
   k.row_pos = r.row_pos;
